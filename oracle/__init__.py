@@ -1,0 +1,8 @@
+"""Float64 CPU oracle for exact attention.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the package smoke check and
+by the benchmark's ``cpu_baseline`` leg, never by the product path.  It shares no
+code with the HIP library.
+"""
+from .attention import (dense_bwd, dense_fwd, dense_probs, online_fwd,  # noqa: F401
+                        transfer_ledger)

@@ -1,0 +1,239 @@
+"""CPU oracle for exact attention, forward and backward, in float64.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or link
+this module: only the tests, the package's smoke check and the benchmark's CPU
+baseline leg use it.  It shares no code with the HIP library and imports
+nothing from it.
+
+Contents
+--------
+``dense_fwd``    the materialised definition: scores, masked row softmax, P V.
+``online_fwd``   the tiled Q-block-outer / key-block-inner forward with the
+                 running (max m, denominator l, unnormalised numerator a) row
+                 state, written from the online-softmax description.
+``dense_bwd``    the textbook gradient of softmax attention, recomputing P
+                 from Q, K and the log-sum-exp.
+``transfer_ledger``  the element-transfer count of the explorer's declared
+                 dense and tiled schedules.
+
+Conventions shared by all functions (readings of the pages where they are
+silent; each is also listed with the design notes):
+
+* Tensors are [..., N, d] arrays (any leading batch/head axes); every head is
+  independent.  Arithmetic is float64 whatever the input dtype.
+* Scores are ``scale * q_i . k_j``; the scale multiplies the raw dot product
+  before the maximum is taken.
+* Causal: key j is visible to query i iff j <= i (lower-triangular mask with
+  -inf fill, as in nanoGPT's manual attention quoted on "FlashAttention -- the
+  same attention, made memory-aware", section 00).
+* The saved per-row statistic is the natural-log log-sum-exp of the scaled,
+  masked scores: LSE_i = m_i + ln(l_i).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _as64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _scores(q, k, scale, causal, rows=None):
+    """Scaled scores S[..., i, j] = scale * q_i . k_j with the causal mask applied.
+
+    ``rows`` optionally restricts the queries to the given indices (the
+    definition is per row, so a subset of rows is the same computation).
+    """
+    q = _as64(q)
+    k = _as64(k)
+    qi = q if rows is None else q[..., rows, :]
+    s = (qi @ np.swapaxes(k, -1, -2)) * float(scale)
+    if causal:
+        n_k = k.shape[-2]
+        r = np.arange(q.shape[-2]) if rows is None else np.asarray(rows)
+        visible = np.arange(n_k)[None, :] <= r[:, None]
+        s = np.where(visible, s, -np.inf)
+    return s
+
+
+def dense_fwd(q, k, v, causal=False, scale=None, rows=None):
+    """Materialised attention O = softmax(scale * Q K^T) V and its row LSE.
+
+    Follows the dense three-step path ("Flash Attention: IO-Aware Exact
+    Attention", section "Why intermediate matrices cost memory traffic"): form
+    every score S, normalise each row of S by its own max and sum to get P, then
+    multiply P by V.  The same steps are nanoGPT's manual attention on
+    "FlashAttention -- the same attention, made memory-aware", section 00.
+
+    Returns ``(o, lse)`` with o [..., R, d_v] and lse [..., R] in float64, where R
+    is N or ``len(rows)``.
+    """
+    q = _as64(q)
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[-1])
+    s = _scores(q, k, scale, causal, rows)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    ell = e.sum(axis=-1, keepdims=True)
+    p = e / ell
+    o = p @ _as64(v)
+    lse = m[..., 0] + np.log(ell[..., 0])
+    return o, lse
+
+
+def dense_probs(q, k, causal=False, scale=None):
+    """The normalised probability matrix P of the dense path (for row-sum checks)."""
+    q = _as64(q)
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[-1])
+    s = _scores(q, k, scale, causal)
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def online_fwd(q, k, v, causal=False, scale=None, query_block=2, key_block=2, trace=None):
+    """Tiled forward with the online softmax, one head at a time.
+
+    Loop order: query blocks outside, key/value blocks inside; each query block
+    keeps its row state resident while every key tile passes ("Flash Attention:
+    IO-Aware Exact Attention", section "Loop order changes which data is
+    reloaded").  Row state per query: running maximum ``m`` (starts at -inf),
+    denominator ``l`` (starts at 0) and the d_v-wide unnormalised numerator ``a``
+    (starts at 0).  For a tile of scores t and values V_tile the update is the
+    one of section "Online softmax makes tiling exact" of the same page (the
+    displayed formulas did not survive extraction; this is the reading that
+    the page's own NumPy check, the two-block worked example on Road to
+    Intelligence "FlashAttention", section "The trick that makes tiling
+    possible", and section 03 of "FlashAttention -- the same attention, made
+    memory-aware" all agree on):
+
+        m' = max(m, max_j t_j)
+        alpha = exp(m - m')                 (alpha = 0 while no key was seen)
+        p_j = exp(t_j - m')
+        l' = alpha * l + sum_j p_j
+        a' = alpha * a + sum_j p_j V_tile[j]
+
+    and at the end O = a / l (one division, the FlashAttention-2 form of the
+    unnormalised accumulator), LSE = m + ln l.
+
+    Masked keys (causal j > i) have t_j = -inf and contribute p_j = 0.  A tile in
+    which every key of a row is masked leaves that row's state unchanged.
+    Tail tiles are simply shorter (keys beyond N do not exist); tiles larger
+    than N are allowed.
+
+    ``trace``, when a list, receives one dict per (query block, key tile) with
+    copies of the state after that tile: keys ``row0``, ``col0``, ``m``, ``l``, ``a``.
+    """
+    q = _as64(q)
+    k = _as64(k)
+    v = _as64(v)
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[-1])
+    lead = q.shape[:-2]
+    n_q, n_k = q.shape[-2], k.shape[-2]
+    dv = v.shape[-1]
+    qf = q.reshape((-1, n_q, q.shape[-1]))
+    kf = k.reshape((-1, n_k, k.shape[-1]))
+    vf = v.reshape((-1, n_k, dv))
+    out = np.empty((qf.shape[0], n_q, dv))
+    lse = np.empty((qf.shape[0], n_q))
+    for h in range(qf.shape[0]):
+        for row0 in range(0, n_q, query_block):
+            rows = np.arange(row0, min(n_q, row0 + query_block))
+            query = qf[h, rows]
+            m = np.full(len(rows), -np.inf)
+            ell = np.zeros(len(rows))
+            a = np.zeros((len(rows), dv))
+            for col0 in range(0, n_k, key_block):
+                cols = np.arange(col0, min(n_k, col0 + key_block))
+                t = (query @ kf[h, cols].T) * scale
+                if causal:
+                    t = np.where(cols[None, :] <= rows[:, None], t, -np.inf)
+                m_new = np.maximum(m, t.max(axis=1))
+                seen = np.isfinite(m_new)          # rows with at least one visible key so far
+                m_safe = np.where(seen, m_new, 0.0)
+                alpha = np.where(np.isfinite(m), np.exp(m - m_safe), 0.0)
+                p = np.where(seen[:, None], np.exp(t - m_safe[:, None]), 0.0)
+                ell_new = alpha * ell + p.sum(axis=1)
+                a_new = alpha[:, None] * a + p @ vf[h, cols]
+                # a row whose keys were all masked so far keeps its initial state
+                m = np.where(seen, m_new, m)
+                ell = np.where(seen, ell_new, ell)
+                a = np.where(seen[:, None], a_new, a)
+                if trace is not None:
+                    trace.append({"head": h, "row0": row0, "col0": col0,
+                                  "m": m.copy(), "l": ell.copy(), "a": a.copy()})
+            out[h, rows] = a / ell[:, None]
+            lse[h, rows] = m + np.log(ell)
+    return out.reshape(lead + (n_q, dv)), lse.reshape(lead + (n_q,))
+
+
+def dense_bwd(q, k, v, do, causal=False, scale=None):
+    """Gradients of L = sum(O * dO) for O = softmax(scale * Q K^T) V.
+
+    The pages state only that the backward pass recomputes the score and
+    probability tiles from Q, K, V and the saved normalisation statistics
+    instead of storing them ("Flash Attention: IO-Aware Exact Attention",
+    section "Storage, arithmetic and IO are separate quantities"; Road to
+    Intelligence "FlashAttention", section "The trick that makes tiling
+    possible").  The gradient itself is the textbook one of a row softmax
+    followed by a matrix product, written out here without autograd:
+
+        P    = exp(S - LSE)                 (recomputed)
+        dV   = P^T dO
+        dP   = dO V^T
+        D_i  = sum_c dO_ic O_ic             (= sum_j P_ij dP_ij)
+        dS   = P * (dP - D)
+        dQ   = scale * dS K
+        dK   = scale * dS^T Q
+
+    Returns ``(dq, dk, dv, o, lse)`` in float64.
+    """
+    q = _as64(q)
+    k = _as64(k)
+    v = _as64(v)
+    do = _as64(do)
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[-1])
+    o, lse = dense_fwd(q, k, v, causal, scale)
+    s = _scores(q, k, scale, causal)
+    p = np.exp(s - lse[..., None])
+    kt = np.swapaxes
+    dv = kt(p, -1, -2) @ do
+    dp = do @ kt(v, -1, -2)
+    D = (do * o).sum(axis=-1, keepdims=True)
+    ds = p * (dp - D)
+    dq = scale * (ds @ k)
+    dk = scale * (kt(ds, -1, -2) @ q)
+    return dq, dk, dv, o, lse
+
+
+def transfer_ledger(n, d, dv, query_block, key_block):
+    """Count element transfers of the explorer's declared dense and tiled schedules.
+
+    Both schedules keep one query block resident and stream every key/value
+    tile past it ("Flash Attention: IO-Aware Exact Attention", section "Loop
+    order changes which data is reloaded"): a query block is read once, every
+    K and V tile is read once per query block, the output block is written
+    once.  The dense schedule additionally writes each score tile to HBM, reads
+    it back for the softmax, writes the probability tile and reads it back for
+    the product with V.  The walk below visits the tiles in loop order and adds
+    up the elements each step moves; caches and spills are not modelled.
+    """
+    tiled = {"Q_read": 0, "K_read": 0, "V_read": 0, "O_write": 0}
+    extra = {"S_write": 0, "S_read": 0, "P_write": 0, "P_read": 0}
+    for row0 in range(0, n, query_block):
+        rows = min(n, row0 + query_block) - row0
+        tiled["Q_read"] += rows * d
+        for col0 in range(0, n, key_block):
+            cols = min(n, col0 + key_block) - col0
+            tiled["K_read"] += cols * d
+            tiled["V_read"] += cols * dv
+            extra["S_write"] += rows * cols
+            extra["S_read"] += rows * cols
+            extra["P_write"] += rows * cols
+            extra["P_read"] += rows * cols
+        tiled["O_write"] += rows * dv
+    dense = dict(tiled, **extra)
+    return {"tiled": tiled, "dense": dense,
+            "tiled_total": sum(tiled.values()), "dense_total": sum(dense.values())}

@@ -1,0 +1,429 @@
+"""Pins for the float64 CPU oracle (no GPU).
+
+The oracle is checked against facts fixed by the pages (worked examples, the
+explorer's self-check, the transfer ledger), closed forms, invariants and
+library routines that compute the same textbook quantity.  A final group plants
+plausible mistakes in a copy of the online recurrence and shows that these
+pins catch each one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import workloads
+
+RNG = np.random.default_rng(1234)
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def _rand(*shape, seed=0, std=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * std
+
+
+# ---------------------------------------------------------------- page facts
+
+def test_two_block_row_matches_worked_example(golden_dir):
+    """Road to Intelligence 'FlashAttention', 'The trick that makes tiling possible'."""
+    g = _load(golden_dir, "two_block_row.json")
+    tol = g["printed_tolerance"]
+    scores = [x for blk in g["blocks"] for x in blk]
+    # one query, d = 1, q = 1, keys = the scores, scale 1: raw scores are the page's scores
+    q = np.array([[1.0]])
+    k = np.array(scores, dtype=np.float64)[:, None]
+    v = np.eye(len(scores))  # a one-hot value per key exposes the weights
+    trace = []
+    o, lse = oracle.online_fwd(q, k, v, scale=1.0, query_block=1, key_block=2, trace=trace)
+    assert len(trace) == 2
+    t1, t2 = trace
+    assert t1["m"][0] == g["after_block_1"]["m"]
+    assert abs(t1["l"][0] - g["after_block_1"]["l"]) <= tol
+    assert t2["m"][0] == g["after_block_2"]["m"]
+    assert abs(t2["l"][0] - g["after_block_2"]["l"]) <= tol
+    # the rescale factor applied to the old sum is exp(3 - 5)
+    old_sum_scaled = t2["l"][0] - (math.exp(2 - 5) + math.exp(5 - 5))
+    assert abs(old_sum_scaled / t1["l"][0] - g["after_block_2"]["rescale"]) <= tol
+    for printed, exact in zip(g["after_block_2"]["terms"],
+                              [t1["l"][0] * math.exp(3 - 5), math.exp(2 - 5), 1.0]):
+        assert abs(printed - exact) <= tol
+    # direct one-pass sum
+    direct = sum(math.exp(s - 5) for s in scores)
+    assert abs(direct - g["direct"]["l"]) <= tol
+    for printed, s in zip(g["direct"]["terms"], [1, 3, 2, 5]):
+        assert abs(printed - math.exp(s - 5)) <= tol
+    # and the exact values: l1 = 1 + e^-2, l2 = e^-4 + e^-2 + e^-3 + 1
+    assert t1["l"][0] == pytest.approx(1 + math.exp(-2), rel=1e-15)
+    assert t2["l"][0] == pytest.approx(direct, rel=1e-15)
+    assert lse[0] == pytest.approx(scipy.special.logsumexp(scores), rel=1e-15)
+    np.testing.assert_allclose(o[0], scipy.special.softmax(scores), rtol=1e-14)
+
+
+def test_explorer_tiled_equals_dense(golden_dir):
+    """'Flash Attention: IO-Aware Exact Attention', 'Check the recurrence on CPU'."""
+    g = _load(golden_dir, "explorer_vectors.json")
+    q, k, v = (np.array(g[x], dtype=np.float64) for x in "qkv")
+    dense, dense_lse = oracle.dense_fwd(q, k, v)
+    for kb in g["key_blocks"]:
+        tiled, lse = oracle.online_fwd(q, k, v, query_block=g["query_block"], key_block=kb)
+        np.testing.assert_allclose(tiled, dense, rtol=g["rtol"], atol=g["atol"])
+        np.testing.assert_allclose(lse, dense_lse, rtol=g["rtol"], atol=g["atol"])
+    # the same check over every query block size and with the causal mask
+    for causal in (False, True):
+        ref, ref_lse = oracle.dense_fwd(q, k, v, causal=causal)
+        for qb in range(1, 8):
+            for kb in range(1, 8):
+                o, lse = oracle.online_fwd(q, k, v, causal=causal, query_block=qb, key_block=kb)
+                np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+                np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_explorer_q0_max_rises_in_every_tile(golden_dir):
+    g = _load(golden_dir, "explorer_vectors.json")
+    q, k, v = (np.array(g[x], dtype=np.float64) for x in "qkv")
+    trace = []
+    oracle.online_fwd(q, k, v, query_block=2, key_block=g["q0_max_rises_with_key_block"], trace=trace)
+    m0 = [t["m"][0] for t in trace if t["row0"] == 0]
+    assert len(m0) == 3
+    assert all(b > a for a, b in zip(m0, m0[1:]))
+    # raw dots of Q0 with the six keys are -1, 0, 2, 1, 3, -1: tile maxima 0, 2, 3
+    np.testing.assert_allclose(np.array(m0) * math.sqrt(2), [0, 2, 3], rtol=1e-15)
+    # the values differ across keys, so the rescale of the numerator matters
+    assert len({tuple(r) for r in v}) == len(v)
+
+
+def test_explorer_causal_rows_closed_form(golden_dir):
+    g = _load(golden_dir, "explorer_vectors.json")
+    q, k, v = (np.array(g[x], dtype=np.float64) for x in "qkv")
+    o, lse = oracle.online_fwd(q, k, v, causal=True, query_block=2, key_block=2)
+    np.testing.assert_allclose(o[0], v[0], rtol=0, atol=1e-15)
+    assert lse[0] == pytest.approx(-1 / math.sqrt(2), rel=1e-15)
+    full, full_lse = oracle.dense_fwd(q, k, v)
+    np.testing.assert_allclose(o[-1], full[-1], rtol=1e-14)
+    assert lse[-1] == pytest.approx(full_lse[-1], rel=1e-14)
+
+
+def test_transfer_ledger(golden_dir):
+    """'Loop order changes which data is reloaded': 240 versus 96 transfers."""
+    g = _load(golden_dir, "transfer_ledger.json")
+    for kb in range(1, 8):
+        led = oracle.transfer_ledger(g["N"], g["d"], g["d_v"], g["query_block"], kb)
+        for key in ("Q_read", "K_read", "V_read", "O_write"):
+            assert led["tiled"][key] == g[key]
+        for key in ("S_write", "S_read", "P_write", "P_read"):
+            assert led["dense"][key] == g[key]
+        assert led["dense_total"] == g["dense_total"]
+        assert led["tiled_total"] == g["tiled_total"]
+    # the S and P round trips alone move 4 N^2 elements
+    # ('Why intermediate matrices cost memory traffic')
+    for n in (6, 17, 64):
+        led = oracle.transfer_ledger(n, 2, 2, 4, 3)
+        assert led["dense_total"] - led["tiled_total"] == 4 * n * n
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_of_p_sum_to_one(causal):
+    q, k = _rand(3, 37, 8, seed=1, std=2), _rand(3, 37, 8, seed=2, std=2)
+    p = oracle.dense_probs(q, k, causal=causal)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-15 * 37)
+    if causal:
+        assert np.all(np.triu(p[0], 1) == 0)
+
+
+def test_single_key_gives_value():
+    q, k, v = _rand(2, 1, 5, seed=3), _rand(2, 1, 5, seed=4), _rand(2, 1, 5, seed=5)
+    for fn in (lambda: oracle.dense_fwd(q, k, v, scale=0.7),
+               lambda: oracle.online_fwd(q, k, v, scale=0.7, query_block=3, key_block=2)):
+        o, lse = fn()
+        np.testing.assert_allclose(o, v, rtol=1e-15)
+        np.testing.assert_allclose(lse, 0.7 * (q * k).sum(-1), rtol=1e-14)
+
+
+@pytest.mark.parametrize("n", [1, 5, 33])
+def test_zero_queries_average_the_values(n):
+    q = np.zeros((1, n, 4))
+    k, v = _rand(1, n, 4, seed=6), _rand(1, n, 3, seed=7)
+    o, lse = oracle.dense_fwd(q, k, v)
+    np.testing.assert_allclose(o[0], np.broadcast_to(v[0].mean(0), (n, 3)), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse, math.log(n), rtol=1e-15)
+    oc, lsec = oracle.online_fwd(q, k, v, causal=True, query_block=4, key_block=3)
+    cm = np.cumsum(v[0], axis=0) / np.arange(1, n + 1)[:, None]
+    np.testing.assert_allclose(oc[0], cm, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lsec[0], np.log(np.arange(1, n + 1)), rtol=1e-15, atol=1e-15)
+
+
+def test_equal_values_give_that_value():
+    q, k = _rand(2, 19, 6, seed=8, std=3), _rand(2, 19, 6, seed=9, std=3)
+    row = _rand(6, seed=10)
+    v = np.broadcast_to(row, (2, 19, 6)).copy()
+    for causal in (False, True):
+        o, _ = oracle.online_fwd(q, k, v, causal=causal, query_block=5, key_block=4)
+        np.testing.assert_allclose(o, v, rtol=1e-13)
+
+
+def test_causal_first_and_last_rows():
+    q, k, v = _rand(2, 23, 8, seed=11), _rand(2, 23, 8, seed=12), _rand(2, 23, 8, seed=13)
+    o, lse = oracle.dense_fwd(q, k, v, causal=True, scale=0.3)
+    full, full_lse = oracle.dense_fwd(q, k, v, causal=False, scale=0.3)
+    np.testing.assert_allclose(o[:, 0], v[:, 0], rtol=1e-15)
+    np.testing.assert_allclose(lse[:, 0], 0.3 * (q[:, 0] * k[:, 0]).sum(-1), rtol=1e-14)
+    np.testing.assert_allclose(o[:, -1], full[:, -1], rtol=1e-15)
+    np.testing.assert_allclose(lse[:, -1], full_lse[:, -1], rtol=1e-15)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_key_shift_invariance():
+    q, k, v = _rand(1, 2, 17, 8, seed=14), _rand(1, 2, 17, 8, seed=15), _rand(1, 2, 17, 8, seed=16)
+    c = _rand(8, seed=17)
+    for causal in (False, True):
+        o, lse = oracle.online_fwd(q, k, v, causal=causal, scale=0.5, query_block=4, key_block=5)
+        o2, lse2 = oracle.online_fwd(q, k + c, v, causal=causal, scale=0.5, query_block=4, key_block=5)
+        np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse2, lse + 0.5 * (q @ c), rtol=1e-12, atol=1e-13)
+
+
+def test_permutation_invariances():
+    q, k, v = _rand(3, 21, 8, seed=18), _rand(3, 21, 8, seed=19), _rand(3, 21, 8, seed=20)
+    perm = np.random.default_rng(21).permutation(21)
+    o, lse = oracle.online_fwd(q, k, v, query_block=4, key_block=6)
+    o_kv, lse_kv = oracle.online_fwd(q, k[:, perm], v[:, perm], query_block=4, key_block=6)
+    np.testing.assert_allclose(o_kv, o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse_kv, lse, rtol=1e-13)
+    o_q, lse_q = oracle.online_fwd(q[:, perm], k, v, query_block=4, key_block=6)
+    np.testing.assert_allclose(o_q, o[:, perm], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse_q, lse[:, perm], rtol=1e-13)
+
+
+def test_prefix_property():
+    """After t tiles, a/l is attention over exactly the keys seen so far.
+
+    'Online softmax makes tiling exact': the partial ratio a/l attends only to
+    the processed keys, and alpha is zero before any key is seen.
+    """
+    q, k, v = _rand(1, 9, 4, seed=22), _rand(1, 9, 4, seed=23), _rand(1, 9, 3, seed=24)
+    kb, scale = 2, 0.8
+    for causal in (False, True):
+        trace = []
+        oracle.online_fwd(q, k, v, causal=causal, scale=scale, query_block=9, key_block=kb, trace=trace)
+        assert len(trace) == 5
+        for t in trace:
+            keys = min(9, t["col0"] + kb)
+            for i in range(9):
+                visible = min(keys, i + 1) if causal else keys
+                if visible == 0:
+                    # no key seen yet: the initial state is untouched
+                    assert t["m"][i] == -np.inf and t["l"][i] == 0 and np.all(t["a"][i] == 0)
+                    continue
+                r, rl = oracle.dense_fwd(q[0, i:i + 1], k[0, :visible], v[0, :visible], scale=scale)
+                np.testing.assert_allclose(t["a"][i] / t["l"][i], r[0], rtol=1e-12, atol=1e-14)
+                assert t["m"][i] + math.log(t["l"][i]) == pytest.approx(rl[0], rel=1e-12)
+
+
+# ---------------------------------------------------------------- library cross-checks
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,d", [(1, 4), (7, 3), (64, 16), (130, 32)])
+def test_against_torch_sdpa_and_logsumexp(causal, n, d):
+    q, k, v = _rand(2, 3, n, d, seed=25), _rand(2, 3, n, d, seed=26), _rand(2, 3, n, d, seed=27)
+    scale = 1.0 / math.sqrt(d)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=causal).numpy()
+    s = scale * (q @ np.swapaxes(k, -1, -2))
+    if causal:
+        s = np.where(np.tril(np.ones((n, n), bool)), s, -np.inf)
+    ref_lse = scipy.special.logsumexp(s, axis=-1)
+    for o, lse in (oracle.dense_fwd(q, k, v, causal=causal),
+                   oracle.online_fwd(q, k, v, causal=causal, query_block=16, key_block=24)):
+        np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-13, atol=1e-13)
+
+
+def test_dense_rows_subset_matches_full():
+    q, k, v = _rand(2, 50, 8, seed=28), _rand(2, 50, 8, seed=29), _rand(2, 50, 8, seed=30)
+    rows = np.array([0, 3, 17, 49])
+    for causal in (False, True):
+        o, lse = oracle.dense_fwd(q, k, v, causal=causal)
+        os_, lses = oracle.dense_fwd(q, k, v, causal=causal, rows=rows)
+        np.testing.assert_allclose(os_, o[:, rows], rtol=1e-14)
+        np.testing.assert_allclose(lses, lse[:, rows], rtol=1e-14)
+
+
+def test_negative_and_zero_scale():
+    q, k, v = _rand(1, 13, 4, seed=31), _rand(1, 13, 4, seed=32), _rand(1, 13, 4, seed=33)
+    for scale in (-0.9, 0.0):
+        for causal in (False, True):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                is_causal=causal, scale=scale).numpy()
+            o, _ = oracle.online_fwd(q, k, v, causal=causal, scale=scale, query_block=3, key_block=4)
+            np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- backward
+
+def _loss(q, k, v, do, causal, scale):
+    o, _ = oracle.dense_fwd(q, k, v, causal=causal, scale=scale)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_finite_differences(causal):
+    n, d = 5, 3
+    q, k, v, do = (_rand(n, d, seed=s) for s in (40, 41, 42, 43))
+    scale = 0.7
+    dq, dk, dv, _, _ = oracle.dense_bwd(q, k, v, do, causal=causal, scale=scale)
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy()
+            xm = x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            num[idx] = (_loss(*args_p, do, causal, scale) - _loss(*args_m, do, causal, scale)) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_against_torch_autograd(causal):
+    q, k, v, do = (_rand(2, 33, 8, seed=s) for s in (44, 45, 46, 47))
+    dq, dk, dv, o, lse = oracle.dense_bwd(q, k, v, do, causal=causal)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal)
+    to.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(o, to.detach().numpy(), rtol=1e-12, atol=1e-13)
+    for a, b in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(a, b.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_invariants():
+    q, k, v, do = (_rand(2, 17, 6, seed=s) for s in (48, 49, 50, 51))
+    for causal in (False, True):
+        dq, dk, dv, _, _ = oracle.dense_bwd(q, k, v, do, causal=causal)
+        # shifting every key by the same vector leaves O unchanged -> sum_j dK_j = 0
+        np.testing.assert_allclose(dk.sum(-2), 0, atol=1e-12)
+        # rows of P sum to one -> sum_j dV_j = sum_i dO_i
+        np.testing.assert_allclose(dv.sum(-2), do.sum(-2), rtol=1e-12, atol=1e-12)
+    veq = np.broadcast_to(_rand(6, seed=52), v.shape).copy()
+    dq, dk, _, _, _ = oracle.dense_bwd(q, k, veq, do, causal=True)
+    np.testing.assert_allclose(dq, 0, atol=1e-12)
+    np.testing.assert_allclose(dk, 0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- inputs
+
+def test_bf16_rounding_matches_torch_cast():
+    x = np.random.default_rng(60).standard_normal(100000).astype(np.float32) * 10
+    # exact ties: values halfway between two bf16 numbers
+    ties = (np.arange(1, 2001, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, -ties, np.float32([0.0, -0.0, 1e-40, 3.4e38])])
+    ours = workloads.round_to_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(ours.view(np.uint32), ref.view(np.uint32))
+
+
+def test_needle_inputs_are_near_one_hot():
+    """Needle rows attend (almost) only to their target, never the forbidden key."""
+    d, n = 16, 160
+    x = workloads.needle_inputs(1, 1, n, d, "bf16", seed=3, causal=True)
+    o, _ = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=True)
+    o_nomask, _ = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=False)
+    # run 0 is row 0 alone, target key 0; run 1 covers rows 2..8, target key 2, forbidden key 9
+    np.testing.assert_allclose(o[0, 0, 0], x["v"][0, 0, 0], atol=1e-6)
+    for i in range(2, 9):
+        np.testing.assert_allclose(o[0, 0, i], x["v"][0, 0, 2], atol=1e-6)
+        # without the mask the forbidden key would win by a wide margin
+        assert np.abs(o_nomask[0, 0, i] - x["v"][0, 0, 9]).max() < 1e-6
+
+
+def test_workload_flops_and_bytes():
+    w = workloads.WORKLOADS["long_causal_bf16"]
+    assert w.fwd_flops() == 4 * 128 * (8192 * 8193 // 2) * 16 == 274911461376
+    assert w.fwd_bytes() == 134742016
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _mutant_online(q, k, v, causal, scale, qb, kb, bug):
+    """A copy of the online recurrence with one deliberate mistake."""
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    n, dv = q.shape[0], v.shape[1]
+    out, lse = np.empty((n, dv)), np.empty(n)
+    for r0 in range(0, n, qb):
+        rows = np.arange(r0, min(n, r0 + qb))
+        m, ell, a = np.full(len(rows), -np.inf), np.zeros(len(rows)), np.zeros((len(rows), dv))
+        for c0 in range(0, n, kb):
+            cols = np.arange(c0, min(n, c0 + kb))
+            t = q[rows] @ k[cols].T
+            if bug != "scale_after_max":
+                t = t * scale
+            if causal:
+                vis = cols[None, :] < rows[:, None] if bug == "strict_causal" else cols[None, :] <= rows[:, None]
+                t = np.where(vis, t, -np.inf)
+            m_new = np.maximum(m, t.max(1))
+            ms = np.where(np.isfinite(m_new), m_new, 0.0)
+            alpha = np.where(np.isfinite(m), np.exp(m - ms), 0.0)
+            p = np.exp(t - ms[:, None])
+            if bug == "scale_after_max":
+                p = np.exp(scale * (t - ms[:, None]))
+                alpha = np.where(np.isfinite(m), np.exp(scale * (m - ms)), 0.0)
+            if bug == "no_alpha_on_l":
+                ell = ell + p.sum(1)
+            else:
+                ell = alpha * ell + p.sum(1)
+            if bug == "no_alpha_on_a":
+                a = a + p @ v[cols]
+            elif bug == "transposed_pv":
+                a = alpha[:, None] * a + (p @ k[cols] if k.shape == v.shape else p @ v[cols])
+            elif bug == "drop_last_tile" and c0 + kb >= n:
+                pass
+            else:
+                a = alpha[:, None] * a + p @ v[cols]
+            m = np.where(np.isfinite(m_new), m_new, m)
+        out[rows] = a / ell[:, None]
+        lse[rows] = m + (np.log2(ell) if bug == "lse_base2" else np.log(ell))
+    return out, lse
+
+
+BUGS = ["no_alpha_on_a", "no_alpha_on_l", "strict_causal", "scale_after_max",
+        "transposed_pv", "drop_last_tile", "lse_base2"]
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+@pytest.mark.parametrize("bug", BUGS)
+def test_pins_catch_planted_mistakes(bug):
+    """Each mistake fails at least one of the checks used above as pins."""
+    q, k, v = _rand(13, 4, seed=70, std=2), _rand(13, 4, seed=71, std=2), _rand(13, 4, seed=72)
+    failures = 0
+    for causal in (False, True):
+        for scale in (0.5, -0.5):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                is_causal=causal, scale=scale).numpy()
+            s = scale * (q @ k.T)
+            if causal:
+                s = np.where(np.tril(np.ones((13, 13), bool)), s, -np.inf)
+            ref_lse = scipy.special.logsumexp(s, axis=-1)
+            o, lse = _mutant_online(q, k, v, causal, scale, 4, 3, bug)
+            if not (np.allclose(o, ref, rtol=1e-10, atol=1e-12)
+                    and np.allclose(lse, ref_lse, rtol=1e-10, atol=1e-12)):
+                failures += 1
+    assert failures > 0
+    # and the unmutated recurrence passes the same checks
+    o, lse = _mutant_online(q, k, v, True, 0.5, 4, 3, bug="none")
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=True, scale=0.5).numpy()
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-13)
