@@ -1,0 +1,164 @@
+"""Benchmark of the exact-attention forward on one MI355X.
+
+One step = one ``attn_fwd`` call over the long-context causal workload
+(B=1, H=16, N=8192, d=128, bf16, scale 1/sqrt(128)) with seeded synthetic
+N(0, 1) inputs already resident in device memory.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+The reported throughput counts algorithmic FLOPs only: 4 * d * (visible query-key
+pairs) * B * H, i.e. the two matrix products over the causal triangle.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (bf16, causal, T=8192, d=128) and % of MFMA peak"
+WORKLOAD = "long_causal_bf16"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+KERNEL_SOURCES = ("fwd_mfma.hip",)
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fwd_long_causal_bf16_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "io_aware_exact_12_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary.
+
+    Returns None when no summary exists or when it was taken on a different
+    version of the kernel source than the one being benchmarked.
+    """
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    text = open(TRAFFIC_PROFILE).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, x, budget_s=12.0):
+    """Time the float64 oracle on the host on whole heads of the same workload."""
+    import numpy as np
+
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) \
+            if threadpoolctl.threadpool_info() else 1
+    except Exception:  # threadpoolctl missing or no BLAS pool found
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    heads = 0
+    pairs = w.N * (w.N + 1) // 2 if w.causal else w.N * w.N
+    for h in range(w.H):
+        oracle.dense_fwd(x["q"][0, h], x["k"][0, h], x["v"][0, h], causal=w.causal, scale=w.scale)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.d * pairs * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"dense float64 oracle on {heads} of {w.B * w.H} heads (all {w.N} rows each, "
+                      f"full N x N scores computed, causal-visible FLOPs counted), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(attention shards over (batch, head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import io_aware_exact_12_amd as fa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = workloads.WORKLOADS[WORKLOAD]
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(torch.bfloat16).contiguous() for n in "qkv")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        fa.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        fa.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    flops = w.fwd_flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    record = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "mask": "causal" if w.causal else "none", "scale": w.scale,
+                   "inputs": "Q, K, V i.i.d. N(0,1) rounded to bf16, seed 3"},
+        "pct_of_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "fwd_kernel<bf16, d=128, causal>",
+                     "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": w.fwd_bytes(),
+                     "kernel_source_sha256_16": kernel_source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        record["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,102 @@
+/*
+ * fa_attn.h -- C ABI of the exact-attention library (libfa_attn.so) for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library computes exact scaled dot-product attention
+ *
+ *     O = softmax(scale * Q K^T) V,     LSE_i = ln sum_j exp(scale * q_i . k_j)
+ *
+ * over visible keys j, without ever writing the N x N score or probability
+ * matrix to device memory: query blocks stay resident on chip while key/value
+ * tiles stream past, and each query row carries a running maximum, denominator
+ * and unnormalised numerator that are rescaled whenever a later tile raises
+ * the maximum ("Flash Attention: IO-Aware Exact Attention", sections "Online
+ * softmax makes tiling exact" and "Loop order changes which data is
+ * reloaded"; Road to Intelligence "FlashAttention", section "The trick that
+ * makes tiling possible").
+ *
+ * Layout.  Every tensor argument is a dense, contiguous [B][H][N][d] array of
+ * the element type ``dtype`` (d innermost; d_v = d), 16-byte aligned, resident
+ * in device memory of the current HIP device.  ``lse`` is a dense [B][H][N]
+ * float array.
+ *
+ * Ownership.  All pointers belong to the caller; the library never allocates,
+ * frees or retains them, and holds no mutable global state.  ``o`` must not
+ * overlap q, k or v.
+ *
+ * Streams and errors.  Work is enqueued on ``stream`` (a hipStream_t; NULL is
+ * the default stream) and the call returns without waiting.  Every argument
+ * check happens before anything is enqueued and returns a status code; no call
+ * throws or prints.  A fault while the kernel runs is reported by the HIP
+ * runtime at the caller's next synchronisation.  FA_ERR_HIP means a launch was
+ * rejected by the runtime (hipGetLastError).
+ */
+#ifndef FA_ATTN_H
+#define FA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v, o (and of dout, dq, dk, dv in the backward). */
+enum fa_dtype { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 };
+
+/* FA_MASK_CAUSAL: key j is visible to query i iff j <= i (lower-triangular
+ * mask filled with -inf before the softmax, as in nanoGPT's manual attention
+ * on "FlashAttention -- the same attention, made memory-aware", section 00). */
+enum fa_mask { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1 };
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  FA_ERR_SHAPE = 2,       /* B, H or N < 1, or an element count overflows       */
+  FA_ERR_DTYPE = 3,       /* dtype is not one of enum fa_dtype                  */
+  FA_ERR_MASK = 4,        /* mask is not one of enum fa_mask                    */
+  FA_ERR_SCALE = 5,       /* scale is NaN or infinite                           */
+  FA_ERR_UNSUPPORTED = 6, /* head dimension d is not 64 or 128                  */
+  FA_ERR_WORKSPACE = 7,   /* backward workspace missing or too small            */
+  FA_ERR_HIP = 8,         /* the HIP runtime rejected a launch                  */
+  FA_ERR_ALIGN = 9        /* a tensor pointer is not 16-byte aligned            */
+};
+
+/*
+ * attn_fwd -- forward pass.
+ *
+ *   q, k, v  [B][H][N][d] inputs of type dtype.
+ *   o        [B][H][N][d] output of type dtype: O = P V with P the row softmax of
+ *            scale * Q K^T (masked), accumulated in fp32 and rounded to nearest
+ *            even once at the end.
+ *   lse      [B][H][N] fp32 output, the natural-log log-sum-exp of each row's
+ *            scaled, masked scores (the normalisation statistic the backward
+ *            pass recomputes probabilities from: "Flash Attention: IO-Aware
+ *            Exact Attention", section "Storage, arithmetic and IO are
+ *            separate quantities").  May be NULL, in which case it is not
+ *            written.
+ *   B, H, N  batch, heads, sequence length (queries and keys), each >= 1.
+ *   d        head dimension of q, k and v: 64 or 128.
+ *   mask     enum fa_mask.
+ *   scale    finite multiplier of the raw dot products (any sign; usually
+ *            1/sqrt(d)).
+ *   dtype    enum fa_dtype.
+ *   stream   hipStream_t to enqueue on, or NULL.
+ *
+ * The result is deterministic: the same inputs give bitwise the same outputs.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t B, int64_t H, int64_t N, int64_t d,
+             int mask, float scale, int dtype, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* fa_status_str(int status);
+
+/* Version of this ABI; bumped on any incompatible change. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_ATTN_H */

@@ -1,0 +1,104 @@
+"""ctypes binding of libfa_attn.so (argument marshalling only).
+
+Every computation runs in the library's HIP kernels.  If the library has not
+been built, loading raises; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa_attn.so")
+HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "fa_attn.h")
+
+F32, F16, BF16 = 0, 1, 2
+MASK_NONE, MASK_CAUSAL = 0, 1
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_str(status)})")
+
+
+def lib():
+    """Load the shared library once (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m io_aware_exact_12_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        L.attn_fwd.restype = ctypes.c_int
+        L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                               ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+        L.fa_status_str.restype = ctypes.c_char_p
+        L.fa_status_str.argtypes = [ctypes.c_int]
+        L.fa_abi_version.restype = ctypes.c_int
+        L.fa_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().fa_status_str(int(status)).decode()
+
+
+def declared_symbols(header: str = HEADER):
+    """Names of the functions include/fa_attn.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def attn_fwd_raw(q, k, v, o, lse, B, H, N, d, mask, scale, dtype, stream):
+    """Direct call of the C entry point with integer pointers; returns the status."""
+    return lib().attn_fwd(q, k, v, o, lse, B, H, N, d, mask, scale, dtype, stream)
+
+
+def _torch_dtype_code(t):
+    import torch
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=None, lse=None,
+             return_lse: bool = True, stream=None):
+    """Exact attention forward on the GPU: returns ``(o, lse)`` (lse None if not requested).
+
+    q, k, v: contiguous device tensors [B, H, N, d] of one dtype (float32,
+    float16 or bfloat16), d in {64, 128}.  ``scale`` defaults to 1/sqrt(d).
+    Work is enqueued on ``stream`` (default: torch's current stream).
+    """
+    import torch
+    if q.shape != k.shape or q.shape != v.shape or q.dim() != 4:
+        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {q.shape}, {k.shape}, {v.shape}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                        lse.data_ptr() if return_lse else None, B, H, N, d,
+                        MASK_CAUSAL if causal else MASK_NONE, float(scale), _torch_dtype_code(q),
+                        stream.cuda_stream)
+    if st != 0:
+        raise FaError(st, "attn_fwd")
+    return out, (lse if return_lse else None)

@@ -1,0 +1,78 @@
+// C ABI of libfa_attn.so: argument validation, kernel choice and launch.
+// The declarations and their contract are in include/fa_attn.h.
+#include <hip/hip_runtime.h>
+#include <cmath>
+#include <cstdint>
+
+#include "fa_attn.h"
+#include "fa_internal.hpp"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+// Largest query-block count times B*H that still indexes a 1-D grid, with the
+// smallest query block any kernel uses (64 rows).
+constexpr int64_t kMaxGrid = (int64_t)INT32_MAX;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by the forward and backward entry points.
+int check_common(int64_t B, int64_t H, int64_t N, int64_t d, int mask, float scale, int dtype) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_SHAPE;
+  if (N > INT32_MAX / 2 || B > INT32_MAX || H > INT32_MAX) return FA_ERR_SHAPE;
+  if (B * H > INT32_MAX) return FA_ERR_SHAPE;
+  const int64_t bh = B * H;
+  if (bh > INT64_MAX / N || bh * N > INT64_MAX / 128 / 4) return FA_ERR_SHAPE;
+  if (((N + 63) / 64) * bh > kMaxGrid) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+             int64_t H, int64_t N, int64_t d, int mask, float scale, int dtype, void* stream) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_NULL;
+  const int st = check_common(B, H, N, d, mask, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
+    return FA_ERR_ALIGN;
+
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, mask == FA_MASK_CAUSAL, scale};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (dtype) {
+    case FA_BF16: e = fa::launch_fwd_bf16(a, s); break;
+    case FA_F16: e = fa::launch_fwd_f16(a, s); break;
+    default: e = fa::launch_fwd_f32(a, s); break;
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H or N is < 1 or the problem is too large to index";
+    case FA_ERR_DTYPE: return "unknown dtype";
+    case FA_ERR_MASK: return "unknown mask";
+    case FA_ERR_SCALE: return "scale is not finite";
+    case FA_ERR_UNSUPPORTED: return "head dimension must be 64 or 128";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "the HIP runtime rejected a launch";
+    case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int fa_abi_version(void) { return kAbiVersion; }
+
+}  // extern "C"

@@ -1,0 +1,27 @@
+// Internal declarations shared by the launch code of libfa_attn.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fa {
+
+// Arguments of one forward launch after validation.  Pointers are device
+// pointers to dense [B][H][N][d] arrays (lse: [B][H][N], may be null).
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t B, H, N, d;
+  bool causal;
+  float scale;
+};
+
+// Launchers return the hipError_t of the launch (hipSuccess when enqueued).
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+
+}  // namespace fa

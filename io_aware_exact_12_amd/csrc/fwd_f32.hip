@@ -1,0 +1,140 @@
+// Exact attention forward for fp32 inputs on gfx950.
+//
+// The fp32 path is held to a 1e-5 absolute error, also for sharp softmax rows
+// where a score of magnitude ~30 rounded to fp32 would already move exp() by
+// ~2e-6 relative.  So the scores, the running maximum, the exponentials and
+// the denominator are carried in fp64 (products of fp32 inputs are exact in
+// fp64), while the d-wide numerator is accumulated in fp32 from the same
+// fp32-rounded probabilities and rescale factors that enter the denominator,
+// so that their ratio does not drift.  Same schedule as the MFMA path -- query
+// rows resident, key/value tiles streamed through LDS, a running
+// (max, denominator, unnormalised numerator) per row rescaled by
+// alpha = exp(m_old - m_new) ("Flash Attention: IO-Aware Exact Attention",
+// section "Online softmax makes tiling exact") -- with one query row per lane
+// and scalar arithmetic.  It is the small-size, high-precision path, not a
+// throughput path.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "fa_internal.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int kRows = 64;   // query rows per workgroup (one wave, one row per lane)
+constexpr int kKeys = 16;   // keys per LDS tile
+
+template <int D, bool Causal>
+__global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict__ Q,
+                                                         const float* __restrict__ K,
+                                                         const float* __restrict__ V,
+                                                         float* __restrict__ O,
+                                                         float* __restrict__ LSE, int N,
+                                                         int n_qblocks, float scale) {
+  constexpr int kQStride = D + 1;  // odd stride: lanes reading their own row hit distinct banks
+  __shared__ float qs[kRows * kQStride];
+  __shared__ __attribute__((aligned(16))) float ks[kKeys * D];
+  __shared__ __attribute__((aligned(16))) float vs[kKeys * D];
+
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x / n_qblocks;
+  const int q0 = (blockIdx.x % n_qblocks) * kRows;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const float* Qh = Q + head_off;
+  const float* Kh = K + head_off;
+  const float* Vh = V + head_off;
+
+  for (int idx = lane; idx < kRows * D; idx += kRows) {
+    const int r = idx / D, col = idx % D;
+    qs[r * kQStride + col] = (q0 + r < N) ? Qh[(int64_t)(q0 + r) * D + col] : 0.f;
+  }
+
+  const int my_q = q0 + lane;
+  const int last_row = min(N, q0 + kRows) - 1;
+  const int n_keys = Causal ? last_row + 1 : N;
+
+  float acc[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) acc[i] = 0.f;
+  double m_run = -INFINITY, l_run = 0.0;
+  const double dscale = (double)scale;
+
+  for (int key0 = 0; key0 < n_keys; key0 += kKeys) {
+    __syncthreads();  // previous tile fully consumed (and Q staged on the first pass)
+    for (int idx = lane; idx < kKeys * D / 4; idx += kRows) {
+      const int r = (idx * 4) / D, col = (idx * 4) % D;
+      const bool ok = key0 + r < N;
+      const float4 kv = ok ? *reinterpret_cast<const float4*>(Kh + (int64_t)(key0 + r) * D + col)
+                           : float4{0.f, 0.f, 0.f, 0.f};
+      const float4 vv = ok ? *reinterpret_cast<const float4*>(Vh + (int64_t)(key0 + r) * D + col)
+                           : float4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<float4*>(ks + r * D + col) = kv;
+      *reinterpret_cast<float4*>(vs + r * D + col) = vv;
+    }
+    __syncthreads();
+
+    double t[kKeys];
+#pragma unroll
+    for (int j = 0; j < kKeys; ++j) t[j] = 0.0;
+    for (int col = 0; col < D; ++col) {
+      const double qv = (double)qs[lane * kQStride + col];
+#pragma unroll
+      for (int j = 0; j < kKeys; ++j) t[j] = __builtin_fma(qv, (double)ks[j * D + col], t[j]);
+    }
+    double tmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kKeys; ++j) {
+      const int key = key0 + j;
+      const bool hide = key >= N || (Causal && key > my_q);
+      t[j] = hide ? -INFINITY : t[j] * dscale;
+      tmax = fmax(tmax, t[j]);
+    }
+    const double m_new = fmax(m_run, tmax);
+    if (m_new == -INFINITY) continue;  // no visible key yet: state unchanged
+    const float alpha = (m_run == -INFINITY) ? 0.f : (float)exp(m_run - m_new);
+    float p[kKeys];
+    double psum = 0.0;
+#pragma unroll
+    for (int j = 0; j < kKeys; ++j) {
+      p[j] = (t[j] == -INFINITY) ? 0.f : (float)exp(t[j] - m_new);
+      psum += (double)p[j];
+    }
+    l_run = (double)alpha * l_run + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int col = 0; col < D; ++col) {
+      float a = alpha * acc[col];
+#pragma unroll
+      for (int j = 0; j < kKeys; ++j) a = __builtin_fmaf(p[j], vs[j * D + col], a);
+      acc[col] = a;
+    }
+  }
+
+  if (my_q < N) {
+    float* orow = O + head_off + (int64_t)my_q * D;
+#pragma unroll
+    for (int col = 0; col < D; ++col) orow[col] = (float)((double)acc[col] / l_run);
+    if (LSE != nullptr) LSE[(int64_t)bh * N + my_q] = (float)(m_run + log(l_run));
+  }
+}
+
+template <int D, bool Causal>
+hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+  const int N = (int)a.N;
+  const int n_qblocks = (N + kRows - 1) / kRows;
+  const dim3 grid((unsigned)(n_qblocks * a.B * a.H));
+  hipLaunchKernelGGL((fwd_f32_kernel<D, Causal>), grid, dim3(kRows), 0, stream,
+                     static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                     static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, N, n_qblocks,
+                     a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
+  if (a.d == 128) return a.causal ? launch<128, true>(a, s) : launch<128, false>(a, s);
+  return a.causal ? launch<64, true>(a, s) : launch<64, false>(a, s);
+}
+
+}  // namespace fa

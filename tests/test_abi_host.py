@@ -1,0 +1,103 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/fa_attn.h declares, and
+reject bad arguments with the documented status codes before it enqueues any
+work -- so these calls never reach the GPU.
+"""
+import ctypes
+import math
+import os
+
+import pytest
+
+import io_aware_exact_12_amd as fa
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_DTYPE, FA_ERR_MASK, FA_ERR_SCALE, \
+    FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_ALIGN = range(10)
+
+# fake, never-dereferenced addresses: validation fails before any use
+P = [0x10000 * (i + 1) for i in range(8)]
+
+
+def fwd(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=16, d=64, mask=0, scale=0.125,
+        dtype=fa.BF16):
+    return fa.attn_fwd_raw(q, k, v, o, lse, B, H, N, d, mask, scale, dtype, None)
+
+
+def test_library_exports_every_declared_symbol():
+    declared = fa.declared_symbols()
+    assert {"attn_fwd", "fa_status_str", "fa_abi_version"} <= set(declared)
+    lib = ctypes.CDLL(fa._binding.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert fa.lib().fa_abi_version() >= 1
+
+
+def test_status_strings():
+    for st in range(10):
+        assert fa.status_str(st)
+    assert fa.status_str(123) == "unknown status"
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_null_pointers(which):
+    assert fwd(**{which: None}) == FA_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=-5), dict(B=-1),
+                                dict(N=2**40), dict(B=2**31, H=2**31)])
+def test_bad_shapes(kw):
+    assert fwd(**kw) == FA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("d", [1, 32, 96, 127, 256])
+def test_unsupported_head_dim(d):
+    assert fwd(d=d) == FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", [-1, 3, 99])
+def test_bad_dtype(dtype):
+    assert fwd(dtype=dtype) == FA_ERR_DTYPE
+
+
+@pytest.mark.parametrize("mask", [-1, 2, 7])
+def test_bad_mask(mask):
+    assert fwd(mask=mask) == FA_ERR_MASK
+
+
+@pytest.mark.parametrize("scale", [math.nan, math.inf, -math.inf])
+def test_bad_scale(scale):
+    assert fwd(scale=scale) == FA_ERR_SCALE
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_misaligned(which):
+    assert fwd(**{which: P[5] + 2}) == FA_ERR_ALIGN
+
+
+def test_misaligned_lse():
+    assert fwd(lse=P[6] + 2) == FA_ERR_ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.attn_fwd(x, x, x)
+
+
+def test_header_documents_each_status():
+    text = open(fa._binding.HEADER).read()
+    for name in ["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_DTYPE", "FA_ERR_MASK",
+                 "FA_ERR_SCALE", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_ALIGN"]:
+        assert name in text
+
+
+def test_no_oracle_in_product_path():
+    """The package and its C sources never reference the oracle."""
+    pkg = os.path.dirname(fa.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(root, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
