@@ -85,9 +85,13 @@ def cpu_baseline(w, x, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # the GPU needs about half a second of load to reach steady clocks
+    ap.add_argument("--warmup", type=int, default=1500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (3 times), "
+                         "the reference kernel for scaling HBM byte counters, and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -104,6 +108,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy_mb:
+        n = args.calibrate_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n * 4, "launches": 3}), flush=True)
+        return
     w = workloads.WORKLOADS[WORKLOAD]
     x = workloads.make_inputs(w)
     dev = torch.device("cuda:0")

@@ -61,8 +61,9 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;          // two waves per SIMD, one workgroup per CU
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+constexpr int kStages = 4;        // LDS ring depth of the K and of the V tiles
 constexpr int kBN = 64;           // keys per tile
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -78,11 +79,48 @@ __device__ __forceinline__ i16x4 read_tr16(const lds_void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+// HBM -> LDS copy of 16 bytes per lane: lane l writes LDS bytes
+// [lds_addr + 16 l, +16) with the 16 bytes at byte offset voff of the buffer
+// rsrc (zeros when voff is past the buffer's size).  Issued as inline assembly
+// so the compiler does not treat every later LDS read as a possible alias of
+// the copy (it would wait for all copies in flight); completion is tracked by
+// the caller with explicit vmcnt waits before the workgroup barrier.  M0, which
+// carries the LDS address, is saved and restored around the copy.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+// Buffer resource (base, size in bytes) for raw, bounds-checked access.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = kRsrcFlags;
+  return r;
+}
+
 template <bool V> struct BoolTag { static constexpr bool value = V; };
 
 template <bool IsBf16> struct Elt;
 template <> struct Elt<true> {
   using scalar = __bf16;
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) float f2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 h2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
+  }
   using vec8 = bf16x8;
   using vec4 = bf16x4;
   static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
@@ -94,6 +132,11 @@ template <> struct Elt<true> {
 };
 template <> struct Elt<false> {
   using scalar = _Float16;
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) float f2;
+    typedef __attribute__((ext_vector_type(2))) _Float16 h2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
+  }
   using vec8 = f16x8;
   using vec4 = f16x4;
   static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
@@ -126,7 +169,7 @@ template <int D> struct Lds {
   static constexpr int kVStride = kRowBytes + 64;
   static constexpr int kKStage = kBN * kKStride;  // multiple of 1 KB
   static constexpr int kVStage = kBN * kVStride;  // multiple of 1 KB
-  static constexpr int kBytes = 2 * kKStage + 2 * kVStage;
+  static constexpr int kBytes = kStages * (kKStage + kVStage);
   static_assert(kKStage % 1024 == 0 && kVStage % 1024 == 0, "stages are whole 1 KB loads");
 };
 
@@ -145,40 +188,47 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 // Per-workgroup state and steps of the forward pass.  Everything here is
 // device-only; the kernel below only constructs it and runs the tile loop.
+//
+// Work unit of a wave: 32 query rows against 32-key sub-tiles (two per 64-key
+// LDS tile).  One sub-step u issues the score MFMAs of sub-tile u+1 together
+// with the exponentials of sub-tile u, then the PV MFMAs of sub-tile u
+// together with the mask and maximum of sub-tile u+1.
 template <bool IsBf16, int D, bool Causal>
 struct FwdBlock {
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using L = Lds<D>;
-  static constexpr int kKs = D / 16;  // MFMA k-steps for S^T = K Q^T
+  static constexpr int kKs = D / 16;  // MFMA k-steps of one 32x32 score block
   static constexpr int kDB = D / 32;  // 32-row blocks of O^T
   static constexpr int kRowBytes = L::kRowBytes;
   static constexpr int kKLoads = L::kKStage / 1024;  // wave-wide 1 KB LDS loads per K tile
   static constexpr int kVLoads = L::kVStage / 1024;
-  static constexpr int kKPerWave = (kKLoads + kWaves - 1) / kWaves;
-  static constexpr int kVPerWave = (kVLoads + kWaves - 1) / kWaves;
+  // K and V loads of one iteration are dealt round-robin to the waves
+  static constexpr int kSlots = (kKLoads + kVLoads + kWaves - 1) / kWaves;
   static constexpr uint32_t kNoData = 0x80000000u;  // past any buffer end: reads as zero
 
-  uint8_t* smem;  // K stages 0,1 then V stages 0,1
-  const uint16_t* Kh;
-  const uint16_t* Vh;
+  uint8_t* smem;  // K stages 0..kStages-1, then V stages
+  const uint8_t* k_ptr;  // K and V of this head (wave-uniform)
+  const uint8_t* v_ptr;
   uint32_t head_bytes;
-  int N, wave, lane, l32, g, q0, my_q, n_tiles, n_w;
+  int N, wave, lane, l32, g, q0, my_q, n_tiles, n_sub;
   float c, tau;
-  uint32_t k_src[kKPerWave], v_src[kVPerWave];
+  uint32_t src[kSlots];  // per-lane source byte offset of each load slot
   int k_base, v_base;
 
   vec8 qf[kKs];       // Q^T B operands: query my_q, d = 16 ks + 8 g + 0..7
   f32x16 acc[kDB];    // O^T: d = 32 db + 8 (r/4) + 4 g + r%4 of query my_q
   float m_ref;        // reference maximum the probabilities are taken against
   float l_part;       // this lane half's share of the denominator
-  f32x16 s_cur[2], s_nxt[2];
-  float mx_cur;
+  float mx_next;      // max over this lane half of the next sub-tile's scores
 
   __device__ __forceinline__ uint8_t* k_stage(int s) const { return smem + s * L::kKStage; }
   __device__ __forceinline__ uint8_t* v_stage(int s) const {
-    return smem + 2 * L::kKStage + s * L::kVStage;
+    return smem + kStages * L::kKStage + s * L::kVStage;
   }
+  // load slot i of this wave carries combined chunk w + kWaves*i: K chunks
+  // first, then V chunks
+  __device__ __forceinline__ int slot_chunk(int i) const { return wave + kWaves * i; }
 
   __device__ __forceinline__ void init(uint8_t* lds, const uint16_t* Q, const uint16_t* K,
                                        const uint16_t* V, int N_, int bh, int qb, float c_,
@@ -189,22 +239,24 @@ struct FwdBlock {
     tau = tau_;
     const int tid = threadIdx.x;
     lane = tid & 63;
-    wave = tid >> 6;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
     l32 = lane & 31;
     g = lane >> 5;
     const int64_t head_off = (int64_t)bh * N * D;
     head_bytes = (uint32_t)N * kRowBytes;
-    Kh = K + head_off;
-    Vh = V + head_off;
+    k_ptr = reinterpret_cast<const uint8_t*>(K + head_off);
+    v_ptr = reinterpret_cast<const uint8_t*>(V + head_off);
 
     const int q0_blk = qb * kBM;
     q0 = q0_blk + 32 * wave;
     my_q = q0 + l32;
     const int last_blk_row = min(N, q0_blk + kBM) - 1;
     n_tiles = Causal ? (last_blk_row / kBN + 1) : (N + kBN - 1) / kBN;
+    // 32-key sub-tiles this wave computes: all of them, or (causal) those
+    // whose first key is not beyond the wave's last row
     const int wave_last_row = min(N, q0 + 32) - 1;
-    // tiles this wave computes: all, or (causal) those up to its last row
-    n_w = q0 >= N ? 0 : (Causal ? min(n_tiles, wave_last_row / kBN + 1) : n_tiles);
+    const int all_sub = (N + 31) / 32;
+    n_sub = q0 >= N ? 0 : (Causal ? min(all_sub, wave_last_row / 32 + 1) : all_sub);
 
     // Q^T fragments; rows past N read as zeros through the buffer bounds
     const __amdgpu_buffer_rsrc_t q_rs =
@@ -217,28 +269,30 @@ struct FwdBlock {
       qf[ks] = __builtin_bit_cast(vec8, raw);
     }
 
-    // HBM -> LDS copies: load i of wave w fills LDS bytes [(w + 4 i) KB, +1 KB)
-    // of a stage, lane l writing 16 bytes at offset 16 l.  The per-lane source
-    // offset picks the (key, 16-byte chunk) that belongs in that slot; slots in
-    // row padding get an offset past the buffer end.
+    // HBM -> LDS copies.  A K tile is kKLoads and a V tile kVLoads wave-wide
+    // loads of 1 KB: load c fills LDS bytes [c KB, c KB + 1 KB) of its stage,
+    // lane l writing 16 bytes at offset 16 l.  The per-lane source offset picks
+    // the (key, 16-byte chunk) that belongs in that slot; slots in row padding
+    // get an offset past the buffer end, which reads as zeros.
 #pragma unroll
-    for (int i = 0; i < kKPerWave; ++i) {
-      const int byte = (wave + kWaves * i) * 1024 + lane * 16;
-      const int row = byte / L::kKStride, col = byte % L::kKStride;
-      k_src[i] = col < kRowBytes ? (uint32_t)(k_row_key(row) * kRowBytes + col) : kNoData;
+    for (int i = 0; i < kSlots; ++i) {
+      const int ci = slot_chunk(i);
+      if (ci < kKLoads) {
+        const int byte = ci * 1024 + lane * 16;
+        const int row = byte / L::kKStride, col = byte % L::kKStride;
+        src[i] = col < kRowBytes ? (uint32_t)(k_row_key(row) * kRowBytes + col) : kNoData;
+      } else {
+        const int byte = (ci - kKLoads) * 1024 + lane * 16;
+        const int row = byte / L::kVStride, col = byte % L::kVStride;
+        src[i] = col < kRowBytes ? (uint32_t)(row * kRowBytes + col) : kNoData;
+      }
     }
-#pragma unroll
-    for (int i = 0; i < kVPerWave; ++i) {
-      const int byte = (wave + kWaves * i) * 1024 + lane * 16;
-      const int row = byte / L::kVStride, col = byte % L::kVStride;
-      v_src[i] = col < kRowBytes ? (uint32_t)(row * kRowBytes + col) : kNoData;
-    }
-    // K operand reads (A of S^T): LDS row kb*32 + l32, 16-byte chunk 2*kk + g.
+    // K operand reads (A of S^T): LDS row 32 h + l32 of the tile, 16-byte chunk 2 kk + g.
     k_base = l32 * L::kKStride + g * 16;
-    // V operand reads (A of O^T, transpose reads): for key step t, d-block db
-    // and half h, lane s of each 16-lane group points at key 16t + 8g + 4h + s/4,
-    // columns 32 db + 16 (group & 1) + 4 (s & 3) .. +3; the transpose hands each
-    // lane the four keys of its own d column.
+    // V operand reads (A of O^T, transpose reads): for 16-key step t of the
+    // tile, d-block db and half hh, lane s of each 16-lane group points at key
+    // 16 t + 8 g + 4 hh + s/4, columns 32 db + 16 (group & 1) + 4 (s & 3) .. +3;
+    // the transpose hands each lane the four keys of its own d column.
     const int grp = lane >> 4, s16 = lane & 15;
     v_base = (8 * g + (s16 >> 2)) * L::kVStride + 2 * (16 * (grp & 1) + 4 * (s16 & 3));
 
@@ -246,77 +300,87 @@ struct FwdBlock {
     for (int i = 0; i < kDB; ++i) acc[i] = f32x16{};
     m_ref = -INFINITY;
     l_part = 0.f;
-    mx_cur = -INFINITY;
+    mx_next = -INFINITY;
   }
 
-  __device__ __forceinline__ void load_k(int j, int s) const {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)Kh, 0, (int)head_bytes, kRsrcFlags);
-    const uint32_t base = (uint32_t)j * kBN * kRowBytes;
+  // Issue this wave's share of the copies of K tile jk into K stage sk and of
+  // V tile jv into V stage sv (tiles past the end are skipped); returns the
+  // number of loads issued.
+  __device__ __forceinline__ int load_tiles(int jk, int sk, int jv, int sv) const {
+    const bool do_k = jk < n_tiles, do_v = jv < n_tiles;
+    // resources based at the tile's first row, bounded by the rows left in the
+    // head: per-lane offsets are tile-relative and padding slots (offset
+    // kNoData >= 2^31) fall outside any bound
+    constexpr uint32_t kTileBytes = kBN * kRowBytes;
+    const i32x4 tk = make_rsrc(k_ptr + (size_t)jk * kTileBytes, head_bytes - jk * kTileBytes);
+    const i32x4 tv = make_rsrc(v_ptr + (size_t)jv * kTileBytes, head_bytes - jv * kTileBytes);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;
+    int issued = 0;
 #pragma unroll
-    for (int i = 0; i < kKPerWave; ++i)
-      if (wave + kWaves * i < kKLoads)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void*)(k_stage(s) + (wave + kWaves * i) * 1024), 16,
-            k_src[i] == kNoData ? kNoData : base + k_src[i], 0, 0, 0);
-  }
-  __device__ __forceinline__ void load_v(int j, int s) const {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)Vh, 0, (int)head_bytes, kRsrcFlags);
-    const uint32_t base = (uint32_t)j * kBN * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < kVPerWave; ++i)
-      if (wave + kWaves * i < kVLoads)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void*)(v_stage(s) + (wave + kWaves * i) * 1024), 16,
-            v_src[i] == kNoData ? kNoData : base + v_src[i], 0, 0, 0);
-  }
-  static __device__ __forceinline__ void wait_loads_and_sync() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS copies have landed
-    __syncthreads();
-  }
-
-  // S^T of the tile in K stage s
-  __device__ __forceinline__ void compute_s(int s, f32x16 (&st)[2]) const {
-    const uint8_t* kt = k_stage(s) + k_base;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      st[kb] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < kKs; ++kk) {
-        const vec8 a = *reinterpret_cast<const vec8*>(kt + kb * 32 * L::kKStride + kk * 32);
-        st[kb] = E::mfma(a, qf[kk], st[kb]);
+    for (int i = 0; i < kSlots; ++i) {
+      const int ci = slot_chunk(i);
+      if (ci < kKLoads) {
+        if (do_k) {
+          dma16(tk, lds0 + (uint32_t)(sk * L::kKStage + ci * 1024), src[i]);
+          ++issued;
+        }
+      } else if (ci < kKLoads + kVLoads) {
+        if (do_v) {
+          dma16(tv, lds0 + (uint32_t)(kStages * L::kKStage + sv * L::kVStage + (ci - kKLoads) * 1024),
+                src[i]);
+          ++issued;
+        }
       }
+    }
+    return issued;
+  }
+  // Wait until at most n of this wave's HBM -> LDS loads are outstanding.
+  static __device__ __forceinline__ void wait_vm(int n) {
+    static_assert(kSlots <= 8, "vmcnt immediates below cover up to 8 loads");
+    switch (n) {  // s_waitcnt immediates: vmcnt = n, expcnt and lgkmcnt unchecked
+      case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+      case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+      case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+      case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+      case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+      case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+      case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+      case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+      default: __builtin_amdgcn_s_waitcnt(0x0F78); break;
     }
   }
 
-  __device__ __forceinline__ bool tile_masked(int j) const {
-    return (Causal && j * kBN + kBN - 1 > q0) || (j * kBN + kBN > N);
+  __device__ __forceinline__ bool sub_masked(int u) const {
+    return (Causal && 32 * u + 31 > q0) || (32 * u + 32 > N);
   }
 
-  // Hide the keys of tile j this lane's query may not see (causal diagonal,
-  // sequence end) and return the max over this lane half's 32 scores.
+  // Score block of sub-tile 0 (prologue), masked, and its max.
+  __device__ __forceinline__ void first_scores(f32x16& st) {
+    const uint8_t* kt = k_stage(0) + k_base;
+    st = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < kKs; ++kk)
+      st = E::mfma(*reinterpret_cast<const vec8*>(kt + kk * 32), qf[kk], st);
+    mx_next = sub_masked(0) ? mask_max<true>(0, st) : mask_max<false>(0, st);
+  }
+
+  // Hide keys of sub-tile u that this lane's query may not see (causal
+  // diagonal, sequence end); return the max over this lane half's 16 scores.
   template <bool kMasked>
-  __device__ __forceinline__ float mask_and_max(int j, f32x16 (&st)[2]) const {
-    // register r of lane half g holds key j*64 + kb*32 + 16*(r>>3) + 8g + (r&7);
-    // it is visible iff that offset is <= lim
-    const int lim = (Causal ? min(my_q, N - 1) : N - 1) - j * kBN - 8 * g;
+  __device__ __forceinline__ float mask_max(int u, f32x16& st) const {
+    // register r of lane half g holds key 32 u + 16 (r >> 3) + 8 g + (r & 7)
+    const int lim = (Causal ? min(my_q, N - 1) : N - 1) - 32 * u - 8 * g;
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (kMasked) {
-          const int off = kb * 32 + 16 * (r >> 3) + (r & 7);
-          st[kb][r] = off > lim ? -INFINITY : st[kb][r];
-        }
-        mx = fmaxf(mx, st[kb][r]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      if (kMasked) st[r] = (16 * (r >> 3) + (r & 7)) > lim ? -INFINITY : st[r];
+      mx = fmaxf(mx, st[r]);
+    }
     return mx;
   }
 
   // Move the reference maximum only when some row grew by more than tau; the
-  // branch is wave-uniform and rarely taken after the first tile.
+  // branch is wave-uniform and rarely taken after the first sub-tile.
   __device__ __forceinline__ void maybe_rescale(float mx) {
     if (__builtin_amdgcn_ballot_w64(mx > m_ref + tau) != 0) {
       const float m_row = fmaxf(m_ref, xhalf_max(mx));
@@ -329,95 +393,133 @@ struct FwdBlock {
     }
   }
 
-  // p = exp2(c s - c m_ref) for the tile's 32 scores per lane (hidden scores
-  // are -inf and give 0), summed into l and rounded into the four P^T
-  // operands: step t covers keys 16t..16t+15, lane half g holds 8 of them.
-  __device__ __forceinline__ void exp_tile(const f32x16 (&st)[2], vec8 (&pb)[4]) {
+  // Sub-step u, written in issue order.  Phase 1: the score MFMAs of sub-tile
+  // u+1 (K operand reads running up to four MFMAs ahead) interleaved with the
+  // exponentials of sub-tile u.  Phase 2: the PV MFMAs of sub-tile u (V
+  // transpose reads two MFMAs ahead) interleaved with the mask and max of
+  // sub-tile u+1.  Scheduling fences keep the VALU work in the shadow of the
+  // MFMAs.  k_st / v_st: LDS stages of the K tile holding sub-tile u+1 and of
+  // the V tile holding sub-tile u.  On a wave's last sub-tile the scores of
+  // "sub-tile u+1" are still formed from whatever that K stage holds and then
+  // ignored, so that every sub-step runs the same branch-free phase 1.
+  __device__ __forceinline__ void phase1(int u, int k_st, const f32x16& cur, f32x16& nxt,
+                                         u32x4 (&pw)[2]) {
+    static_assert(kKs == 8 || kKs == 4, "head dim 128 or 64");
+    constexpr int kPerMfma = 16 / kKs;  // scores exponentiated per score MFMA
+    constexpr int kRing = 4;
+    const uint8_t* kt = k_stage(k_st) + k_base + ((u + 1) & 1) * 32 * L::kKStride;
     const float neg_mc = (m_ref == -INFINITY) ? 0.f : -m_ref * c;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    vec8 ka[kRing];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f32x8 pf;
+    for (int i = 0; i < kRing; ++i) ka[i] = *reinterpret_cast<const vec8*>(kt + i * 32);
+    float ps[2] = {0.f, 0.f};
+    float p_even = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t >> 1][8 * (t & 1) + e], c, neg_mc));
-        pf[e] = p;
-        ps[e & 3] += p;
+    for (int i = 0; i < kKs; ++i) {
+      nxt = E::mfma(ka[i % kRing], qf[i], i == 0 ? f32x16{} : nxt);
+      if (i + kRing < kKs) ka[i % kRing] = *reinterpret_cast<const vec8*>(kt + (i + kRing) * 32);
+#pragma unroll
+      for (int w = 0; w < kPerMfma; ++w) {
+        const int e = i * kPerMfma + w;  // score register 0..15
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[e], c, neg_mc));
+        ps[e & 1] += p;
+        if (e & 1)
+          pw[e >> 3][(e & 7) >> 1] = E::pack2(p_even, p);
+        else
+          p_even = p;
       }
-      pb[t] = __builtin_convertvector(pf, vec8);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    l_part += ps[0] + ps[1];
   }
 
-  // O^T += V^T P^T for tile j
-  __device__ __forceinline__ void pv_tile(int j, const vec8 (&pb)[4]) {
-    const uint8_t* vt = v_stage(j & 1) + v_base;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint8_t* vp = vt + 16 * t * L::kVStride + 64 * db;
-        const auto lo = E::read_tr((const lds_void*)vp);
-        const auto hi = E::read_tr((const lds_void*)(vp + 4 * L::kVStride));
-        const vec8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[db] = E::mfma(a, pb[t], acc[db]);
-      }
-  }
-
-  // One step for tile j when tile j+1 also has work: the score MFMAs of tile
-  // j+1 are issued together with the exponentials of tile j, then the PV
-  // MFMAs of tile j together with the mask and max of tile j+1.
   template <bool kMaskNext>
-  __device__ __forceinline__ void pipelined_step(int j) {
-    vec8 pb[4];
-    compute_s((j + 1) & 1, s_nxt);
-    exp_tile(s_cur, pb);
-    pv_tile(j, pb);
-    mx_cur = mask_and_max<kMaskNext>(j + 1, s_nxt);
-    s_cur[0] = s_nxt[0];
-    s_cur[1] = s_nxt[1];
-  }
-
-  __device__ __forceinline__ void last_step(int j) {
-    vec8 pb[4];
-    exp_tile(s_cur, pb);
-    pv_tile(j, pb);
-  }
-
-  __device__ __forceinline__ void run() {
-    // prologue: K0, V0, K1 in LDS; S0 computed and masked
-    load_k(0, 0);
-    load_v(0, 0);
-    if (n_tiles > 1) load_k(1, 1);
-    wait_loads_and_sync();
-    if (n_w > 0) {
-      compute_s(0, s_cur);
-      mx_cur = tile_masked(0) ? mask_and_max<true>(0, s_cur) : mask_and_max<false>(0, s_cur);
-    }
-    __syncthreads();  // K stage 0 is refilled in iteration 0
-
-    // K of tile j+2 and V of tile j+1 stream in while tile j is consumed
-    for (int j = 0; j < n_tiles; ++j) {
-      if (j + 2 < n_tiles) load_k(j + 2, j & 1);
-      if (j + 1 < n_tiles) load_v(j + 1, (j + 1) & 1);
-      if (j < n_w) {
-        maybe_rescale(mx_cur);
-        if (j + 1 < n_w) {
-          if (tile_masked(j + 1))
-            pipelined_step<true>(j);
-          else
-            pipelined_step<false>(j);
-        } else {
-          last_step(j);
-        }
+  __device__ __forceinline__ void phase2(int u, int v_st, f32x16& nxt, const u32x4 (&pw)[2]) {
+    constexpr int kMfmaPV = 2 * kDB;
+    const uint8_t* vt = v_stage(v_st) + v_base + (u & 1) * 32 * L::kVStride;
+    auto v_frag = [&](int i) {
+      const int db = i >> 1, tt = i & 1;
+      const uint8_t* vp = vt + 16 * tt * L::kVStride + 64 * db;
+      const auto lo = E::read_tr((const lds_void*)vp);
+      const auto hi = E::read_tr((const lds_void*)(vp + 4 * L::kVStride));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // register r of lane half g holds key 32 (u+1) + 16 (r >> 3) + 8 g + (r & 7)
+    const int lim = (Causal ? min(my_q, N - 1) : N - 1) - 32 * (u + 1) - 8 * g;
+    constexpr int kMaxPerMfma = 16 / kMfmaPV;
+    vec8 va[2];
+    va[0] = v_frag(0);
+    va[1] = v_frag(1);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMfmaPV; ++i) {
+      acc[i >> 1] = E::mfma(va[i & 1], __builtin_bit_cast(vec8, pw[i & 1]), acc[i >> 1]);
+      if (i + 2 < kMfmaPV) va[i & 1] = v_frag(i + 2);
+#pragma unroll
+      for (int w = 0; w < kMaxPerMfma; ++w) {
+        const int r = i * kMaxPerMfma + w;
+        if (kMaskNext) nxt[r] = (16 * (r >> 3) + (r & 7)) > lim ? -INFINITY : nxt[r];
+        mx = fmaxf(mx, nxt[r]);
       }
-      wait_loads_and_sync();
+      __builtin_amdgcn_sched_barrier(0);
     }
+    mx_next = mx;
+  }
+
+  // One sub-step u, if this wave has work for it.  Only each wave's last
+  // sub-tile (the causal diagonal, or the ragged end of the sequence) needs a
+  // mask; iterations that cannot reach one use the mask-free variant.
+  template <bool kMaskable>
+  __device__ __forceinline__ void sub(int u, int k_st, int v_st, const f32x16& cur, f32x16& nxt) {
+    if (u >= n_sub) return;
+    maybe_rescale(mx_next);
+    u32x4 pw[2];  // P^T operands (keys 16 tt + 8 g + 0..7 of sub-tile u) as packed pairs
+    phase1(u, k_st, cur, nxt, pw);
+    if (kMaskable && sub_masked(u + 1))
+      phase2<true>(u, v_st, nxt, pw);
+    else
+      phase2<false>(u, v_st, nxt, pw);
+  }
+
+  template <bool kMaskable>
+  __device__ __forceinline__ void iteration(int j, f32x16& sa, f32x16& sb) {
+    const int s0 = j & 3, s1 = (j + 1) & 3, s2 = (j + 2) & 3, s3 = (j + 3) & 3;
+    const int issued = load_tiles(j + 3, s3, j + 2, s2);
+    sub<kMaskable>(2 * j, s0, s0, sa, sb);      // next sub-tile: second half of K tile j
+    sub<kMaskable>(2 * j + 1, s1, s0, sb, sa);  // next sub-tile: first half of K tile j+1
+    wait_vm(issued);
+    __syncthreads();
+  }
+
+  // Tile loop.  LDS holds rings of kStages K tiles and kStages V tiles.
+  // Iteration j consumes sub-tiles 2j and 2j+1: it reads K tiles j (second
+  // half) and j+1 (first half) and V tile j.  It issues K tile j+3 (into the
+  // stage K tile j-1 left) and V tile j+2 (into the stage V tile j-2 left) and,
+  // before its closing barrier, waits only for the loads issued one iteration
+  // earlier, so every copy has two iterations to land.
+  __device__ __forceinline__ void run(int q0_blk) {
+    static_assert(kStages == 4, "the ring arithmetic below assumes four stages");
+    f32x16 sa, sb;
+    // prologue: K0, V0, K1 resident; K2, V1 in flight; scores of sub-tile 0
+    load_tiles(0, 0, 0, 0);
+    load_tiles(1, 1, n_tiles, 0);
+    const int n1 = load_tiles(2, 2, 1, 1);
+    wait_vm(n1);
+    __syncthreads();
+    if (n_sub > 0) first_scores(sa);
+
+    // first iteration in which some wave's next sub-tile may need a mask
+    const int all_sub = (N + 31) / 32;
+    const int j_mask = Causal ? max(0, (q0_blk / 32 - 1) / 2)
+                              : ((N % 32) ? max(0, (all_sub - 2) / 2) : n_tiles);
+    int j = 0;
+    for (; j < min(j_mask, n_tiles); ++j) iteration<false>(j, sa, sb);
+    for (; j < n_tiles; ++j) iteration<true>(j, sa, sb);
   }
 
   // O = a / l once; LSE = ln(sum) of the scaled scores
   __device__ __forceinline__ void store(uint16_t* O, float* LSE, int bh) {
-    if (n_w == 0) return;
+    if (n_sub == 0) return;
     const float l_tot = xhalf_sum(l_part);
     const float inv = 1.0f / l_tot;
     if (my_q >= N) return;
@@ -439,7 +541,7 @@ struct FwdBlock {
 };
 
 template <bool IsBf16, int D, bool Causal>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(
+__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int BH, int n_qblocks, float c,
     float tau, uint32_t q_sign) {
@@ -450,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(
   if (Causal) qb = n_qblocks - 1 - qb;
   FwdBlock<IsBf16, D, Causal> blk;
   blk.init(smem, Q, K, V, N, bh, qb, c, tau, q_sign);
-  blk.run();
+  blk.run(qb * kBM);
   blk.store(O, LSE, bh);
 }
 
