@@ -56,7 +56,7 @@ enum fa_status {
   FA_ERR_DTYPE = 3,       /* dtype is not one of enum fa_dtype                  */
   FA_ERR_MASK = 4,        /* mask is not one of enum fa_mask                    */
   FA_ERR_SCALE = 5,       /* scale is NaN or infinite                           */
-  FA_ERR_UNSUPPORTED = 6, /* head dimension d is not 64 or 128                  */
+  FA_ERR_UNSUPPORTED = 6, /* head dimension d is not 64 or 128 (or fp32 backward) */
   FA_ERR_WORKSPACE = 7,   /* backward workspace missing or too small            */
   FA_ERR_HIP = 8,         /* the HIP runtime rejected a launch                  */
   FA_ERR_ALIGN = 9        /* a tensor pointer is not 16-byte aligned            */
@@ -88,6 +88,47 @@ enum fa_status {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int64_t B, int64_t H, int64_t N, int64_t d,
              int mask, float scale, int dtype, void* stream);
+
+/*
+ * attn_bwd -- backward pass by recomputation.
+ *
+ * Gradients of L = sum(O * dout) with respect to q, k and v for the forward
+ * pass above.  No N x N matrix is stored or read: score and probability tiles
+ * are recomputed from q, k and the forward's lse ("Flash Attention: IO-Aware
+ * Exact Attention", section "Storage, arithmetic and IO are separate
+ * quantities"; Road to Intelligence "FlashAttention", section "The trick that
+ * makes tiling possible").  With P = exp(scale q k^T - lse):
+ *     dv = P^T dout,  dP = dout v^T,  dS = P * (dP - rowsum(P * dP)),
+ *     dq = scale dS k,  dk = scale dS^T q.
+ *
+ *   q, k, v, dout     [B][H][N][d] inputs of type dtype.
+ *   o                 [B][H][N][d] forward output of type dtype.  Checked like
+ *                     the other pointers but not read: the row term
+ *                     D_i = sum_j P_ij dP_ij (= dout_i . o_i in exact
+ *                     arithmetic) is formed from the recomputed P and dP in
+ *                     fp32, which keeps o's rounding out of dS.
+ *   lse               [B][H][N] fp32 natural-log log-sum-exp returned by
+ *                     attn_fwd for the same q, k, v, mask and scale.
+ *   dq, dk, dv        [B][H][N][d] outputs of type dtype (must not overlap the
+ *                     inputs or each other).
+ *   workspace         device memory of at least attn_bwd_workspace_bytes()
+ *                     bytes, 16-byte aligned, owned by the caller; its
+ *                     contents are scratch on return.
+ *   mask, scale, B, H, N, d, stream: as for attn_fwd.
+ *   dtype             FA_F16 or FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED).
+ *
+ * Deterministic: no atomics are used.  FA_ERR_WORKSPACE if workspace is NULL
+ * or too small.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv,
+             int64_t B, int64_t H, int64_t N, int64_t d,
+             int mask, float scale, int dtype, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/* Bytes of workspace attn_bwd needs for these sizes (4 * B * H * N today);
+ * 0 if the sizes, d or dtype are invalid. */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_str(int status);

@@ -38,6 +38,11 @@ def lib():
         L.attn_fwd.restype = ctypes.c_int
         L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+        L.attn_bwd.restype = ctypes.c_int
+        L.attn_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                          ctypes.c_int, vp, ctypes.c_size_t, vp]
+        L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.fa_status_str.restype = ctypes.c_char_p
         L.fa_status_str.argtypes = [ctypes.c_int]
         L.fa_abi_version.restype = ctypes.c_int
@@ -60,6 +65,17 @@ def declared_symbols(header: str = HEADER):
 def attn_fwd_raw(q, k, v, o, lse, B, H, N, d, mask, scale, dtype, stream):
     """Direct call of the C entry point with integer pointers; returns the status."""
     return lib().attn_fwd(q, k, v, o, lse, B, H, N, d, mask, scale, dtype, stream)
+
+
+def attn_bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, scale, dtype, ws, ws_bytes,
+                 stream):
+    """Direct call of the C entry point with integer pointers; returns the status."""
+    return lib().attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, scale, dtype, ws,
+                          ws_bytes, stream)
+
+
+def bwd_workspace_bytes(B, H, N, d, dtype_code):
+    return lib().attn_bwd_workspace_bytes(B, H, N, d, dtype_code)
 
 
 def _torch_dtype_code(t):
@@ -102,3 +118,43 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=N
     if st != 0:
         raise FaError(st, "attn_fwd")
     return out, (lse if return_lse else None)
+
+
+def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, *,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(o * dout) for o, lse = attn_fwd(q, k, v, causal, scale).
+
+    All tensors are contiguous device tensors; q, k, v, o, dout share one
+    [B, H, N, d] shape and dtype (float16 or bfloat16), lse is float32 [B, H, N].
+    ``workspace`` (a uint8 device tensor) is allocated when not given.
+    """
+    import torch
+    shape = q.shape
+    for t in (k, v, o, dout):
+        if t.shape != shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, dout must share one shape and dtype")
+    for t in (q, k, v, o, dout, lse):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous device tensors")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape[:3]):
+        raise ValueError("lse must be float32 [B, H, N]")
+    B, H, N, d = shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _torch_dtype_code(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = bwd_workspace_bytes(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                        MASK_CAUSAL if causal else MASK_NONE, float(scale), code,
+                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                        stream.cuda_stream)
+    if st != 0:
+        raise FaError(st, "attn_bwd")
+    return dq, dk, dv

@@ -57,6 +57,35 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK) return 0;
+  return fa::bwd_workspace_bytes(B, H, N);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+             int64_t d, int mask, float scale, int dtype, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr ||
+      lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return FA_ERR_NULL;
+  const int st = check_common(B, H, N, d, mask, scale, dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < fa::bwd_workspace_bytes(B, H, N))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return FA_ERR_ALIGN;
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask == FA_MASK_CAUSAL, scale, workspace};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f16(a, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -65,7 +94,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_MASK: return "unknown mask";
     case FA_ERR_SCALE: return "scale is not finite";
-    case FA_ERR_UNSUPPORTED: return "head dimension must be 64 or 128";
+    case FA_ERR_UNSUPPORTED: return "unsupported: head dimension must be 64 or 128 (backward: fp16/bf16 only)";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "the HIP runtime rejected a launch";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";

@@ -1,0 +1,417 @@
+// Exact attention backward for bf16 / fp16 on gfx950 (MI355X), using MFMA.
+//
+// The forward pass keeps only O and the per-row log-sum-exp; the backward pass
+// recomputes each tile of scores and probabilities from Q, K and that
+// statistic instead of reading a stored N x N matrix ("Flash Attention:
+// IO-Aware Exact Attention", section "Storage, arithmetic and IO are separate
+// quantities"; Road to Intelligence "FlashAttention", section "The trick that
+// makes tiling possible").  With S = scale Q K^T, P = exp(S - LSE) and dO the
+// output gradient, the gradient of a row softmax followed by P V is
+//
+//     dV = P^T dO,   dP = dO V^T,   D_i = sum_c dO_ic O_ic,
+//     dS = P * (dP - D),   dQ = scale dS K,   dK = scale dS^T Q.
+//
+// D_i equals sum_j P_ij dP_ij.  Computing it as rowsum(dO * O) from the
+// stored low-precision O puts O's rounding (2^-9 relative in bf16) straight
+// into dS = P (dP - D), where dP and D nearly cancel on a row's dominant
+// keys; so D is formed from the recomputed P and dP in fp32 instead.
+//
+// Two kernels, no atomics, so the result is deterministic:
+//   * bwd_dq:     a workgroup keeps 128 query rows resident (Q^T and dO^T in
+//                 registers) and streams 64-key tiles of K and V through LDS
+//                 twice: pass 1 accumulates D = sum_j P dP and stores it in
+//                 the caller's workspace, pass 2 accumulates dQ^T;
+//   * bwd_dkdv:   a workgroup keeps 128 keys resident (K^T and V^T as MFMA
+//                 operands in registers, dK^T and dV^T accumulated in
+//                 registers) and streams 64-query tiles of Q, dO, LSE and D
+//                 through LDS.  It runs after bwd_dq on the same stream.
+// Both main kernels use the 32x32x16 MFMA with the resident index in the lane
+// column, so per-row (or per-key) scalars stay lane-local.  Tile rows are
+// stored in LDS in the permuted order that makes a 32-row block's MFMA output
+// hold 8 consecutive rows per lane half, so P and dS are reused as MFMA
+// operands straight from registers; the transposed operands (Q^T, dO^T, K^T)
+// come from the gfx950 LDS transpose read.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "fa_internal.hpp"
+#include "mfma_common.hpp"
+
+namespace fa {
+namespace {
+
+using namespace mfma;
+
+constexpr int kW = 4;              // waves per workgroup
+constexpr int kThr = 64 * kW;
+constexpr int kRes = 32 * kW;      // resident rows (keys or queries) per workgroup
+constexpr int kT = 64;             // streamed tile rows
+
+// LDS row of logical index `idx` (0..63) of a streamed tile: the inverse of
+// the permutation in which MFMA output row 8b + 4g + j of each 32-row half
+// holds index 16 (b >> 1) + 8 g + 4 (b & 1) + j.
+__device__ __forceinline__ int tile_row(int idx) {
+  const int half = idx & 32, kk = idx & 31;
+  const int j = kk & 3, b1 = (kk >> 2) & 1, g = (kk >> 3) & 1, bh = (kk >> 4) & 1;
+  return half + 16 * bh + 8 * b1 + 4 * g + j;
+}
+
+// LDS geometry of a streamed tile of 64 rows: 16 bytes of padding per row
+// keep the 16-byte MFMA operand reads conflict free.
+template <int D> struct Tile {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kStride = kRowBytes + 16;
+  static constexpr int kBytes = kT * kStride;
+  static constexpr int kChunks = kT * kRowBytes / 16;  // 16-byte chunks per tile
+  static constexpr int kPerThread = kChunks / kThr;
+  static_assert(kPerThread * kThr == kChunks, "tile must split evenly over the threads");
+};
+
+// Copy rows [row0, row0 + 64) of a [rows][D] tensor into LDS in permuted row
+// order (rows past `rows` read as zeros), staged through registers.
+template <int D>
+__device__ __forceinline__ void stage_tile(uint8_t* lds, const uint16_t* base, int rows, int row0) {
+  using T = Tile<D>;
+  constexpr int kCh = T::kRowBytes / 16;  // chunks per row
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)((uint32_t)rows * T::kRowBytes), kRsrcFlags);
+  u32x4 v[T::kPerThread];
+#pragma unroll
+  for (int i = 0; i < T::kPerThread; ++i) {
+    const int c = threadIdx.x + i * kThr;
+    const int r = c / kCh, ch = c % kCh;
+    v[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (row0 + r) * T::kRowBytes + ch * 16, 0, 0));
+  }
+#pragma unroll
+  for (int i = 0; i < T::kPerThread; ++i) {
+    const int c = threadIdx.x + i * kThr;
+    const int r = c / kCh, ch = c % kCh;
+    *reinterpret_cast<u32x4*>(lds + tile_row(r) * T::kStride + ch * 16) = v[i];
+  }
+}
+
+// Offsets of the transpose reads that gather an A operand whose rows are the
+// D dimension and whose 16-wide k dimension runs over 16 consecutive tile
+// rows (k step t): lane s of each 16-lane group points at logical row
+// 16 t + 8 g + 4 h + s/4 (h = 0, 1 for the two halves of the 8 elements),
+// columns 32 db + 16 (group & 1) + 4 (s & 3) .. + 3.  With the permuted row
+// order the LDS row is 16 t + 8 h + 4 g + s/4.
+template <int D>
+__device__ __forceinline__ int tr_base(int lane) {
+  const int g = lane >> 5, grp = lane >> 4, s16 = lane & 15;
+  return (4 * g + (s16 >> 2)) * Tile<D>::kStride + 2 * (16 * (grp & 1) + 4 * (s16 & 3));
+}
+template <bool IsBf16, int D>
+__device__ __forceinline__ typename Elt<IsBf16>::vec8 tr_frag(const uint8_t* tile, int base, int t,
+                                                              int db) {
+  using E = Elt<IsBf16>;
+  const uint8_t* p = tile + base + 16 * t * Tile<D>::kStride + 64 * db;
+  const auto lo = E::read_tr((const lds_void*)p);
+  const auto hi = E::read_tr((const lds_void*)(p + 8 * Tile<D>::kStride));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Resident operand of one lane: row `row` of a [rows][D] tensor as the MFMA
+// B operand (d = 16 ks + 8 g + 0..7), zero past `rows`, optionally sign-flipped.
+template <bool IsBf16, int D>
+__device__ __forceinline__ void load_resident(typename Elt<IsBf16>::vec8 (&f)[D / 16],
+                                              const uint16_t* base, int rows, int row, int g,
+                                              uint32_t sign) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)((uint32_t)rows * 2 * D), kRsrcFlags);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 raw = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, row * 2 * D + (2 * ks + g) * 16, 0, 0));
+    raw ^= sign;
+    f[ks] = __builtin_bit_cast(typename Elt<IsBf16>::vec8, raw);
+  }
+}
+
+// Store one lane's column of a transposed accumulator (rows = d) as row `row`
+// of a [rows][D] tensor, multiplied by `mul` and rounded to the element type.
+template <bool IsBf16, int D>
+__device__ __forceinline__ void store_row(uint16_t* base, int row, int g, const f32x16 (&acc)[D / 32],
+                                          float mul) {
+  using E = Elt<IsBf16>;
+  typedef __attribute__((ext_vector_type(4))) typename E::scalar h4_t;
+  uint16_t* orow = base + (int64_t)row * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const f32x4 v4 = {acc[db][4 * gq] * mul, acc[db][4 * gq + 1] * mul,
+                        acc[db][4 * gq + 2] * mul, acc[db][4 * gq + 3] * mul};
+      *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * gq + 4 * g) =
+          __builtin_bit_cast(u32x2, __builtin_convertvector(v4, h4_t));
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV
+// Per wave: 32 resident keys kw0 .. kw0 + 31 (lane column = key).  For each
+// 32-query half of a streamed 64-query tile:
+//   S  = Q K^T and dP = dO V^T   (A = Q / dO rows from LDS, B = K^T / V^T resident)
+//   P  = exp2(c S - LSE2), dS = P (dP - D)         (per element, query in the register index)
+//   dV^T += dO^T P,  dK^T += Q^T dS                (A = dO^T / Q^T by transpose reads)
+template <bool IsBf16, int D, bool Causal>
+__global__ __launch_bounds__(kThr, 1) void bwd_dkdv(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BH, float c, float dk_mul,
+    uint32_t q_sign) {
+  using E = Elt<IsBf16>;
+  using vec8 = typename E::vec8;
+  using T = Tile<D>;
+  constexpr int kKs = D / 16, kDB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[T::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t do_lds[T::kBytes];
+  __shared__ __attribute__((aligned(16))) float lse_lds[kT];
+  __shared__ __attribute__((aligned(16))) float d_lds[kT];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int bh = blockIdx.x % BH, kblk = blockIdx.x / BH;  // heaviest (earliest keys) first
+  const int64_t head = (int64_t)bh * N * D;
+  const int k0 = kblk * kRes, kw0 = k0 + 32 * wave, my_k = kw0 + l32;
+
+  vec8 kf[kKs], vf[kKs];
+  load_resident<IsBf16, D>(kf, K + head, N, my_k, g, 0u);
+  load_resident<IsBf16, D>(vf, V + head, N, my_k, g, 0u);
+  f32x16 dk[kDB], dv[kDB];
+#pragma unroll
+  for (int i = 0; i < kDB; ++i) dk[i] = dv[i] = f32x16{};
+
+  const int n_tiles = (N + kT - 1) / kT;
+  const int t_first = Causal ? k0 / kT : 0;  // earlier query tiles see none of these keys
+  const int trb = tr_base<D>(lane);
+  const float* lse_h = LSE + (int64_t)bh * N;
+  const float* d_h = Dsum + (int64_t)bh * N;
+  const bool wave_live = kw0 < N;
+
+  for (int it = t_first; it < n_tiles; ++it) {
+    const int qt0 = it * kT;
+    __syncthreads();  // previous tile consumed
+    stage_tile<D>(q_lds, Q + head, N, qt0);
+    stage_tile<D>(do_lds, dO + head, N, qt0);
+    if (threadIdx.x < kT) {
+      const int qi = qt0 + threadIdx.x;
+      // log2-domain LSE; rows past N get +inf so that their probabilities are 0
+      lse_lds[threadIdx.x] = qi < N ? lse_h[qi] * 1.4426950408889634f : INFINITY;
+      d_lds[threadIdx.x] = qi < N ? d_h[qi] : 0.f;
+    }
+    __syncthreads();
+    if (q_sign) {  // negative scale: S uses -Q (exact), and so does dK (with |scale|)
+      for (int c2 = threadIdx.x; c2 < T::kBytes / 16; c2 += kThr) {
+        *reinterpret_cast<u32x4*>(q_lds + c2 * 16) ^= q_sign;
+      }
+      __syncthreads();
+    }
+    if (!wave_live) continue;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int qs0 = qt0 + 32 * qh;  // first query of this half
+      if (Causal && qs0 + 31 < kw0) continue;  // every query before every key of the wave
+      if (qs0 >= N) continue;
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const uint8_t* qrow = q_lds + (32 * qh + l32) * T::kStride + 16 * g;
+      const uint8_t* orow = do_lds + (32 * qh + l32) * T::kStride + 16 * g;
+#pragma unroll
+      for (int kk = 0; kk < kKs; ++kk) {
+        s = E::mfma(*reinterpret_cast<const vec8*>(qrow + 32 * kk), kf[kk], s);
+        dp = E::mfma(*reinterpret_cast<const vec8*>(orow + 32 * kk), vf[kk], dp);
+      }
+      // register e of lane half g holds query qs0 + 16 (e >> 3) + 8 g + (e & 7)
+      const float* lq = lse_lds + 32 * qh + 8 * g;
+      const float* dq = d_lds + 32 * qh + 8 * g;
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        l4[i] = *reinterpret_cast<const f32x4*>(lq + 16 * (i >> 1) + 4 * (i & 1));
+        d4[i] = *reinterpret_cast<const f32x4*>(dq + 16 * (i >> 1) + 4 * (i & 1));
+      }
+      u32x4 pw[2], sw[2];
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        float p2[2], ds2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = e + u;
+          const int qi = qs0 + 16 * (r >> 3) + 8 * g + (r & 7);
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l4[r >> 2][r & 3]));
+          if (Causal) p = (my_k > qi) ? 0.f : p;
+          p = (my_k >= N) ? 0.f : p;
+          p2[u] = p;
+          ds2[u] = p * (dp[r] - d4[r >> 2][r & 3]);
+        }
+        pw[e >> 3][(e & 7) >> 1] = E::pack2(p2[0], p2[1]);
+        sw[e >> 3][(e & 7) >> 1] = E::pack2(ds2[0], ds2[1]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries (two k steps of 16)
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          dv[db] = E::mfma(tr_frag<IsBf16, D>(do_lds + 32 * qh * T::kStride, trb, t, db),
+                           __builtin_bit_cast(vec8, pw[t]), dv[db]);
+          dk[db] = E::mfma(tr_frag<IsBf16, D>(q_lds + 32 * qh * T::kStride, trb, t, db),
+                           __builtin_bit_cast(vec8, sw[t]), dk[db]);
+        }
+    }
+  }
+  if (!wave_live || my_k >= N) return;
+  store_row<IsBf16, D>(dK + head, my_k, g, dk, dk_mul);
+  store_row<IsBf16, D>(dV + head, my_k, g, dv, 1.f);
+}
+
+// ---------------------------------------------------------------- D and dQ
+// Per wave: 32 resident queries (lane column = query).  For each 32-key half
+// of a streamed 64-key tile:
+//   S^T = K Q^T and dP^T = V dO^T (A = K / V rows from LDS, B = Q^T / dO^T resident)
+//   P^T = exp2(c S^T - LSE2)                           (LSE2: lane scalar)
+//   pass 1:  D += sum over the keys of P^T dP^T
+//   pass 2:  dS^T = P^T (dP^T - D),  dQ^T += K^T dS^T  (A = K^T by transpose reads)
+template <bool IsBf16, int D, bool Causal>
+__global__ __launch_bounds__(kThr, 1) void bwd_dq(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dsum,
+    uint16_t* __restrict__ dQ, int N, int BH, int n_qblocks, float c, float dq_mul,
+    uint32_t q_sign) {
+  using E = Elt<IsBf16>;
+  using vec8 = typename E::vec8;
+  using T = Tile<D>;
+  constexpr int kKs = D / 16, kDB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[T::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[T::kBytes];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int bh = blockIdx.x % BH;
+  int qb = blockIdx.x / BH;
+  if (Causal) qb = n_qblocks - 1 - qb;  // heaviest first
+  const int64_t head = (int64_t)bh * N * D;
+  const int q0 = qb * kRes, qw0 = q0 + 32 * wave, my_q = qw0 + l32;
+
+  vec8 qf[kKs], of[kKs];
+  load_resident<IsBf16, D>(qf, Q + head, N, my_q, g, q_sign);
+  load_resident<IsBf16, D>(of, dO + head, N, my_q, g, 0u);
+  const bool q_ok = my_q < N;
+  const float lse2 = q_ok ? LSE[(int64_t)bh * N + my_q] * 1.4426950408889634f : INFINITY;
+
+  const int last_row = min(N, q0 + kRes) - 1;
+  const int n_tiles = Causal ? last_row / kT + 1 : (N + kT - 1) / kT;
+  const int trb = tr_base<D>(lane);
+  const bool wave_live = qw0 < N;
+
+  // S^T and dP^T of key half kh of the staged tile, and P^T with the masks
+  // applied; register e of lane half g holds key ks0 + 16 (e >> 3) + 8 g + (e & 7).
+  auto scores = [&](int kh, int ks0, f32x16& p, f32x16& dp) {
+    f32x16 s = f32x16{};
+    dp = f32x16{};
+    const uint8_t* krow = k_lds + (32 * kh + l32) * T::kStride + 16 * g;
+    const uint8_t* vrow = v_lds + (32 * kh + l32) * T::kStride + 16 * g;
+#pragma unroll
+    for (int kk = 0; kk < kKs; ++kk) {
+      s = E::mfma(*reinterpret_cast<const vec8*>(krow + 32 * kk), qf[kk], s);
+      dp = E::mfma(*reinterpret_cast<const vec8*>(vrow + 32 * kk), of[kk], dp);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kj = ks0 + 16 * (r >> 3) + 8 * g + (r & 7);
+      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+      p[r] = (kj >= N || (Causal && kj > my_q)) ? 0.f : pr;
+    }
+  };
+
+  // ---- pass 1: D = sum_j P_ij dP_ij
+  float dpart = 0.f;
+  for (int it = 0; it < n_tiles; ++it) {
+    const int kt0 = it * kT;
+    __syncthreads();
+    stage_tile<D>(k_lds, K + head, N, kt0);
+    stage_tile<D>(v_lds, V + head, N, kt0);
+    __syncthreads();
+    if (!wave_live) continue;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int ks0 = kt0 + 32 * kh;
+      if ((Causal && ks0 > qw0 + 31) || ks0 >= N) continue;
+      f32x16 p, dp;
+      scores(kh, ks0, p, dp);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dpart = __builtin_fmaf(p[r], dp[r], dpart);
+    }
+  }
+  const float dsum = xhalf_sum(dpart);
+  if (wave_live && q_ok && g == 0) Dsum[(int64_t)bh * N + my_q] = dsum;
+
+  // ---- pass 2: dQ^T += K^T dS^T
+  f32x16 dq[kDB];
+#pragma unroll
+  for (int i = 0; i < kDB; ++i) dq[i] = f32x16{};
+  for (int it = 0; it < n_tiles; ++it) {
+    const int kt0 = it * kT;
+    __syncthreads();
+    stage_tile<D>(k_lds, K + head, N, kt0);
+    stage_tile<D>(v_lds, V + head, N, kt0);
+    __syncthreads();
+    if (!wave_live) continue;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int ks0 = kt0 + 32 * kh;
+      if ((Causal && ks0 > qw0 + 31) || ks0 >= N) continue;
+      f32x16 p, dp;
+      scores(kh, ks0, p, dp);
+      u32x4 sw[2];
+#pragma unroll
+      for (int e = 0; e < 16; e += 2)
+        sw[e >> 3][(e & 7) >> 1] = E::pack2(p[e] * (dp[e] - dsum), p[e + 1] * (dp[e + 1] - dsum));
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          dq[db] = E::mfma(tr_frag<IsBf16, D>(k_lds + 32 * kh * T::kStride, trb, t, db),
+                           __builtin_bit_cast(vec8, sw[t]), dq[db]);
+    }
+  }
+  if (!wave_live || !q_ok) return;
+  store_row<IsBf16, D>(dQ + head, my_q, g, dq, dq_mul);
+}
+
+template <bool IsBf16, int D, bool Causal>
+hipError_t launch(const BwdArgs& a, hipStream_t st) {
+  const int N = (int)a.N;
+  const int BH = (int)(a.B * a.H);
+  const int nblk = (N + kRes - 1) / kRes;
+  // |scale| * log2(e); a zero scale is run as the limit scale -> 0+
+  const float c = a.scale != 0.f ? __builtin_fabsf(a.scale) * 1.4426950408889634f : 1e-30f;
+  const uint32_t q_sign = a.scale < 0.f ? 0x80008000u : 0u;
+  const auto* q = static_cast<const uint16_t*>(a.q);
+  const auto* k = static_cast<const uint16_t*>(a.k);
+  const auto* v = static_cast<const uint16_t*>(a.v);
+  const auto* dout = static_cast<const uint16_t*>(a.dout);
+  float* dsum = static_cast<float*>(a.workspace);
+  // dQ (and D into the workspace) first; dK, dV read D afterwards on the same stream
+  hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st, q,
+                     k, v, dout, a.lse, dsum, static_cast<uint16_t*>(a.dq), N, BH, nblk, c, a.scale,
+                     q_sign);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dK = scale dS^T Q; with a sign-flipped Q for negative scales this is |scale| dS^T (-Q)
+  hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
+                     q, k, v, dout, a.lse, dsum, static_cast<uint16_t*>(a.dk),
+                     static_cast<uint16_t*>(a.dv), N, BH, c, __builtin_fabsf(a.scale), q_sign);
+  return hipGetLastError();
+}
+
+template <bool IsBf16>
+hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
+  if (a.d == 128) return a.causal ? launch<IsBf16, 128, true>(a, s) : launch<IsBf16, 128, false>(a, s);
+  return a.causal ? launch<IsBf16, 64, true>(a, s) : launch<IsBf16, 64, false>(a, s);
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) { return (size_t)(B * H * N) * 4; }
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) { return dispatch<true>(a, s); }
+hipError_t launch_bwd_f16(const BwdArgs& a, hipStream_t s) { return dispatch<false>(a, s); }
+
+}  // namespace fa

@@ -19,9 +19,30 @@ struct FwdArgs {
   float scale;
 };
 
+// Arguments of one backward launch after validation.  workspace holds at
+// least bwd_workspace_bytes(B, H, N) bytes of device memory.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t B, H, N, d;
+  bool causal;
+  float scale;
+  void* workspace;
+};
+
 // Launchers return the hipError_t of the launch (hipSuccess when enqueued).
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_f16(const BwdArgs& a, hipStream_t s);
+size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N);
 
 }  // namespace fa

@@ -101,3 +101,33 @@ def test_no_oracle_in_product_path():
             if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 text = open(os.path.join(root, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+# ---------------------------------------------------------------- backward validation
+
+def bwd(q=P[0], k=P[1], v=P[2], o=P[3], do=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[0] + 0x100000,
+        B=1, H=1, N=16, d=64, mask=0, scale=0.125, dtype=fa.BF16, ws=P[1] + 0x100000, ws_bytes=1 << 20):
+    return fa.attn_bwd_raw(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, mask, scale, dtype, ws, ws_bytes,
+                           None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"])
+def test_bwd_null_pointers(which):
+    assert bwd(**{which: None}) == FA_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,status", [(dict(B=0), FA_ERR_SHAPE), (dict(N=-1), FA_ERR_SHAPE),
+                                       (dict(d=96), FA_ERR_UNSUPPORTED), (dict(dtype=7), FA_ERR_DTYPE),
+                                       (dict(mask=3), FA_ERR_MASK), (dict(scale=math.nan), FA_ERR_SCALE),
+                                       (dict(dtype=fa.F32), FA_ERR_UNSUPPORTED),
+                                       (dict(ws=None), FA_ERR_WORKSPACE),
+                                       (dict(ws_bytes=4 * 16 - 1), FA_ERR_WORKSPACE),
+                                       (dict(dq=P[6] + 4), FA_ERR_ALIGN), (dict(lse=P[5] + 2), FA_ERR_ALIGN)])
+def test_bwd_validation(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_bwd_workspace_query():
+    assert fa.bwd_workspace_bytes(4, 16, 4096, 128, fa.BF16) == 4 * 4 * 16 * 4096
+    assert fa.bwd_workspace_bytes(0, 16, 4096, 128, fa.BF16) == 0
+    assert fa.bwd_workspace_bytes(1, 1, 16, 96, fa.BF16) == 0
