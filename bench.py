@@ -4,10 +4,14 @@ One step = one ``attn_fwd`` call over the long-context causal workload
 (B=1, H=16, N=8192, d=128, bf16, scale 1/sqrt(128)) with seeded synthetic
 N(0, 1) inputs already resident in device memory.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd]
 
 The reported throughput counts algorithmic FLOPs only: 4 * d * (visible query-key
 pairs) * B * H, i.e. the two matrix products over the causal triangle.
+
+The same line carries, under "attn_bwd", the backward pass timed the same way
+on its own workload (B=4, H=16, N=4096, d=128, bf16, causal), counted as
+10 * d * pairs * B * H algorithmic FLOPs (S and dP recomputed, dV, dQ, dK).
 """
 from __future__ import annotations
 
@@ -28,7 +32,7 @@ METRIC = "attention fwd TFLOP/s (bf16, causal, T=8192, d=128) and % of MFMA peak
 WORKLOAD = "long_causal_bf16"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
-KERNEL_SOURCES = ("fwd_mfma.hip",)
+KERNEL_SOURCES = ("fwd_mfma.hip", "mfma_common.hpp")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fwd_long_causal_bf16_traffic.md")
 
 
@@ -82,6 +86,63 @@ def cpu_baseline(w, x, budget_s=12.0):
                       f"full N x N scores computed, causal-visible FLOPs counted), {dt:.1f} s"}
 
 
+def time_graph(step, steps, warmup, torch):
+    """Capture `steps` calls of step() in one HIP graph, replay it for the
+    warm-up, then time one replay with events; returns ms per call."""
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            step()
+    torch.cuda.synchronize()
+    n_rep = max(1, -(-warmup // steps))  # warm-up calls, rounded up to whole graphs
+    for _ in range(n_rep):
+        graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, n_rep * steps
+
+
+def bwd_record(fa, workloads, torch, steps, warmup):
+    """Backward pass on its own workload, timed like the forward."""
+    w = workloads.WORKLOADS["fwd_bwd_causal_bf16"]
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (torch.from_numpy(x[n]).to(dev).to(torch.bfloat16).contiguous()
+                   for n in ("q", "k", "v", "do"))
+    o, lse = fa.attn_fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d, fa.BF16), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        fa.attn_bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                    workspace=ws, stream=torch.cuda.current_stream(dev))
+
+    # default warm-up: about half a second, as for the forward
+    ms, warm = time_graph(step, steps, warmup, torch)
+    assert all(torch.isfinite(t).all().item() for t in (dq, dk, dv))
+    flops = w.bwd_flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"metric": "attention bwd TFLOP/s (bf16, causal, T=4096, d=128)",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warm,
+            "ms_per_step": round(ms, 5),
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                       "mask": "causal", "scale": w.scale,
+                       "inputs": "Q, K, V, dO i.i.d. N(0,1) rounded to bf16, seed 5"},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "kernels": "bwd_dq + bwd_dkdv (one call)",
+                         "algorithmic_flops_per_launch": flops}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,6 +150,9 @@ def main():
     # the GPU needs about half a second of load to reach steady clocks
     ap.add_argument("--warmup", type=int, default=1500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--bwd-steps", type=int, default=40)
+    ap.add_argument("--bwd-warmup", type=int, default=300)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times), "
                          "the reference kernel for scaling HBM byte counters, and exit")
@@ -131,27 +195,8 @@ def main():
         fa.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse,
                     stream=torch.cuda.current_stream(dev))
 
-    step()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _ in range(args.steps):
-            step()
-    torch.cuda.synchronize()
-    n_rep = max(1, -(-args.warmup // args.steps))  # warmup steps, rounded up to whole graphs
-    for _ in range(n_rep):
-        graph.replay()
-    torch.cuda.synchronize()
+    ms, warm = time_graph(step, args.steps, args.warmup, torch)
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
-
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    graph.replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
 
     flops = w.fwd_flops()
     tflops = flops / (ms * 1e-3) / 1e12
@@ -162,7 +207,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": n_rep * args.steps,
+        "warmup": warm,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -181,6 +226,8 @@ def main():
                      "algorithmic_bytes_per_launch": w.fwd_bytes(),
                      "kernel_source_sha256_16": kernel_source_hash()},
     }
+    if not args.no_bwd:
+        record["attn_bwd"] = bwd_record(fa, workloads, torch, args.bwd_steps, args.bwd_warmup)
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(record), flush=True)

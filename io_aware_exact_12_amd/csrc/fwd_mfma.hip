@@ -117,8 +117,10 @@ struct FwdBlock {
   int N, wave, lane, l32, g, q0, my_q, n_tiles, n_sub;
   float c;
   uint32_t src_k[kFullK], src_v[kFullV], src_x;  // per-lane source offsets of the copies
-  int x_kind;    // extra copy: 0 = K chunk, 1 = V chunk, 2 = zeros into the sink
-  int x_chunk;   // its chunk index within the tile
+  // The extra copy writes LDS byte x_off + (K stage offset & x_kmask) +
+  // (V stage offset & x_vmask), reading the V tile iff x_vmask != 0 (a copy
+  // into the sink reads nothing: its source offset is past every buffer).
+  uint32_t x_off, x_kmask, x_vmask;
   int k_base, v_base;
 
   vec8 qf[kKs];       // Q^T B operands: query my_q, d = 16 ks + 8 g + 0..7
@@ -130,9 +132,6 @@ struct FwdBlock {
   u32x4 p_prev[2];    // probabilities of the previous block (B operands)
   vec8 vfr[kPV];      // V^T operands of the previous block
 
-  __device__ __forceinline__ uint32_t lds_addr(int byte) const {
-    return (uint32_t)(uintptr_t)(lds_void*)smem + (uint32_t)byte;
-  }
   __device__ __forceinline__ const uint8_t* k_stage(int s) const { return smem + s * L::kKStage; }
   __device__ __forceinline__ const uint8_t* v_stage(int s) const {
     return smem + kStages * L::kKStage + s * L::kVStage;
@@ -189,17 +188,24 @@ struct FwdBlock {
     for (int i = 0; i < kFullK; ++i) src_k[i] = chunk_src(false, wave + kWaves * i);
 #pragma unroll
     for (int i = 0; i < kFullV; ++i) src_v[i] = chunk_src(true, wave + kWaves * i);
-    if (wave < kRemV) {
-      x_kind = 1;
-      x_chunk = kFullV * kWaves + wave;
-    } else if (wave < kRemV + kRemK) {
-      x_kind = 0;
-      x_chunk = kFullK * kWaves + wave - kRemV;
-    } else {
-      x_kind = 2;
-      x_chunk = 0;
+    if (wave < kRemV) {  // a chunk of the V remainder
+      const int ci = kFullV * kWaves + wave;
+      x_off = ci * 1024;
+      x_kmask = 0u;
+      x_vmask = ~0u;
+      src_x = chunk_src(true, ci);
+    } else if (wave < kRemV + kRemK) {  // a chunk of the K remainder
+      const int ci = kFullK * kWaves + wave - kRemV;
+      x_off = ci * 1024;
+      x_kmask = ~0u;
+      x_vmask = 0u;
+      src_x = chunk_src(false, ci);
+    } else {  // zeros into the sink
+      x_off = L::kSink;
+      x_kmask = 0u;
+      x_vmask = 0u;
+      src_x = kNoData;
     }
-    src_x = x_kind == 2 ? kNoData : chunk_src(x_kind == 1, x_chunk);
 
     // K operand reads (A of S^T): LDS row 32 h + l32 of the tile, 16-byte chunk 2 kk + g.
     k_base = l32 * L::kKStride + g * 16;
@@ -219,24 +225,29 @@ struct FwdBlock {
 
   // Copy K tile jk into K stage sk and V tile jv into V stage sv (a tile at
   // or past n_tiles copies zeros: its buffer is empty).  Every wave issues
-  // exactly kCopies copies.
+  // exactly kCopies copies, in one asm statement that saves and restores M0
+  // once.
   __device__ __forceinline__ void load_tiles(int jk, int sk, int jv, int sv) const {
     constexpr uint32_t kTileBytes = kBN * kRowBytes;
     const uint32_t k_left = jk < n_tiles ? head_bytes - (uint32_t)jk * kTileBytes : 0u;
     const uint32_t v_left = jv < n_tiles ? head_bytes - (uint32_t)jv * kTileBytes : 0u;
     const i32x4 tk = make_rsrc(k_ptr + (size_t)jk * kTileBytes, k_left);
     const i32x4 tv = make_rsrc(v_ptr + (size_t)jv * kTileBytes, v_left);
-    const int k_st = sk * L::kKStage;
-    const int v_st = kStages * L::kKStage + sv * L::kVStage;
+    i32x4 tx;
 #pragma unroll
-    for (int i = 0; i < kFullK; ++i)
-      dma16(tk, lds_addr(k_st + (wave + kWaves * i) * 1024), src_k[i]);
-#pragma unroll
-    for (int i = 0; i < kFullV; ++i)
-      dma16(tv, lds_addr(v_st + (wave + kWaves * i) * 1024), src_v[i]);
-    const int x_byte = x_kind == 0 ? k_st + x_chunk * 1024
-                                   : (x_kind == 1 ? v_st + x_chunk * 1024 : L::kSink);
-    dma16(x_kind == 1 ? tv : tk, lds_addr(x_byte), src_x);
+    for (int w = 0; w < 4; ++w) tx[w] = (int)(((uint32_t)tk[w] & ~x_vmask) | ((uint32_t)tv[w] & x_vmask));
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)smem + (uint32_t)(wave * 1024);
+    const uint32_t k_st = base + (uint32_t)(sk * L::kKStage);
+    const uint32_t v_st = base + (uint32_t)(kStages * L::kKStage + sv * L::kVStage);
+    const uint32_t x_lds = (uint32_t)(uintptr_t)(lds_void*)smem + x_off +
+                           ((uint32_t)(sk * L::kKStage) & x_kmask) +
+                           ((uint32_t)(kStages * L::kKStage + sv * L::kVStage) & x_vmask);
+    static_assert(kFullK == kFullV && (kFullK == 1 || kFullK == 2), "copy groups of 3 or 5");
+    if constexpr (kFullK == 2)
+      dma_group5(tk, tv, tx, k_st, k_st + kWaves * 1024, v_st, v_st + kWaves * 1024, x_lds,
+                 src_k[0], src_k[1], src_v[0], src_v[1], src_x);
+    else
+      dma_group3(tk, tv, tx, k_st, v_st, x_lds, src_k[0], src_v[0], src_x);
   }
   // Wait until at most one tile step's copies of this wave are outstanding.
   static __device__ __forceinline__ void wait_older_copies() {

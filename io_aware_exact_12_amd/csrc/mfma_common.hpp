@@ -54,6 +54,41 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_addr, uint
       : "memory");
 }
 
+// Groups of such copies in one asm statement (M0 saved and restored once):
+// copies 0.. use rsrc a (K), then b (V), the last one rsrc x.
+__device__ __forceinline__ void dma_group5(const i32x4& a, const i32x4& b, const i32x4& x,
+                                           uint32_t l0, uint32_t l1, uint32_t l2, uint32_t l3,
+                                           uint32_t l4, uint32_t v0, uint32_t v1, uint32_t v2,
+                                           uint32_t v3, uint32_t v4) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\tbuffer_load_dwordx4 %9, %1, 0 offen lds\n\t"
+      "s_mov_b32 m0, %5\n\tbuffer_load_dwordx4 %10, %1, 0 offen lds\n\t"
+      "s_mov_b32 m0, %6\n\tbuffer_load_dwordx4 %11, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %7\n\tbuffer_load_dwordx4 %12, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %8\n\tbuffer_load_dwordx4 %13, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(a), "s"(b), "s"(x), "s"(l0), "s"(l1), "s"(l2), "s"(l3), "s"(l4), "v"(v0), "v"(v1),
+        "v"(v2), "v"(v3), "v"(v4)
+      : "memory");
+}
+__device__ __forceinline__ void dma_group3(const i32x4& a, const i32x4& b, const i32x4& x,
+                                           uint32_t l0, uint32_t l1, uint32_t l2, uint32_t v0,
+                                           uint32_t v1, uint32_t v2) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\tbuffer_load_dwordx4 %7, %1, 0 offen lds\n\t"
+      "s_mov_b32 m0, %5\n\tbuffer_load_dwordx4 %8, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %6\n\tbuffer_load_dwordx4 %9, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(a), "s"(b), "s"(x), "s"(l0), "s"(l1), "s"(l2), "v"(v0), "v"(v1), "v"(v2)
+      : "memory");
+}
+
 // Buffer resource (base, size in bytes) for raw, bounds-checked access.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
