@@ -47,69 +47,98 @@ constexpr int kThr = 64 * kW;
 constexpr int kRes = 32 * kW;      // resident rows (keys or queries) per workgroup
 constexpr int kT = 64;             // streamed tile rows
 
-// LDS row of logical index `idx` (0..63) of a streamed tile: the inverse of
-// the permutation in which MFMA output row 8b + 4g + j of each 32-row half
-// holds index 16 (b >> 1) + 8 g + 4 (b & 1) + j.
+// LDS row of logical index `idx` (0..63) of a streamed tile: MFMA output row
+// 8b + 4g + j of each 32-row half holds index 16 (b >> 1) + 8 g + 4 (b & 1) + j,
+// i.e. bits 2 and 3 of the index are swapped (the map is its own inverse).
 __device__ __forceinline__ int tile_row(int idx) {
   const int half = idx & 32, kk = idx & 31;
   const int j = kk & 3, b1 = (kk >> 2) & 1, g = (kk >> 3) & 1, bh = (kk >> 4) & 1;
   return half + 16 * bh + 8 * b1 + 4 * g + j;
 }
 
-// LDS geometry of a streamed tile of 64 rows: 16 bytes of padding per row
-// keep the 16-byte MFMA operand reads conflict free.
-template <int D> struct Tile {
+// A streamed tile of 64 rows of D elements, rows in the permuted order above,
+// no padding.  The 16-byte chunks of LDS row r are XOR-swizzled by swz(r) so
+// that both ways the tile is read are free of bank conflicts: 16 lanes reading
+// one chunk of 16 consecutive rows (row operands), and 32 lanes reading 64
+// contiguous bytes of 4 consecutive rows (transpose reads).
+template <int D> struct STile {
   static constexpr int kRowBytes = 2 * D;
-  static constexpr int kStride = kRowBytes + 16;
-  static constexpr int kBytes = kT * kStride;
-  static constexpr int kChunks = kT * kRowBytes / 16;  // 16-byte chunks per tile
-  static constexpr int kPerThread = kChunks / kThr;
-  static_assert(kPerThread * kThr == kChunks, "tile must split evenly over the threads");
+  static constexpr int kBytes = kT * kRowBytes;
+  static constexpr int kCopies = kBytes / 1024;  // wave-wide 1 KB copies per tile
+  static constexpr int kPerWave = kCopies / kW;
+  static_assert(kPerWave * kW == kCopies, "tile copies split evenly over the waves");
+  static __device__ __forceinline__ int swz(int r) {
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
+  // byte offset in the tile of 16-byte chunk c of LDS row r
+  static __device__ __forceinline__ int at(int r, int c) { return r * kRowBytes + 16 * (c ^ swz(r)); }
+  // Tile-relative source offsets of this wave's copies: copy i of wave w fills
+  // LDS bytes [(w + kW i) KB, +1 KB), lane l the 16 bytes at 16 l.
+  static __device__ __forceinline__ void sources(int wave, int lane, uint32_t (&src)[kPerWave]) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int byte = (wave + kW * i) * 1024 + 16 * lane;
+      const int r = byte / kRowBytes, phys = (byte % kRowBytes) / 16;
+      src[i] = (uint32_t)(tile_row(r) * kRowBytes + 16 * (phys ^ swz(r)));
+    }
+  }
 };
 
-// Copy rows [row0, row0 + 64) of a [rows][D] tensor into LDS in permuted row
-// order (rows past `rows` read as zeros), staged through registers.
-template <int D>
-__device__ __forceinline__ void stage_tile(uint8_t* lds, const uint16_t* base, int rows, int row0) {
-  using T = Tile<D>;
-  constexpr int kCh = T::kRowBytes / 16;  // chunks per row
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)((uint32_t)rows * T::kRowBytes), kRsrcFlags);
-  u32x4 v[T::kPerThread];
-#pragma unroll
-  for (int i = 0; i < T::kPerThread; ++i) {
-    const int c = threadIdx.x + i * kThr;
-    const int r = c / kCh, ch = c % kCh;
-    v[i] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (row0 + r) * T::kRowBytes + ch * 16, 0, 0));
-  }
-#pragma unroll
-  for (int i = 0; i < T::kPerThread; ++i) {
-    const int c = threadIdx.x + i * kThr;
-    const int r = c / kCh, ch = c % kCh;
-    *reinterpret_cast<u32x4*>(lds + tile_row(r) * T::kStride + ch * 16) = v[i];
-  }
+// HBM -> LDS copy of 4 bytes per lane: lane l writes LDS bytes
+// [lds_addr + 4 l, +4) with the dword at byte offset voff of rsrc (zero past
+// its size).  Same M0 handling as dma16.
+__device__ __forceinline__ void dma4(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory");
 }
 
-// Offsets of the transpose reads that gather an A operand whose rows are the
-// D dimension and whose 16-wide k dimension runs over 16 consecutive tile
-// rows (k step t): lane s of each 16-lane group points at logical row
-// 16 t + 8 g + 4 h + s/4 (h = 0, 1 for the two halves of the 8 elements),
-// columns 32 db + 16 (group & 1) + 4 (s & 3) .. + 3.  With the permuted row
-// order the LDS row is 16 t + 8 h + 4 g + s/4.
+// Copy rows [row0, row0 + 64) of a [rows][D] tensor (zeros past `rows`) into
+// the swizzled tile at LDS address lds_addr: this wave's share.
 template <int D>
-__device__ __forceinline__ int tr_base(int lane) {
-  const int g = lane >> 5, grp = lane >> 4, s16 = lane & 15;
-  return (4 * g + (s16 >> 2)) * Tile<D>::kStride + 2 * (16 * (grp & 1) + 4 * (s16 & 3));
+__device__ __forceinline__ void copy_tile(uint32_t lds_addr, const uint16_t* base, int rows, int row0,
+                                          int wave, const uint32_t (&src)[STile<D>::kPerWave]) {
+  using T = STile<D>;
+  const int left = rows - row0;
+  const i32x4 rs = make_rsrc(base + (int64_t)row0 * D, left > 0 ? (uint32_t)left * T::kRowBytes : 0u);
+#pragma unroll
+  for (int i = 0; i < T::kPerWave; ++i) dma16(rs, lds_addr + (uint32_t)((wave + kW * i) * 1024), src[i]);
 }
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
+// Wait for all of this wave's HBM -> LDS copies.
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Transpose-read A operand whose rows are the D dimension and whose 16-wide k
+// dimension runs over 16 consecutive logical tile rows (k step t, d block db):
+// lane s of each 16-lane group reads logical row 16 t + 8 g + 4 h + s/4
+// (LDS row 16 t + 8 h + 4 g + s/4), columns 32 db + 16 (group & 1) + 4 (s & 3)
+// .. + 3, for h = 0 (elements 0..3) and h = 1 (elements 4..7).
 template <bool IsBf16, int D>
-__device__ __forceinline__ typename Elt<IsBf16>::vec8 tr_frag(const uint8_t* tile, int base, int t,
-                                                              int db) {
+__device__ __forceinline__ typename Elt<IsBf16>::vec8 tr_frag(const uint8_t* tile, int lane, int t, int db) {
   using E = Elt<IsBf16>;
-  const uint8_t* p = tile + base + 16 * t * Tile<D>::kStride + 64 * db;
-  const auto lo = E::read_tr((const lds_void*)p);
-  const auto hi = E::read_tr((const lds_void*)(p + 8 * Tile<D>::kStride));
+  using T = STile<D>;
+  const int g = lane >> 5, grp = lane >> 4, s16 = lane & 15;
+  const int col = 2 * (16 * (grp & 1) + 4 * (s16 & 3)) + 64 * db;  // byte column
+  const int r0 = 16 * t + 4 * g + (s16 >> 2);
+  const auto lo = E::read_tr((const lds_void*)(tile + T::at(r0, col >> 4) + (col & 15)));
+  const auto hi = E::read_tr((const lds_void*)(tile + T::at(r0 + 8, col >> 4) + (col & 15)));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Row operand (A of a 32x32x16 MFMA) for k step kk: LDS row r, chunk 2 kk + g.
+template <bool IsBf16, int D>
+__device__ __forceinline__ typename Elt<IsBf16>::vec8 row_frag(const uint8_t* tile, int r, int g, int kk) {
+  return *reinterpret_cast<const typename Elt<IsBf16>::vec8*>(tile + STile<D>::at(r, 2 * kk + g));
 }
 
 // Resident operand of one lane: row `row` of a [rows][D] tensor as the MFMA
@@ -149,33 +178,44 @@ __device__ __forceinline__ void store_row(uint16_t* base, int row, int g, const 
 }
 
 // ---------------------------------------------------------------- dK, dV
-// Per wave: 32 resident keys kw0 .. kw0 + 31 (lane column = key).  For each
-// 32-query half of a streamed 64-query tile:
+// Per wave: 32 resident keys kw0 .. kw0 + 31 (lane column = key).  Query tiles
+// of 64 rows (Q, dO, LSE, D) stream through two LDS stages; the copies of tile
+// it + 1 are issued before tile it is computed.  For each 32-query half:
 //   S  = Q K^T and dP = dO V^T   (A = Q / dO rows from LDS, B = K^T / V^T resident)
 //   P  = exp2(c S - LSE2), dS = P (dP - D)         (per element, query in the register index)
 //   dV^T += dO^T P,  dK^T += Q^T dS                (A = dO^T / Q^T by transpose reads)
+// A negative scale flips the sign of the resident K (exact), so S carries the
+// sign and dK = scale dS^T Q uses Q as stored.
+template <int D> struct DkdvLds {
+  static constexpr int kQ = 0;
+  static constexpr int kDO = STile<D>::kBytes;
+  static constexpr int kLse = 2 * STile<D>::kBytes;
+  static constexpr int kD = kLse + 4 * kT;
+  static constexpr int kStage = kD + 4 * kT;
+  static constexpr int kBytes = 2 * kStage;
+};
+
 template <bool IsBf16, int D, bool Causal>
 __global__ __launch_bounds__(kThr, 1) void bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BH, float c, float dk_mul,
-    uint32_t q_sign) {
+    uint32_t k_sign) {
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
-  using T = Tile<D>;
+  using T = STile<D>;
+  using Ld = DkdvLds<D>;
   constexpr int kKs = D / 16, kDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[T::kBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t do_lds[T::kBytes];
-  __shared__ __attribute__((aligned(16))) float lse_lds[kT];
-  __shared__ __attribute__((aligned(16))) float d_lds[kT];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int bh = blockIdx.x % BH, kblk = blockIdx.x / BH;  // heaviest (earliest keys) first
   const int64_t head = (int64_t)bh * N * D;
   const int k0 = kblk * kRes, kw0 = k0 + 32 * wave, my_k = kw0 + l32;
 
   vec8 kf[kKs], vf[kKs];
-  load_resident<IsBf16, D>(kf, K + head, N, my_k, g, 0u);
+  load_resident<IsBf16, D>(kf, K + head, N, my_k, g, k_sign);
   load_resident<IsBf16, D>(vf, V + head, N, my_k, g, 0u);
   f32x16 dk[kDB], dv[kDB];
 #pragma unroll
@@ -183,42 +223,50 @@ __global__ __launch_bounds__(kThr, 1) void bwd_dkdv(
 
   const int n_tiles = (N + kT - 1) / kT;
   const int t_first = Causal ? k0 / kT : 0;  // earlier query tiles see none of these keys
-  const int trb = tr_base<D>(lane);
+  const uint16_t* q_h = Q + head;
+  const uint16_t* do_h = dO + head;
   const float* lse_h = LSE + (int64_t)bh * N;
   const float* d_h = Dsum + (int64_t)bh * N;
-  const bool wave_live = kw0 < N;
+  uint32_t src[T::kPerWave];
+  T::sources(wave, lane, src);
+  const uint32_t lds0 = lds_u32(smem);
 
-  for (int it = t_first; it < n_tiles; ++it) {
+  // issue the copies of query tile it into stage st (LSE by wave 0, D by wave 1)
+  auto issue = [&](int it, int st) {
     const int qt0 = it * kT;
-    __syncthreads();  // previous tile consumed
-    stage_tile<D>(q_lds, Q + head, N, qt0);
-    stage_tile<D>(do_lds, dO + head, N, qt0);
-    if (threadIdx.x < kT) {
-      const int qi = qt0 + threadIdx.x;
-      // log2-domain LSE; rows past N get +inf so that their probabilities are 0
-      lse_lds[threadIdx.x] = qi < N ? lse_h[qi] * 1.4426950408889634f : INFINITY;
-      d_lds[threadIdx.x] = qi < N ? d_h[qi] : 0.f;
+    const uint32_t base = lds0 + (uint32_t)(st * Ld::kStage);
+    copy_tile<D>(base + Ld::kQ, q_h, N, qt0, wave, src);
+    copy_tile<D>(base + Ld::kDO, do_h, N, qt0, wave, src);
+    const int left = N - qt0;
+    if (wave < 2) {
+      const i32x4 rs = make_rsrc(wave == 0 ? lse_h + qt0 : d_h + qt0, left > 0 ? (uint32_t)left * 4u : 0u);
+      dma4(rs, base + (uint32_t)(wave == 0 ? Ld::kLse : Ld::kD), (uint32_t)lane * 4u);
     }
-    __syncthreads();
-    if (q_sign) {  // negative scale: S uses -Q (exact), and so does dK (with |scale|)
-      for (int c2 = threadIdx.x; c2 < T::kBytes / 16; c2 += kThr) {
-        *reinterpret_cast<u32x4*>(q_lds + c2 * 16) ^= q_sign;
-      }
-      __syncthreads();
-    }
-    if (!wave_live) continue;
+  };
+
+  if (t_first < n_tiles) issue(t_first, 0);
+  wait_copies();
+  __syncthreads();
+  for (int it = t_first; it < n_tiles; ++it) {
+    const int st = (it - t_first) & 1;
+    if (it + 1 < n_tiles) issue(it + 1, st ^ 1);
+    const uint8_t* q_lds = smem + st * Ld::kStage + Ld::kQ;
+    const uint8_t* do_lds = smem + st * Ld::kStage + Ld::kDO;
+    const float* lse_lds = reinterpret_cast<const float*>(smem + st * Ld::kStage + Ld::kLse);
+    const float* d_lds = reinterpret_cast<const float*>(smem + st * Ld::kStage + Ld::kD);
+    const int qt0 = it * kT;
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
       const int qs0 = qt0 + 32 * qh;  // first query of this half
+      if (kw0 >= N) continue;
       if (Causal && qs0 + 31 < kw0) continue;  // every query before every key of the wave
       if (qs0 >= N) continue;
       f32x16 s = f32x16{}, dp = f32x16{};
-      const uint8_t* qrow = q_lds + (32 * qh + l32) * T::kStride + 16 * g;
-      const uint8_t* orow = do_lds + (32 * qh + l32) * T::kStride + 16 * g;
+      const int r = 32 * qh + l32;
 #pragma unroll
       for (int kk = 0; kk < kKs; ++kk) {
-        s = E::mfma(*reinterpret_cast<const vec8*>(qrow + 32 * kk), kf[kk], s);
-        dp = E::mfma(*reinterpret_cast<const vec8*>(orow + 32 * kk), vf[kk], dp);
+        s = E::mfma(row_frag<IsBf16, D>(q_lds, r, g, kk), kf[kk], s);
+        dp = E::mfma(row_frag<IsBf16, D>(do_lds, r, g, kk), vf[kk], dp);
       }
       // register e of lane half g holds query qs0 + 16 (e >> 3) + 8 g + (e & 7)
       const float* lq = lse_lds + 32 * qh + 8 * g;
@@ -235,13 +283,14 @@ __global__ __launch_bounds__(kThr, 1) void bwd_dkdv(
         float p2[2], ds2[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int r = e + u;
-          const int qi = qs0 + 16 * (r >> 3) + 8 * g + (r & 7);
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l4[r >> 2][r & 3]));
+          const int rr = e + u;
+          const int qi = qs0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
+          // natural-log LSE converted to the exp2 domain
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c, -l4[rr >> 2][rr & 3] * 1.4426950408889634f));
           if (Causal) p = (my_k > qi) ? 0.f : p;
-          p = (my_k >= N) ? 0.f : p;
+          p = (my_k >= N || qi >= N) ? 0.f : p;
           p2[u] = p;
-          ds2[u] = p * (dp[r] - d4[r >> 2][r & 3]);
+          ds2[u] = p * (dp[rr] - d4[rr >> 2][rr & 3]);
         }
         pw[e >> 3][(e & 7) >> 1] = E::pack2(p2[0], p2[1]);
         sw[e >> 3][(e & 7) >> 1] = E::pack2(ds2[0], ds2[1]);
@@ -251,25 +300,34 @@ __global__ __launch_bounds__(kThr, 1) void bwd_dkdv(
       for (int db = 0; db < kDB; ++db)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          dv[db] = E::mfma(tr_frag<IsBf16, D>(do_lds + 32 * qh * T::kStride, trb, t, db),
+          dv[db] = E::mfma(tr_frag<IsBf16, D>(do_lds, lane, 2 * qh + t, db),
                            __builtin_bit_cast(vec8, pw[t]), dv[db]);
-          dk[db] = E::mfma(tr_frag<IsBf16, D>(q_lds + 32 * qh * T::kStride, trb, t, db),
+          dk[db] = E::mfma(tr_frag<IsBf16, D>(q_lds, lane, 2 * qh + t, db),
                            __builtin_bit_cast(vec8, sw[t]), dk[db]);
         }
     }
+    wait_copies();
+    __syncthreads();
   }
-  if (!wave_live || my_k >= N) return;
+  if (kw0 >= N || my_k >= N) return;
   store_row<IsBf16, D>(dK + head, my_k, g, dk, dk_mul);
   store_row<IsBf16, D>(dV + head, my_k, g, dv, 1.f);
 }
 
 // ---------------------------------------------------------------- D and dQ
-// Per wave: 32 resident queries (lane column = query).  For each 32-key half
-// of a streamed 64-key tile:
+// Per wave: 32 resident queries (lane column = query).  Key tiles of 64 rows
+// (K, V) stream through two LDS stages, twice.  For each 32-key half:
 //   S^T = K Q^T and dP^T = V dO^T (A = K / V rows from LDS, B = Q^T / dO^T resident)
 //   P^T = exp2(c S^T - LSE2)                           (LSE2: lane scalar)
 //   pass 1:  D += sum over the keys of P^T dP^T
 //   pass 2:  dS^T = P^T (dP^T - D),  dQ^T += K^T dS^T  (A = K^T by transpose reads)
+template <int D> struct DqLds {
+  static constexpr int kK = 0;
+  static constexpr int kV = STile<D>::kBytes;
+  static constexpr int kStage = 2 * STile<D>::kBytes;
+  static constexpr int kBytes = 2 * kStage;
+};
+
 template <bool IsBf16, int D, bool Causal>
 __global__ __launch_bounds__(kThr, 1) void bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -278,12 +336,13 @@ __global__ __launch_bounds__(kThr, 1) void bwd_dq(
     uint32_t q_sign) {
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
-  using T = Tile<D>;
+  using T = STile<D>;
+  using Ld = DqLds<D>;
   constexpr int kKs = D / 16, kDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[T::kBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int bh = blockIdx.x % BH;
   int qb = blockIdx.x / BH;
   if (Causal) qb = n_qblocks - 1 - qb;  // heaviest first
@@ -298,79 +357,97 @@ __global__ __launch_bounds__(kThr, 1) void bwd_dq(
 
   const int last_row = min(N, q0 + kRes) - 1;
   const int n_tiles = Causal ? last_row / kT + 1 : (N + kT - 1) / kT;
-  const int trb = tr_base<D>(lane);
   const bool wave_live = qw0 < N;
+  const uint16_t* k_h = K + head;
+  const uint16_t* v_h = V + head;
+  uint32_t src[T::kPerWave];
+  T::sources(wave, lane, src);
+  const uint32_t lds0 = lds_u32(smem);
 
-  // S^T and dP^T of key half kh of the staged tile, and P^T with the masks
-  // applied; register e of lane half g holds key ks0 + 16 (e >> 3) + 8 g + (e & 7).
-  auto scores = [&](int kh, int ks0, f32x16& p, f32x16& dp) {
+  auto issue = [&](int it, int st) {
+    const uint32_t base = lds0 + (uint32_t)(st * Ld::kStage);
+    copy_tile<D>(base + Ld::kK, k_h, N, it * kT, wave, src);
+    copy_tile<D>(base + Ld::kV, v_h, N, it * kT, wave, src);
+  };
+
+  // S^T and dP^T of key half kh of the tile in stage st, and P^T with the
+  // masks applied; register e of lane half g holds key ks0 + 16 (e >> 3) + 8 g + (e & 7).
+  auto scores = [&](int st, int kh, int ks0, f32x16& p, f32x16& dp) {
+    const uint8_t* k_lds = smem + st * Ld::kStage + Ld::kK;
+    const uint8_t* v_lds = smem + st * Ld::kStage + Ld::kV;
     f32x16 s = f32x16{};
     dp = f32x16{};
-    const uint8_t* krow = k_lds + (32 * kh + l32) * T::kStride + 16 * g;
-    const uint8_t* vrow = v_lds + (32 * kh + l32) * T::kStride + 16 * g;
+    const int r = 32 * kh + l32;
 #pragma unroll
     for (int kk = 0; kk < kKs; ++kk) {
-      s = E::mfma(*reinterpret_cast<const vec8*>(krow + 32 * kk), qf[kk], s);
-      dp = E::mfma(*reinterpret_cast<const vec8*>(vrow + 32 * kk), of[kk], dp);
+      s = E::mfma(row_frag<IsBf16, D>(k_lds, r, g, kk), qf[kk], s);
+      dp = E::mfma(row_frag<IsBf16, D>(v_lds, r, g, kk), of[kk], dp);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kj = ks0 + 16 * (r >> 3) + 8 * g + (r & 7);
-      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-      p[r] = (kj >= N || (Causal && kj > my_q)) ? 0.f : pr;
+    for (int rr = 0; rr < 16; ++rr) {
+      const int kj = ks0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
+      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c, -lse2));
+      p[rr] = (kj >= N || (Causal && kj > my_q)) ? 0.f : pr;
     }
   };
 
   // ---- pass 1: D = sum_j P_ij dP_ij
   float dpart = 0.f;
+  issue(0, 0);
+  wait_copies();
+  __syncthreads();
   for (int it = 0; it < n_tiles; ++it) {
+    const int st = it & 1;
+    // the next tile, or (after the last one) the first tile again for pass 2
+    issue(it + 1 < n_tiles ? it + 1 : 0, st ^ 1);
     const int kt0 = it * kT;
-    __syncthreads();
-    stage_tile<D>(k_lds, K + head, N, kt0);
-    stage_tile<D>(v_lds, V + head, N, kt0);
-    __syncthreads();
-    if (!wave_live) continue;
+    if (wave_live) {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int ks0 = kt0 + 32 * kh;
-      if ((Causal && ks0 > qw0 + 31) || ks0 >= N) continue;
-      f32x16 p, dp;
-      scores(kh, ks0, p, dp);
+      for (int kh = 0; kh < 2; ++kh) {
+        const int ks0 = kt0 + 32 * kh;
+        if ((Causal && ks0 > qw0 + 31) || ks0 >= N) continue;
+        f32x16 p, dp;
+        scores(st, kh, ks0, p, dp);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dpart = __builtin_fmaf(p[r], dp[r], dpart);
+        for (int rr = 0; rr < 16; ++rr) dpart = __builtin_fmaf(p[rr], dp[rr], dpart);
+      }
     }
+    wait_copies();
+    __syncthreads();
   }
   const float dsum = xhalf_sum(dpart);
   if (wave_live && q_ok && g == 0) Dsum[(int64_t)bh * N + my_q] = dsum;
 
-  // ---- pass 2: dQ^T += K^T dS^T
+  // ---- pass 2: dQ^T += K^T dS^T; tile 0 is already in stage n_tiles & 1
   f32x16 dq[kDB];
 #pragma unroll
   for (int i = 0; i < kDB; ++i) dq[i] = f32x16{};
   for (int it = 0; it < n_tiles; ++it) {
+    const int st = (it + n_tiles) & 1;
+    if (it + 1 < n_tiles) issue(it + 1, st ^ 1);
     const int kt0 = it * kT;
-    __syncthreads();
-    stage_tile<D>(k_lds, K + head, N, kt0);
-    stage_tile<D>(v_lds, V + head, N, kt0);
-    __syncthreads();
-    if (!wave_live) continue;
+    if (wave_live) {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int ks0 = kt0 + 32 * kh;
-      if ((Causal && ks0 > qw0 + 31) || ks0 >= N) continue;
-      f32x16 p, dp;
-      scores(kh, ks0, p, dp);
-      u32x4 sw[2];
+      for (int kh = 0; kh < 2; ++kh) {
+        const int ks0 = kt0 + 32 * kh;
+        if ((Causal && ks0 > qw0 + 31) || ks0 >= N) continue;
+        f32x16 p, dp;
+        scores(st, kh, ks0, p, dp);
+        u32x4 sw[2];
 #pragma unroll
-      for (int e = 0; e < 16; e += 2)
-        sw[e >> 3][(e & 7) >> 1] = E::pack2(p[e] * (dp[e] - dsum), p[e + 1] * (dp[e + 1] - dsum));
+        for (int e = 0; e < 16; e += 2)
+          sw[e >> 3][(e & 7) >> 1] = E::pack2(p[e] * (dp[e] - dsum), p[e + 1] * (dp[e + 1] - dsum));
+        const uint8_t* k_lds = smem + st * Ld::kStage + Ld::kK;
 #pragma unroll
-      for (int db = 0; db < kDB; ++db)
+        for (int db = 0; db < kDB; ++db)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          dq[db] = E::mfma(tr_frag<IsBf16, D>(k_lds + 32 * kh * T::kStride, trb, t, db),
-                           __builtin_bit_cast(vec8, sw[t]), dq[db]);
+          for (int t = 0; t < 2; ++t)
+            dq[db] = E::mfma(tr_frag<IsBf16, D>(k_lds, lane, 2 * kh + t, db),
+                             __builtin_bit_cast(vec8, sw[t]), dq[db]);
+      }
     }
+    wait_copies();
+    __syncthreads();
   }
   if (!wave_live || !q_ok) return;
   store_row<IsBf16, D>(dQ + head, my_q, g, dq, dq_mul);
@@ -395,10 +472,10 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
                      q_sign);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // dK = scale dS^T Q; with a sign-flipped Q for negative scales this is |scale| dS^T (-Q)
+  // dK = scale dS^T Q; a negative scale flips the resident K instead of Q
   hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
                      q, k, v, dout, a.lse, dsum, static_cast<uint16_t*>(a.dk),
-                     static_cast<uint16_t*>(a.dv), N, BH, c, __builtin_fabsf(a.scale), q_sign);
+                     static_cast<uint16_t*>(a.dv), N, BH, c, a.scale, q_sign);
   return hipGetLastError();
 }
 

@@ -39,10 +39,9 @@
 //    the start of block u, the V operand of sub-tile u during its second half.
 //  * exp is exp2 with scale*log2(e) folded into one FMA per score.  The
 //    probabilities of a block are taken against the current reference maximum
-//    without first computing the block's own maximum; the block's partial row
-//    sums (formed from the rounded probabilities, so that numerator and
-//    denominator use the same weights) reveal whether any probability exceeded
-//    2^8, and only then is the reference raised to the true running maximum,
+//    without first computing the block's own maximum; the block's fp32
+//    partial row sums reveal whether any probability exceeded 2^8, and only
+//    then is the reference raised to the true running maximum,
 //    a and l rescaled and the block's probabilities recomputed.  Any reference
 //    value gives the same a / l and LSE; the check keeps probabilities <= 256.
 //  * Causal: tiles entirely above a wave's rows are skipped, the mask is only
@@ -233,15 +232,17 @@ struct FwdBlock {
     const uint32_t v_left = jv < n_tiles ? head_bytes - (uint32_t)jv * kTileBytes : 0u;
     const i32x4 tk = make_rsrc(k_ptr + (size_t)jk * kTileBytes, k_left);
     const i32x4 tv = make_rsrc(v_ptr + (size_t)jv * kTileBytes, v_left);
+    // wave-uniform by construction; readfirstlane keeps the selection in SGPRs
     i32x4 tx;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) tx[w] = (int)(((uint32_t)tk[w] & ~x_vmask) | ((uint32_t)tv[w] & x_vmask));
+    for (int w = 0; w < 4; ++w)
+      tx[w] = __builtin_amdgcn_readfirstlane((int)(((uint32_t)tk[w] & ~x_vmask) | ((uint32_t)tv[w] & x_vmask)));
     const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)smem + (uint32_t)(wave * 1024);
     const uint32_t k_st = base + (uint32_t)(sk * L::kKStage);
     const uint32_t v_st = base + (uint32_t)(kStages * L::kKStage + sv * L::kVStage);
-    const uint32_t x_lds = (uint32_t)(uintptr_t)(lds_void*)smem + x_off +
-                           ((uint32_t)(sk * L::kKStage) & x_kmask) +
-                           ((uint32_t)(kStages * L::kKStage + sv * L::kVStage) & x_vmask);
+    const uint32_t x_lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)((uint32_t)(uintptr_t)(lds_void*)smem + x_off + ((uint32_t)(sk * L::kKStage) & x_kmask) +
+              ((uint32_t)(kStages * L::kKStage + sv * L::kVStage) & x_vmask)));
     static_assert(kFullK == kFullV && (kFullK == 1 || kFullK == 2), "copy groups of 3 or 5");
     if constexpr (kFullK == 2)
       dma_group5(tk, tv, tx, k_st, k_st + kWaves * 1024, v_st, v_st + kWaves * 1024, x_lds,
@@ -270,13 +271,12 @@ struct FwdBlock {
   }
 
   // Probabilities of scores 2e, 2e+1 against the current reference, packed
-  // into the B operand and added to a partial row sum.
+  // into the B operand and added (in fp32) to a partial row sum.
   __device__ __forceinline__ void exp_pair(const f32x16& st, int e, u32x4 (&pw)[2], float& sum) const {
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * e], c, neg_mc));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * e + 1], c, neg_mc));
-    const uint32_t pk = E::pack2(p0, p1);
-    pw[e >> 2][e & 3] = pk;
-    sum = E::add_pair(pk, sum);
+    pw[e >> 2][e & 3] = E::pack2(p0, p1);
+    sum += p0 + p1;
   }
 
   // Raise the reference to the running maximum over the scores st (both lane
@@ -307,7 +307,7 @@ struct FwdBlock {
     return st;
   }
 
-  // MFMA slot of step st (0 scale, 1 exp2, 2 pack, 3 partial sum) of score
+  // MFMA slot of step st (0 scale, 1 exp2, 2 pack and partial sum) of score
   // pair e, for blocks of 16, 8 or 4 MFMA slots.  Steps that land in the same
   // slot run in program order.
   template <int kSlots>
@@ -367,8 +367,9 @@ struct FwdBlock {
         vfr[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
       // Probabilities of the 8 score pairs, software-pipelined so that each
-      // step of a pair (scale, exp2, pack, partial sum) runs a few MFMA slots
-      // after the step it depends on and never stalls the wave's in-order issue.
+      // step of a pair (scale, exp2, then pack and fp32 partial sum) runs a
+      // few MFMA slots after the step it depends on and never stalls the
+      // wave's in-order issue.
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (t == slot(e, 0)) {
@@ -379,8 +380,10 @@ struct FwdBlock {
           pr[2 * e] = __builtin_amdgcn_exp2f(pr[2 * e]);
           pr[2 * e + 1] = __builtin_amdgcn_exp2f(pr[2 * e + 1]);
         }
-        if (t == slot(e, 2)) pw[e >> 2][e & 3] = E::pack2(pr[2 * e], pr[2 * e + 1]);
-        if (t == slot(e, 3)) sum[e & 1] = E::add_pair(pw[e >> 2][e & 3], sum[e & 1]);
+        if (t == slot(e, 2)) {
+          pw[e >> 2][e & 3] = E::pack2(pr[2 * e], pr[2 * e + 1]);
+          sum[e & 1] += pr[2 * e] + pr[2 * e + 1];
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -118,12 +118,6 @@ template <> struct Elt<true> {
   static __device__ __forceinline__ vec4 read_tr(const lds_void* p) {
     return __builtin_bit_cast(vec4, read_tr16(p));
   }
-  // acc + x.lo + x.hi for a packed pair x (one v_dot2c against (1, 1))
-  static __device__ __forceinline__ float add_pair(uint32_t x, float acc) {
-    typedef __attribute__((ext_vector_type(2))) __bf16 h2;
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(h2, x),
-                                           __builtin_bit_cast(h2, 0x3F803F80u), acc, false);
-  }
 };
 template <> struct Elt<false> {
   using scalar = _Float16;
@@ -139,11 +133,6 @@ template <> struct Elt<false> {
   }
   static __device__ __forceinline__ vec4 read_tr(const lds_void* p) {
     return __builtin_bit_cast(vec4, read_tr16(p));
-  }
-  static __device__ __forceinline__ float add_pair(uint32_t x, float acc) {
-    typedef __attribute__((ext_vector_type(2))) _Float16 h2;
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, x), __builtin_bit_cast(h2, 0x3C003C00u), acc,
-                                  false);
   }
 };
 

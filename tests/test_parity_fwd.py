@@ -3,7 +3,10 @@
 Every case draws seeded inputs (``workloads``), runs the HIP path through the C
 ABI, runs the oracle on the same dtype-rounded values and compares element by
 element.  Tolerances: fp32 max |err| <= 1e-5 on O and LSE; fp16/bf16
-|err| <= 2e-2 + 1e-2 |ref| on O and LSE.  Full-size workloads compare a
+|err| <= 2e-2 + 1e-2 |ref| on O.  The LSE is an fp32 output computed from the
+rounded inputs in fp32 whatever the input type, so for fp16/bf16 inputs it is
+held to |err| <= 1e-4 + 1e-5 |ref| (fp32 score sums, exp2 and a row sum of up
+to 8192 fp32 probabilities).  Full-size workloads compare a
 sample of rows (first, last, tile and block boundaries, the ragged tail and
 random rows of every head); the dense oracle computes those rows exactly.
 """
@@ -21,6 +24,9 @@ pytestmark = pytest.mark.gpu
 
 TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
 TOL = {"fp32": (1e-5, 0.0), "fp16": (2e-2, 1e-2), "bf16": (2e-2, 1e-2)}
+# LSE of fp16/bf16 inputs: computed in fp32 from the rounded inputs
+LSE_TOL = {"fp32": "fp32", "fp16": "lse", "bf16": "lse"}
+TOL["lse"] = (1e-4, 1e-5)
 
 
 @pytest.fixture(scope="module")
@@ -78,7 +84,7 @@ def test_tiny_fp32_full(fa):
     o, lse = run_fwd(fa, x, w.dtype, w.causal)
     ro, rl = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale)
     compare("O", o, ro, "fp32")
-    compare("LSE", lse, rl, "fp32")
+    compare("LSE", lse, rl, LSE_TOL["fp32"])
 
 
 def test_gpt2s_causal_bf16_full(fa):
@@ -88,7 +94,7 @@ def test_gpt2s_causal_bf16_full(fa):
     o, lse = run_fwd(fa, x, w.dtype, w.causal)
     ro, rl = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=True, scale=w.scale)
     compare("O", o, ro, w.dtype)
-    compare("LSE", lse, rl, w.dtype)
+    compare("LSE", lse, rl, LSE_TOL[w.dtype])
 
 
 @pytest.mark.parametrize("name", ["long_causal_bf16", "ragged_sharp_fp16", "fwd_bwd_causal_bf16"])
@@ -100,7 +106,7 @@ def test_large_workload_sampled_rows(fa, name):
     rows = sample_rows(w.N, seed=w.seed)
     ro, rl = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, rows=rows)
     compare("O[rows]", o[:, :, rows], ro, w.dtype)
-    compare("LSE[rows]", lse[:, :, rows], rl, w.dtype)
+    compare("LSE[rows]", lse[:, :, rows], rl, LSE_TOL[w.dtype])
     assert np.isfinite(o).all() and np.isfinite(lse).all()
 
 
@@ -121,7 +127,7 @@ def test_sweep(fa, dtype, d, causal):
         o, lse = run_fwd(fa, x, dtype, causal)
         ro, rl = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=causal)
         compare("O", o, ro, dtype)
-        compare("LSE", lse, rl, dtype)
+        compare("LSE", lse, rl, LSE_TOL[dtype])
 
 
 # ------------------------------------------------------------------ structured inputs
@@ -136,7 +142,7 @@ def test_needles(fa, dtype, causal, n, d):
     o, lse = run_fwd(fa, x, dtype, causal)
     ro, rl = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=causal)
     compare("O", o, ro, dtype)
-    compare("LSE", lse, rl, dtype)
+    compare("LSE", lse, rl, LSE_TOL[dtype])
     # these rows are nearly one-hot, so the output is held much tighter than the tolerance
     assert np.abs(o - ro).max() < 2e-2
 
@@ -150,7 +156,7 @@ def test_scale_sign_and_zero(fa, dtype, scale):
         o, lse = run_fwd(fa, x, dtype, causal, scale=scale)
         ro, rl = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=causal, scale=scale)
         compare("O", o, ro, dtype)
-        compare("LSE", lse, rl, dtype)
+        compare("LSE", lse, rl, LSE_TOL[dtype])
 
 
 def test_sharp_rows_rescaling(fa):
@@ -164,7 +170,7 @@ def test_sharp_rows_rescaling(fa):
         o, lse = run_fwd(fa, x, "fp16", causal)
         ro, rl = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=causal)
         compare("O", o, ro, "fp16")
-        compare("LSE", lse, rl, "fp16")
+        compare("LSE", lse, rl, LSE_TOL["fp16"])
 
 
 # ------------------------------------------------------------------ properties
