@@ -126,7 +126,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int mask, float scale, int dtype, void* workspace, size_t workspace_bytes,
              void* stream);
 
-/* Bytes of workspace attn_bwd needs for these sizes (4 * B * H * N today);
+/* Bytes of workspace attn_bwd needs for these sizes (8 * B * H * N today);
  * 0 if the sizes, d or dtype are invalid. */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
 

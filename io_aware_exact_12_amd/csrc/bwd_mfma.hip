@@ -41,6 +41,7 @@ namespace fa {
 namespace {
 
 using namespace mfma;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 constexpr int kW = 4;              // waves per workgroup
 constexpr int kThr = 64 * kW;
@@ -179,59 +180,192 @@ __device__ __forceinline__ void store_row(uint16_t* base, int row, int g, const 
 
 // ---------------------------------------------------------------- dK, dV
 // Per wave: 32 resident keys kw0 .. kw0 + 31 (lane column = key).  Query tiles
-// of 64 rows (Q, dO, LSE, D) stream through two LDS stages; the copies of tile
-// it + 1 are issued before tile it is computed.  For each 32-query half:
-//   S  = Q K^T and dP = dO V^T   (A = Q / dO rows from LDS, B = K^T / V^T resident)
-//   P  = exp2(c S - LSE2), dS = P (dP - D)         (per element, query in the register index)
-//   dV^T += dO^T P,  dK^T += Q^T dS                (A = dO^T / Q^T by transpose reads)
-// A negative scale flips the sign of the resident K (exact), so S carries the
-// sign and dK = scale dS^T Q uses Q as stored.
+// of 64 rows (Q, dO, -LSE log2 e, D) stream through two LDS stages; the copies
+// of tile it + 1 are issued before tile it is computed.  Two passes over the
+// tiles, so that only one set of accumulators is live at a time (the kernel
+// then fits two waves per SIMD).  For each 32-query half:
+//   pass V:  S = Q K^T, P = exp2(c S - LSE2), dV^T += dO^T P
+//   pass K:  S, dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS
+// (A = Q / dO rows from LDS or dO^T / Q^T by transpose reads, B = K^T / V^T
+// resident or P / dS from registers; query in the register index).  Masks
+// (causal diagonal, sequence ends) are applied only in tiles that can need
+// them; a half of a masked tile that lies before all of the wave's keys still
+// runs and contributes zeros.  A negative scale flips the sign of the resident
+// K (exact), so S carries the sign and dK = scale dS^T Q uses Q as stored.
 template <int D> struct DkdvLds {
   static constexpr int kQ = 0;
   static constexpr int kDO = STile<D>::kBytes;
-  static constexpr int kLse = 2 * STile<D>::kBytes;
+  static constexpr int kLse = 2 * STile<D>::kBytes;  // -LSE * log2(e) of the 64 queries
   static constexpr int kD = kLse + 4 * kT;
   static constexpr int kStage = kD + 4 * kT;
   static constexpr int kBytes = 2 * kStage;
 };
 
 template <bool IsBf16, int D, bool Causal>
-__global__ __launch_bounds__(kThr, 1) void bwd_dkdv(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BH, float c, float dk_mul,
-    uint32_t k_sign) {
+struct DkdvBlock {
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using T = STile<D>;
   using Ld = DkdvLds<D>;
-  constexpr int kKs = D / 16, kDB = D / 32;
+  static constexpr int kKs = D / 16, kDB = D / 32;
+
+  int lane, g, N, my_k;
+  float c;
+  vec8 kf[kKs], vf[kKs];
+  f32x16 acc[kDB];        // dV^T in pass V, dK^T in pass K
+  int roff[kKs];          // row operand of k step kk: LDS row l32, chunk 2 kk + g
+  int toff[2][kDB];       // transpose reads (elements 0..3 / 4..7) of d block db, k step 0
+
+  __device__ __forceinline__ void init(int lane_, int N_, int kw0, float c_) {
+    lane = lane_;
+    N = N_;
+    c = c_;
+    g = lane >> 5;
+    my_k = kw0 + (lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < kKs; ++kk) roff[kk] = T::at(lane & 31, 2 * kk + g);
+    const int grp = lane >> 4, s16 = lane & 15;
+    const int r0 = 4 * g + (s16 >> 2);
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      const int col = 2 * (16 * (grp & 1) + 4 * (s16 & 3)) + 64 * db;  // byte column
+      toff[0][db] = T::at(r0, col >> 4) + (col & 15);
+      toff[1][db] = T::at(r0 + 8, col >> 4) + (col & 15);
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < kDB; ++i) acc[i] = f32x16{};
+  }
+
+  // Logical tile rows 16 t + 32 h keep their swizzle, so a half and a k step
+  // only add whole-row offsets to the per-lane offsets above.
+  __device__ __forceinline__ vec8 row_op(const uint8_t* tile, int h, int kk) const {
+    return *reinterpret_cast<const vec8*>(tile + roff[kk] + 32 * h * T::kRowBytes);
+  }
+  __device__ __forceinline__ vec8 tr_op(const uint8_t* tile, int h, int t, int db) const {
+    const uint8_t* p = tile + (32 * h + 16 * t) * T::kRowBytes;
+    const auto lo = E::read_tr((const lds_void*)(p + toff[0][db]));
+    const auto hi = E::read_tr((const lds_void*)(p + toff[1][db]));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // per-query floats of registers r, r+1 (consecutive queries) of half h
+  __device__ __forceinline__ f32x2 pair_vals(const uint8_t* sb, int off, int h, int r) const {
+    return *reinterpret_cast<const f32x2*>(reinterpret_cast<const float*>(sb + off) + 32 * h + 8 * g +
+                                           16 * (r >> 3) + (r & 7));
+  }
+
+  // probability of register r of a half whose first query is qs0, given
+  // nl = -LSE2 of that query
+  template <bool kMasked>
+  __device__ __forceinline__ float prob(const f32x16& s, float nl, int qs0, int r) const {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, nl));
+    if (!kMasked) return p;
+    const int qi = qs0 + 16 * (r >> 3) + 8 * g + (r & 7);
+    return ((Causal && my_k > qi) || qi >= N || my_k >= N) ? 0.f : p;
+  }
+
+  template <bool kMasked>
+  __device__ __forceinline__ void half_v(const uint8_t* sb, int h, int qs0) {
+    const uint8_t* q = sb + Ld::kQ;
+    const uint8_t* o = sb + Ld::kDO;
+    // operand reads run two MFMAs ahead; the fences stop the compiler from
+    // hoisting all of them (and holding them in registers)
+    f32x16 s = f32x16{};
+    vec8 a[2] = {row_op(q, h, 0), row_op(q, h, 1)};
+#pragma unroll
+    for (int kk = 0; kk < kKs; ++kk) {
+      s = E::mfma(a[kk & 1], kf[kk], s);
+      if (kk + 2 < kKs) a[kk & 1] = row_op(q, h, kk + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    u32x4 pw[2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const f32x2 nl = pair_vals(sb, Ld::kLse, h, 2 * e);
+      pw[e >> 2][e & 3] = E::pack2(prob<kMasked>(s, nl[0], qs0, 2 * e), prob<kMasked>(s, nl[1], qs0, 2 * e + 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    vec8 b[2] = {tr_op(o, h, 0, 0), tr_op(o, h, 0, 1 % kDB)};
+#pragma unroll
+    for (int i = 0; i < 2 * kDB; ++i) {
+      const int tt = i / kDB, db = i % kDB;
+      acc[db] = E::mfma(b[i & 1], __builtin_bit_cast(vec8, pw[tt]), acc[db]);
+      if (i + 2 < 2 * kDB) b[i & 1] = tr_op(o, h, (i + 2) / kDB, (i + 2) % kDB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  template <bool kMasked>
+  __device__ __forceinline__ void half_k(const uint8_t* sb, int h, int qs0) {
+    const uint8_t* q = sb + Ld::kQ;
+    const uint8_t* o = sb + Ld::kDO;
+    f32x16 s = f32x16{}, dp = f32x16{};
+    vec8 a[2] = {row_op(q, h, 0), row_op(o, h, 0)};
+#pragma unroll
+    for (int i = 0; i < 2 * kKs; ++i) {
+      const int kk = i >> 1;
+      if (i & 1)
+        dp = E::mfma(a[1], vf[kk], dp);
+      else
+        s = E::mfma(a[0], kf[kk], s);
+      if (i + 2 < 2 * kKs) a[i & 1] = (i & 1) ? row_op(o, h, kk + 1) : row_op(q, h, kk + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    u32x4 sw[2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = 2 * e;
+      const f32x2 nl = pair_vals(sb, Ld::kLse, h, r), dd = pair_vals(sb, Ld::kD, h, r);
+      const float d0 = prob<kMasked>(s, nl[0], qs0, r) * (dp[r] - dd[0]);
+      const float d1 = prob<kMasked>(s, nl[1], qs0, r + 1) * (dp[r + 1] - dd[1]);
+      sw[e >> 2][e & 3] = E::pack2(d0, d1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    vec8 b[2] = {tr_op(q, h, 0, 0), tr_op(q, h, 0, 1 % kDB)};
+#pragma unroll
+    for (int i = 0; i < 2 * kDB; ++i) {
+      const int tt = i / kDB, db = i % kDB;
+      acc[db] = E::mfma(b[i & 1], __builtin_bit_cast(vec8, sw[tt]), acc[db]);
+      if (i + 2 < 2 * kDB) b[i & 1] = tr_op(q, h, (i + 2) / kDB, (i + 2) % kDB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+template <bool IsBf16, int D, bool Causal>
+__global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ NLse, const float* __restrict__ Dsum,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BH, float c, float dk_mul,
+    uint32_t k_sign) {
+  using T = STile<D>;
+  using Ld = DkdvLds<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes];
 
-  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int bh = blockIdx.x % BH, kblk = blockIdx.x / BH;  // heaviest (earliest keys) first
   const int64_t head = (int64_t)bh * N * D;
-  const int k0 = kblk * kRes, kw0 = k0 + 32 * wave, my_k = kw0 + l32;
+  const int k0 = kblk * kRes, kw0 = k0 + 32 * wave;
 
-  vec8 kf[kKs], vf[kKs];
-  load_resident<IsBf16, D>(kf, K + head, N, my_k, g, k_sign);
-  load_resident<IsBf16, D>(vf, V + head, N, my_k, g, 0u);
-  f32x16 dk[kDB], dv[kDB];
-#pragma unroll
-  for (int i = 0; i < kDB; ++i) dk[i] = dv[i] = f32x16{};
+  DkdvBlock<IsBf16, D, Causal> blk;
+  blk.init(lane, N, kw0, c);
+  load_resident<IsBf16, D>(blk.kf, K + head, N, blk.my_k, blk.g, k_sign);
+  load_resident<IsBf16, D>(blk.vf, V + head, N, blk.my_k, blk.g, 0u);
 
   const int n_tiles = (N + kT - 1) / kT;
   const int t_first = Causal ? k0 / kT : 0;  // earlier query tiles see none of these keys
+  const int n_it = n_tiles - t_first;
   const uint16_t* q_h = Q + head;
   const uint16_t* do_h = dO + head;
-  const float* lse_h = LSE + (int64_t)bh * N;
+  const float* nl_h = NLse + (int64_t)bh * N;
   const float* d_h = Dsum + (int64_t)bh * N;
   uint32_t src[T::kPerWave];
   T::sources(wave, lane, src);
   const uint32_t lds0 = lds_u32(smem);
 
-  // issue the copies of query tile it into stage st (LSE by wave 0, D by wave 1)
+  // the copies of query tile it into stage st (-LSE2 by wave 0, D by wave 1)
   auto issue = [&](int it, int st) {
     const int qt0 = it * kT;
     const uint32_t base = lds0 + (uint32_t)(st * Ld::kStage);
@@ -239,79 +373,62 @@ __global__ __launch_bounds__(kThr, 1) void bwd_dkdv(
     copy_tile<D>(base + Ld::kDO, do_h, N, qt0, wave, src);
     const int left = N - qt0;
     if (wave < 2) {
-      const i32x4 rs = make_rsrc(wave == 0 ? lse_h + qt0 : d_h + qt0, left > 0 ? (uint32_t)left * 4u : 0u);
+      const i32x4 rs = make_rsrc(wave == 0 ? nl_h + qt0 : d_h + qt0, left > 0 ? (uint32_t)left * 4u : 0u);
       dma4(rs, base + (uint32_t)(wave == 0 ? Ld::kLse : Ld::kD), (uint32_t)lane * 4u);
     }
   };
+  // wave-uniform: does tile it reach this wave's keys, and can it need a mask?
+  auto live = [&](int it) { return kw0 < N && !(Causal && it * kT + kT - 1 < kw0); };
+  auto masked = [&](int it) {
+    const int qt0 = it * kT;
+    return (Causal && qt0 < kw0 + 32) || qt0 + kT > N || kw0 + 32 > N;
+  };
 
-  if (t_first < n_tiles) issue(t_first, 0);
+  issue(t_first, 0);
   wait_copies();
   __syncthreads();
-  for (int it = t_first; it < n_tiles; ++it) {
-    const int st = (it - t_first) & 1;
-    if (it + 1 < n_tiles) issue(it + 1, st ^ 1);
-    const uint8_t* q_lds = smem + st * Ld::kStage + Ld::kQ;
-    const uint8_t* do_lds = smem + st * Ld::kStage + Ld::kDO;
-    const float* lse_lds = reinterpret_cast<const float*>(smem + st * Ld::kStage + Ld::kLse);
-    const float* d_lds = reinterpret_cast<const float*>(smem + st * Ld::kStage + Ld::kD);
-    const int qt0 = it * kT;
+  // ---- pass V
+  blk.zero();
+  for (int i = 0; i < n_it; ++i) {
+    const int it = t_first + i, st = i & 1;
+    // the next tile, or (after the last one) the first tile again for pass K
+    issue(i + 1 < n_it ? it + 1 : t_first, st ^ 1);
+    if (live(it)) {
+      const uint8_t* sb = smem + st * Ld::kStage;
+      const bool m = masked(it);
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      const int qs0 = qt0 + 32 * qh;  // first query of this half
-      if (kw0 >= N) continue;
-      if (Causal && qs0 + 31 < kw0) continue;  // every query before every key of the wave
-      if (qs0 >= N) continue;
-      f32x16 s = f32x16{}, dp = f32x16{};
-      const int r = 32 * qh + l32;
-#pragma unroll
-      for (int kk = 0; kk < kKs; ++kk) {
-        s = E::mfma(row_frag<IsBf16, D>(q_lds, r, g, kk), kf[kk], s);
-        dp = E::mfma(row_frag<IsBf16, D>(do_lds, r, g, kk), vf[kk], dp);
+      for (int h = 0; h < 2; ++h) {
+        if (m)
+          blk.template half_v<true>(sb, h, it * kT + 32 * h);
+        else
+          blk.template half_v<false>(sb, h, it * kT + 32 * h);
       }
-      // register e of lane half g holds query qs0 + 16 (e >> 3) + 8 g + (e & 7)
-      const float* lq = lse_lds + 32 * qh + 8 * g;
-      const float* dq = d_lds + 32 * qh + 8 * g;
-      f32x4 l4[4], d4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        l4[i] = *reinterpret_cast<const f32x4*>(lq + 16 * (i >> 1) + 4 * (i & 1));
-        d4[i] = *reinterpret_cast<const f32x4*>(dq + 16 * (i >> 1) + 4 * (i & 1));
-      }
-      u32x4 pw[2], sw[2];
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        float p2[2], ds2[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int rr = e + u;
-          const int qi = qs0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
-          // natural-log LSE converted to the exp2 domain
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c, -l4[rr >> 2][rr & 3] * 1.4426950408889634f));
-          if (Causal) p = (my_k > qi) ? 0.f : p;
-          p = (my_k >= N || qi >= N) ? 0.f : p;
-          p2[u] = p;
-          ds2[u] = p * (dp[rr] - d4[rr >> 2][rr & 3]);
-        }
-        pw[e >> 3][(e & 7) >> 1] = E::pack2(p2[0], p2[1]);
-        sw[e >> 3][(e & 7) >> 1] = E::pack2(ds2[0], ds2[1]);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries (two k steps of 16)
-#pragma unroll
-      for (int db = 0; db < kDB; ++db)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          dv[db] = E::mfma(tr_frag<IsBf16, D>(do_lds, lane, 2 * qh + t, db),
-                           __builtin_bit_cast(vec8, pw[t]), dv[db]);
-          dk[db] = E::mfma(tr_frag<IsBf16, D>(q_lds, lane, 2 * qh + t, db),
-                           __builtin_bit_cast(vec8, sw[t]), dk[db]);
-        }
     }
     wait_copies();
     __syncthreads();
   }
-  if (kw0 >= N || my_k >= N) return;
-  store_row<IsBf16, D>(dK + head, my_k, g, dk, dk_mul);
-  store_row<IsBf16, D>(dV + head, my_k, g, dv, 1.f);
+  const bool store = kw0 < N && blk.my_k < N;
+  if (store) store_row<IsBf16, D>(dV + head, blk.my_k, blk.g, blk.acc, 1.f);
+  // ---- pass K; tile t_first is already in stage n_it & 1
+  blk.zero();
+  for (int i = 0; i < n_it; ++i) {
+    const int it = t_first + i, st = (i + n_it) & 1;
+    if (i + 1 < n_it) issue(it + 1, st ^ 1);
+    if (live(it)) {
+      const uint8_t* sb = smem + st * Ld::kStage;
+      const bool m = masked(it);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (m)
+          blk.template half_k<true>(sb, h, it * kT + 32 * h);
+        else
+          blk.template half_k<false>(sb, h, it * kT + 32 * h);
+      }
+    }
+    wait_copies();
+    __syncthreads();
+  }
+  if (store) store_row<IsBf16, D>(dK + head, blk.my_k, blk.g, blk.acc, dk_mul);
 }
 
 // ---------------------------------------------------------------- D and dQ
@@ -329,11 +446,11 @@ template <int D> struct DqLds {
 };
 
 template <bool IsBf16, int D, bool Causal>
-__global__ __launch_bounds__(kThr, 1) void bwd_dq(
+__global__ __launch_bounds__(kThr, 2) void bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dsum,
-    uint16_t* __restrict__ dQ, int N, int BH, int n_qblocks, float c, float dq_mul,
-    uint32_t q_sign) {
+    float* __restrict__ NLse, uint16_t* __restrict__ dQ, int N, int BH, int n_qblocks, float c,
+    float dq_mul, uint32_t q_sign) {
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using T = STile<D>;
@@ -416,7 +533,10 @@ __global__ __launch_bounds__(kThr, 1) void bwd_dq(
     __syncthreads();
   }
   const float dsum = xhalf_sum(dpart);
-  if (wave_live && q_ok && g == 0) Dsum[(int64_t)bh * N + my_q] = dsum;
+  if (wave_live && q_ok && g == 0) {
+    Dsum[(int64_t)bh * N + my_q] = dsum;
+    NLse[(int64_t)bh * N + my_q] = -lse2;  // read by the dK/dV kernel
+  }
 
   // ---- pass 2: dQ^T += K^T dS^T; tile 0 is already in stage n_tiles & 1
   f32x16 dq[kDB];
@@ -465,16 +585,18 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
   const auto* k = static_cast<const uint16_t*>(a.k);
   const auto* v = static_cast<const uint16_t*>(a.v);
   const auto* dout = static_cast<const uint16_t*>(a.dout);
+  // workspace: D, then -LSE * log2(e), one fp32 per query each
   float* dsum = static_cast<float*>(a.workspace);
+  float* nlse = dsum + a.B * a.H * a.N;
   // dQ (and D into the workspace) first; dK, dV read D afterwards on the same stream
   hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st, q,
-                     k, v, dout, a.lse, dsum, static_cast<uint16_t*>(a.dq), N, BH, nblk, c, a.scale,
-                     q_sign);
+                     k, v, dout, a.lse, dsum, nlse, static_cast<uint16_t*>(a.dq), N, BH, nblk, c,
+                     a.scale, q_sign);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dK = scale dS^T Q; a negative scale flips the resident K instead of Q
   hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
-                     q, k, v, dout, a.lse, dsum, static_cast<uint16_t*>(a.dk),
+                     q, k, v, dout, nlse, dsum, static_cast<uint16_t*>(a.dk),
                      static_cast<uint16_t*>(a.dv), N, BH, c, a.scale, q_sign);
   return hipGetLastError();
 }
@@ -487,7 +609,7 @@ hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) { return (size_t)(B * H * N) * 4; }
+size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) { return (size_t)(B * H * N) * 8; }
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) { return dispatch<true>(a, s); }
 hipError_t launch_bwd_f16(const BwdArgs& a, hipStream_t s) { return dispatch<false>(a, s); }
 

@@ -128,6 +128,6 @@ def test_bwd_validation(kw, status):
 
 
 def test_bwd_workspace_query():
-    assert fa.bwd_workspace_bytes(4, 16, 4096, 128, fa.BF16) == 4 * 4 * 16 * 4096
+    assert fa.bwd_workspace_bytes(4, 16, 4096, 128, fa.BF16) == 8 * 4 * 16 * 4096
     assert fa.bwd_workspace_bytes(0, 16, 4096, 128, fa.BF16) == 0
     assert fa.bwd_workspace_bytes(1, 1, 16, 96, fa.BF16) == 0
