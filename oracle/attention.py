@@ -26,6 +26,13 @@ silent; each is also listed with the design notes):
 * Causal: key j is visible to query i iff j <= i (lower-triangular mask with
   -inf fill, as in nanoGPT's manual attention quoted on "FlashAttention -- the
   same attention, made memory-aware", section 00).
+* Sliding window (``window`` = W, causal only): key j is visible to query i iff
+  i - W < j <= i, the W most recent keys including the query's own position.
+  This is a further key set whose blocks can be skipped like the causal
+  upper triangle ("Flash Attention: IO-Aware Exact Attention", section
+  "Storage, arithmetic and IO are separate quantities", on skipped blocks
+  changing which pairs are computed); the window's definition is a reading,
+  not a page fact.
 * The saved per-row statistic is the natural-log log-sum-exp of the scaled,
   masked scores: LSE_i = m_i + ln(l_i).
 """
@@ -38,12 +45,22 @@ def _as64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _scores(q, k, scale, causal, rows=None):
-    """Scaled scores S[..., i, j] = scale * q_i . k_j with the causal mask applied.
+def _check_window(causal, window):
+    if window is not None:
+        if not causal:
+            raise ValueError("a sliding window is defined for causal attention only")
+        if int(window) < 1:
+            raise ValueError("window must be >= 1")
+
+
+def _scores(q, k, scale, causal, rows=None, window=None):
+    """Scaled scores S[..., i, j] = scale * q_i . k_j with the causal (and
+    sliding-window) mask applied.
 
     ``rows`` optionally restricts the queries to the given indices (the
     definition is per row, so a subset of rows is the same computation).
     """
+    _check_window(causal, window)
     q = _as64(q)
     k = _as64(k)
     qi = q if rows is None else q[..., rows, :]
@@ -51,12 +68,15 @@ def _scores(q, k, scale, causal, rows=None):
     if causal:
         n_k = k.shape[-2]
         r = np.arange(q.shape[-2]) if rows is None else np.asarray(rows)
-        visible = np.arange(n_k)[None, :] <= r[:, None]
+        j = np.arange(n_k)[None, :]
+        visible = j <= r[:, None]
+        if window is not None:
+            visible &= j > r[:, None] - int(window)
         s = np.where(visible, s, -np.inf)
     return s
 
 
-def dense_fwd(q, k, v, causal=False, scale=None, rows=None):
+def dense_fwd(q, k, v, causal=False, scale=None, rows=None, window=None):
     """Materialised attention O = softmax(scale * Q K^T) V and its row LSE.
 
     Follows the dense three-step path ("Flash Attention: IO-Aware Exact
@@ -71,7 +91,7 @@ def dense_fwd(q, k, v, causal=False, scale=None, rows=None):
     q = _as64(q)
     if scale is None:
         scale = 1.0 / np.sqrt(q.shape[-1])
-    s = _scores(q, k, scale, causal, rows)
+    s = _scores(q, k, scale, causal, rows, window)
     m = s.max(axis=-1, keepdims=True)
     e = np.exp(s - m)
     ell = e.sum(axis=-1, keepdims=True)
@@ -81,17 +101,18 @@ def dense_fwd(q, k, v, causal=False, scale=None, rows=None):
     return o, lse
 
 
-def dense_probs(q, k, causal=False, scale=None):
+def dense_probs(q, k, causal=False, scale=None, window=None):
     """The normalised probability matrix P of the dense path (for row-sum checks)."""
     q = _as64(q)
     if scale is None:
         scale = 1.0 / np.sqrt(q.shape[-1])
-    s = _scores(q, k, scale, causal)
+    s = _scores(q, k, scale, causal, window=window)
     e = np.exp(s - s.max(axis=-1, keepdims=True))
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def online_fwd(q, k, v, causal=False, scale=None, query_block=2, key_block=2, trace=None):
+def online_fwd(q, k, v, causal=False, scale=None, query_block=2, key_block=2, trace=None,
+               window=None):
     """Tiled forward with the online softmax, one head at a time.
 
     Loop order: query blocks outside, key/value blocks inside; each query block
@@ -116,14 +137,16 @@ def online_fwd(q, k, v, causal=False, scale=None, query_block=2, key_block=2, tr
     and at the end O = a / l (one division, the FlashAttention-2 form of the
     unnormalised accumulator), LSE = m + ln l.
 
-    Masked keys (causal j > i) have t_j = -inf and contribute p_j = 0.  A tile in
-    which every key of a row is masked leaves that row's state unchanged.
+    Masked keys (causal j > i, or j <= i - window) have t_j = -inf and
+    contribute p_j = 0.  A tile in which every key of a row is masked leaves
+    that row's state unchanged.
     Tail tiles are simply shorter (keys beyond N do not exist); tiles larger
     than N are allowed.
 
     ``trace``, when a list, receives one dict per (query block, key tile) with
     copies of the state after that tile: keys ``row0``, ``col0``, ``m``, ``l``, ``a``.
     """
+    _check_window(causal, window)
     q = _as64(q)
     k = _as64(k)
     v = _as64(v)
@@ -149,6 +172,8 @@ def online_fwd(q, k, v, causal=False, scale=None, query_block=2, key_block=2, tr
                 t = (query @ kf[h, cols].T) * scale
                 if causal:
                     t = np.where(cols[None, :] <= rows[:, None], t, -np.inf)
+                if window is not None:
+                    t = np.where(cols[None, :] > rows[:, None] - int(window), t, -np.inf)
                 m_new = np.maximum(m, t.max(axis=1))
                 seen = np.isfinite(m_new)          # rows with at least one visible key so far
                 m_safe = np.where(seen, m_new, 0.0)
@@ -168,7 +193,7 @@ def online_fwd(q, k, v, causal=False, scale=None, query_block=2, key_block=2, tr
     return out.reshape(lead + (n_q, dv)), lse.reshape(lead + (n_q,))
 
 
-def dense_bwd(q, k, v, do, causal=False, scale=None):
+def dense_bwd(q, k, v, do, causal=False, scale=None, window=None):
     """Gradients of L = sum(O * dO) for O = softmax(scale * Q K^T) V.
 
     The pages state only that the backward pass recomputes the score and
@@ -195,8 +220,8 @@ def dense_bwd(q, k, v, do, causal=False, scale=None):
     do = _as64(do)
     if scale is None:
         scale = 1.0 / np.sqrt(q.shape[-1])
-    o, lse = dense_fwd(q, k, v, causal, scale)
-    s = _scores(q, k, scale, causal)
+    o, lse = dense_fwd(q, k, v, causal, scale, window=window)
+    s = _scores(q, k, scale, causal, window=window)
     p = np.exp(s - lse[..., None])
     kt = np.swapaxes
     dv = kt(p, -1, -2) @ do

@@ -323,6 +323,115 @@ def test_backward_invariants():
     np.testing.assert_allclose(dk, 0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- sliding window
+# Key j is visible to query i iff i - W < j <= i (causal only).
+
+def _window_mask(n, w):
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    return (j <= i) & (j > i - w)
+
+
+def test_window_one_attends_to_self():
+    """W = 1: every query sees only its own key, so O = V and LSE = scale q_i . k_i."""
+    q, k, v = (_rand(2, 19, 5, seed=s) for s in (80, 81, 82))
+    o, lse = oracle.dense_fwd(q, k, v, causal=True, scale=0.3, window=1)
+    np.testing.assert_array_equal(o, v)
+    np.testing.assert_allclose(lse, 0.3 * (q * k).sum(-1), rtol=1e-14, atol=1e-14)
+
+
+def _brute_window_row(q, k, v, scale, w, i):
+    """Softmax over the explicit key list of row i, in plain Python."""
+    keys = list(range(max(0, i - w + 1), i + 1))
+    t = [scale * sum(q[i, c] * k[j, c] for c in range(q.shape[1])) for j in keys]
+    mx = max(t)
+    e = [math.exp(x - mx) for x in t]
+    z = sum(e)
+    o = [sum(e[a] * v[keys[a], c] for a in range(len(keys))) / z for c in range(v.shape[1])]
+    return o, mx + math.log(z)
+
+
+@pytest.mark.parametrize("w", [1, 2, 3, 5, 12, 13, 40])
+def test_window_brute_force_rows(w):
+    n, d = 13, 4
+    q, k, v = (_rand(n, d, seed=s, std=2) for s in (83, 84, 85))
+    o, lse = oracle.dense_fwd(q, k, v, causal=True, scale=0.6, window=w)
+    for i in range(n):
+        bo, bl = _brute_window_row(q, k, v, 0.6, w, i)
+        np.testing.assert_allclose(o[i], bo, rtol=1e-12, atol=1e-12)
+        assert abs(lse[i] - bl) < 1e-12
+    if w < n:  # an off-by-one window is caught by the same comparison
+        o_bad, _ = oracle.dense_fwd(q, k, v, causal=True, scale=0.6, window=w + 1)
+        assert any(not np.allclose(o_bad[i], _brute_window_row(q, k, v, 0.6, w, i)[0], atol=1e-9)
+                   for i in range(n))
+
+
+def test_window_at_least_n_is_causal():
+    q, k, v = (_rand(2, 21, 6, seed=s) for s in (86, 87, 88))
+    ref = oracle.dense_fwd(q, k, v, causal=True)
+    for w in (21, 28):
+        got = oracle.dense_fwd(q, k, v, causal=True, window=w)
+        np.testing.assert_array_equal(got[0], ref[0])
+        np.testing.assert_array_equal(got[1], ref[1])
+
+
+@pytest.mark.parametrize("w", [1, 4, 9, 33])
+def test_window_against_torch_mask_and_autograd(w):
+    n = 33
+    q, k, v, do = (_rand(2, n, 8, seed=s) for s in (89, 90, 91, 92))
+    dq, dk, dv, o, lse = oracle.dense_bwd(q, k, v, do, causal=True, scale=0.4, window=w)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    mask = torch.from_numpy(_window_mask(n, w))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.4)
+    to.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(o, to.detach().numpy(), rtol=1e-12, atol=1e-13)
+    s = 0.4 * (q @ np.swapaxes(k, -1, -2))
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(np.where(_window_mask(n, w), s, -np.inf), axis=-1),
+                               rtol=1e-12, atol=1e-12)
+    for a, b in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(a, b.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("qb,kb", [(1, 1), (3, 5), (8, 2), (64, 64)])
+def test_window_online_matches_dense(qb, kb):
+    q, k, v = (_rand(2, 29, 5, seed=s, std=2) for s in (93, 94, 95))
+    for w in (1, 3, 7, 29):
+        ro, rl = oracle.dense_fwd(q, k, v, causal=True, window=w)
+        oo, ol = oracle.online_fwd(q, k, v, causal=True, window=w, query_block=qb, key_block=kb)
+        np.testing.assert_allclose(oo, ro, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(ol, rl, rtol=1e-12, atol=1e-13)
+
+
+def test_window_backward_finite_differences():
+    n, d, w, scale = 6, 3, 2, 0.7
+    q, k, v, do = (_rand(n, d, seed=s) for s in (96, 97, 98, 99))
+    dq, dk, dv, _, _ = oracle.dense_bwd(q, k, v, do, causal=True, scale=scale, window=w)
+
+    def loss(a, b, c):
+        o, _ = oracle.dense_fwd(a, b, c, causal=True, scale=scale, window=w)
+        return float((o * do).sum())
+
+    h = 1e-6
+    for pos, g in ((0, dq), (1, dk), (2, dv)):
+        base = [q, k, v]
+        num = np.zeros_like(base[pos])
+        for idx in np.ndindex(num.shape):
+            xp = [x.copy() for x in base]
+            xm = [x.copy() for x in base]
+            xp[pos][idx] += h
+            xm[pos][idx] -= h
+            num[idx] = (loss(*xp) - loss(*xm)) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+def test_window_argument_checks():
+    q = _rand(4, 2, seed=1)
+    with pytest.raises(ValueError):
+        oracle.dense_fwd(q, q, q, causal=False, window=2)
+    with pytest.raises(ValueError):
+        oracle.dense_fwd(q, q, q, causal=True, window=0)
+
+
 # ---------------------------------------------------------------- inputs
 
 def test_bf16_rounding_matches_torch_cast():
