@@ -59,7 +59,8 @@ enum fa_status {
   FA_ERR_UNSUPPORTED = 6, /* head dimension d is not 64 or 128 (or fp32 backward) */
   FA_ERR_WORKSPACE = 7,   /* backward workspace missing or too small            */
   FA_ERR_HIP = 8,         /* the HIP runtime rejected a launch                  */
-  FA_ERR_ALIGN = 9        /* a tensor pointer is not 16-byte aligned            */
+  FA_ERR_ALIGN = 9,       /* a tensor pointer is not 16-byte aligned            */
+  FA_ERR_WINDOW = 10      /* sliding window < 1                                 */
 };
 
 /*
@@ -88,6 +89,25 @@ enum fa_status {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int64_t B, int64_t H, int64_t N, int64_t d,
              int mask, float scale, int dtype, void* stream);
+
+/*
+ * attn_fwd_window -- forward pass with a causal sliding window.
+ *
+ * As attn_fwd with mask = FA_MASK_CAUSAL, except that key j is visible to
+ * query i iff i - window < j <= i: each query sees the `window` most recent
+ * keys, its own position included.  Key tiles wholly outside every window of
+ * a query block are skipped, the way causal attention skips the tiles above
+ * the diagonal ("Flash Attention: IO-Aware Exact Attention", section
+ * "Storage, arithmetic and IO are separate quantities": blocks that are
+ * skipped change which pairs are computed).
+ *
+ *   window   >= 1; window >= N is plain causal attention.  FA_ERR_WINDOW
+ *            if window < 1.
+ *   other arguments as for attn_fwd; lse is the log-sum-exp over the window.
+ */
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int64_t B, int64_t H, int64_t N, int64_t d, int64_t window,
+                    float scale, int dtype, void* stream);
 
 /*
  * attn_bwd -- backward pass by recomputation.
@@ -125,6 +145,19 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int64_t B, int64_t H, int64_t N, int64_t d,
              int mask, float scale, int dtype, void* workspace, size_t workspace_bytes,
              void* stream);
+
+/*
+ * attn_bwd_window -- backward pass of attn_fwd_window.
+ *
+ * As attn_bwd with mask = FA_MASK_CAUSAL and the sliding window of
+ * attn_fwd_window; lse must come from attn_fwd_window with the same window.
+ * FA_ERR_WINDOW if window < 1.
+ */
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv,
+                    int64_t B, int64_t H, int64_t N, int64_t d, int64_t window,
+                    float scale, int dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /* Bytes of workspace attn_bwd needs for these sizes (8 * B * H * N today);
  * 0 if the sizes, d or dtype are invalid. */

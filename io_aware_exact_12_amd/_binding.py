@@ -41,6 +41,12 @@ def lib():
         L.attn_bwd.restype = ctypes.c_int
         L.attn_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                           ctypes.c_int, vp, ctypes.c_size_t, vp]
+        L.attn_fwd_window.restype = ctypes.c_int
+        L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                      i64, ctypes.c_float, ctypes.c_int, vp]
+        L.attn_bwd_window.restype = ctypes.c_int
+        L.attn_bwd_window.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, ctypes.c_float,
+                                                 ctypes.c_int, vp, ctypes.c_size_t, vp]
         L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.fa_status_str.restype = ctypes.c_char_p
@@ -74,6 +80,18 @@ def attn_bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, scale, dty
                           ws_bytes, stream)
 
 
+def attn_fwd_window_raw(q, k, v, o, lse, B, H, N, d, window, scale, dtype, stream):
+    """Direct call of the C entry point with integer pointers; returns the status."""
+    return lib().attn_fwd_window(q, k, v, o, lse, B, H, N, d, window, scale, dtype, stream)
+
+
+def attn_bwd_window_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, window, scale, dtype, ws,
+                        ws_bytes, stream):
+    """Direct call of the C entry point with integer pointers; returns the status."""
+    return lib().attn_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, window, scale,
+                                 dtype, ws, ws_bytes, stream)
+
+
 def bwd_workspace_bytes(B, H, N, d, dtype_code):
     return lib().attn_bwd_workspace_bytes(B, H, N, d, dtype_code)
 
@@ -87,12 +105,14 @@ def _torch_dtype_code(t):
 
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=None, lse=None,
-             return_lse: bool = True, stream=None):
+             return_lse: bool = True, stream=None, window: int | None = None):
     """Exact attention forward on the GPU: returns ``(o, lse)`` (lse None if not requested).
 
     q, k, v: contiguous device tensors [B, H, N, d] of one dtype (float32,
     float16 or bfloat16), d in {64, 128}.  ``scale`` defaults to 1/sqrt(d).
-    Work is enqueued on ``stream`` (default: torch's current stream).
+    ``window`` (causal only) calls ``attn_fwd_window``: query i sees keys
+    i - window < j <= i.  Work is enqueued on ``stream`` (default: torch's
+    current stream).
     """
     import torch
     if q.shape != k.shape or q.shape != v.shape or q.dim() != 4:
@@ -111,6 +131,15 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=N
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    if window is not None:
+        if not causal:
+            raise ValueError("a sliding window needs causal=True")
+        st = lib().attn_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr() if return_lse else None, B, H, N, d, int(window),
+                                   float(scale), _torch_dtype_code(q), stream.cuda_stream)
+        if st != 0:
+            raise FaError(st, "attn_fwd_window")
+        return out, (lse if return_lse else None)
     st = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                         lse.data_ptr() if return_lse else None, B, H, N, d,
                         MASK_CAUSAL if causal else MASK_NONE, float(scale), _torch_dtype_code(q),
@@ -121,8 +150,9 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=N
 
 
 def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, *,
-             dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Gradients (dq, dk, dv) of sum(o * dout) for o, lse = attn_fwd(q, k, v, causal, scale).
+             dq=None, dk=None, dv=None, workspace=None, stream=None, window: int | None = None):
+    """Gradients (dq, dk, dv) of sum(o * dout) for o, lse = attn_fwd(q, k, v, causal, scale,
+    window=window) (``window`` calls ``attn_bwd_window``).
 
     All tensors are contiguous device tensors; q, k, v, o, dout share one
     [B, H, N, d] shape and dtype (float16 or bfloat16), lse is float32 [B, H, N].
@@ -150,11 +180,21 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if window is not None:
+        if not causal:
+            raise ValueError("a sliding window needs causal=True")
+        st = lib().attn_bwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), B, H, N, d, int(window), float(scale), code,
+                                   workspace.data_ptr(), ws_bytes, stream.cuda_stream)
+        if st != 0:
+            raise FaError(st, "attn_bwd_window")
+        return dq, dk, dv
     st = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
                         MASK_CAUSAL if causal else MASK_NONE, float(scale), code,
-                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                        stream.cuda_stream)
+                        workspace.data_ptr(), ws_bytes, stream.cuda_stream)
     if st != 0:
         raise FaError(st, "attn_bwd")
     return dq, dk, dv

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 // Largest query-block count times B*H that still indexes a 1-D grid, with the
 // smallest query block any kernel uses (64 rows).
 constexpr int64_t kMaxGrid = (int64_t)INT32_MAX;
@@ -31,12 +31,8 @@ int check_common(int64_t B, int64_t H, int64_t N, int64_t d, int mask, float sca
   return FA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-             int64_t H, int64_t N, int64_t d, int mask, float scale, int dtype, void* stream) {
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+             int64_t N, int64_t d, int mask, int64_t window, float scale, int dtype, void* stream) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_NULL;
@@ -46,7 +42,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
       (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
     return FA_ERR_ALIGN;
 
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, mask == FA_MASK_CAUSAL, scale};
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, mask == FA_MASK_CAUSAL, scale, window < N ? window : N};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (dtype) {
@@ -57,15 +53,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
-  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK) return 0;
-  return fa::bwd_workspace_bytes(B, H, N);
-}
-
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
-             int64_t d, int mask, float scale, int dtype, void* workspace, size_t workspace_bytes,
-             void* stream) {
+             int64_t d, int mask, int64_t window, float scale, int dtype, void* workspace,
+             size_t workspace_bytes, void* stream) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr ||
@@ -80,10 +71,49 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
     return FA_ERR_ALIGN;
-  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask == FA_MASK_CAUSAL, scale, workspace};
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask == FA_MASK_CAUSAL, scale,
+                workspace, window < N ? window : N};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f16(a, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+             int64_t H, int64_t N, int64_t d, int mask, float scale, int dtype, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, mask, N, scale, dtype, stream);
+}
+
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                    int64_t H, int64_t N, int64_t d, int64_t window, float scale, int dtype,
+                    void* stream) {
+  if (window < 1) return FA_ERR_WINDOW;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, FA_MASK_CAUSAL, window, scale, dtype, stream);
+}
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK) return 0;
+  return fa::bwd_workspace_bytes(B, H, N);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+             int64_t d, int mask, float scale, int dtype, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, N, scale, dtype, workspace,
+                  workspace_bytes, stream);
+}
+
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                    int64_t d, int64_t window, float scale, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (window < 1) return FA_ERR_WINDOW;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, FA_MASK_CAUSAL, window, scale, dtype,
+                  workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_str(int status) {
@@ -98,6 +128,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "the HIP runtime rejected a launch";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case FA_ERR_WINDOW: return "sliding window must be >= 1";
     default: return "unknown status";
   }
 }

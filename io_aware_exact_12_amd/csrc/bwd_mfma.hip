@@ -209,16 +209,17 @@ struct DkdvBlock {
   using Ld = DkdvLds<D>;
   static constexpr int kKs = D / 16, kDB = D / 32;
 
-  int lane, g, N, my_k;
+  int lane, g, N, win, my_k;
   float c;
   vec8 kf[kKs], vf[kKs];
   f32x16 acc[kDB];        // dV^T in pass V, dK^T in pass K
   int roff[kKs];          // row operand of k step kk: LDS row l32, chunk 2 kk + g
   int toff[2][kDB];       // transpose reads (elements 0..3 / 4..7) of d block db, k step 0
 
-  __device__ __forceinline__ void init(int lane_, int N_, int kw0, float c_) {
+  __device__ __forceinline__ void init(int lane_, int N_, int win_, int kw0, float c_) {
     lane = lane_;
     N = N_;
+    win = win_;
     c = c_;
     g = lane >> 5;
     my_k = kw0 + (lane & 31);
@@ -262,7 +263,7 @@ struct DkdvBlock {
     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, nl));
     if (!kMasked) return p;
     const int qi = qs0 + 16 * (r >> 3) + 8 * g + (r & 7);
-    return ((Causal && my_k > qi) || qi >= N || my_k >= N) ? 0.f : p;
+    return ((Causal && (my_k > qi || qi >= my_k + win)) || qi >= N || my_k >= N) ? 0.f : p;
   }
 
   template <bool kMasked>
@@ -337,8 +338,8 @@ template <bool IsBf16, int D, bool Causal>
 __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NLse, const float* __restrict__ Dsum,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BH, float c, float dk_mul,
-    uint32_t k_sign) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int win, int BH, float c,
+    float dk_mul, uint32_t k_sign) {
   using T = STile<D>;
   using Ld = DkdvLds<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes];
@@ -350,11 +351,14 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
   const int k0 = kblk * kRes, kw0 = k0 + 32 * wave;
 
   DkdvBlock<IsBf16, D, Causal> blk;
-  blk.init(lane, N, kw0, c);
+  blk.init(lane, N, win, kw0, c);
   load_resident<IsBf16, D>(blk.kf, K + head, N, blk.my_k, blk.g, k_sign);
   load_resident<IsBf16, D>(blk.vf, V + head, N, blk.my_k, blk.g, 0u);
 
-  const int n_tiles = (N + kT - 1) / kT;
+  // query tiles that can see these keys: from the diagonal to the end of the
+  // last key's sliding window
+  const int n_tiles = Causal ? min((N + kT - 1) / kT, (k0 + kRes - 1 + win - 1) / kT + 1)
+                             : (N + kT - 1) / kT;
   const int t_first = Causal ? k0 / kT : 0;  // earlier query tiles see none of these keys
   const int n_it = n_tiles - t_first;
   const uint16_t* q_h = Q + head;
@@ -378,10 +382,12 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
     }
   };
   // wave-uniform: does tile it reach this wave's keys, and can it need a mask?
-  auto live = [&](int it) { return kw0 < N && !(Causal && it * kT + kT - 1 < kw0); };
+  auto live = [&](int it) {
+    return kw0 < N && !(Causal && (it * kT + kT - 1 < kw0 || it * kT > kw0 + 31 + win - 1));
+  };
   auto masked = [&](int it) {
     const int qt0 = it * kT;
-    return (Causal && qt0 < kw0 + 32) || qt0 + kT > N || kw0 + 32 > N;
+    return (Causal && (qt0 < kw0 + 32 || qt0 + kT - 1 >= kw0 + win)) || qt0 + kT > N || kw0 + 32 > N;
   };
 
   issue(t_first, 0);
@@ -449,8 +455,8 @@ template <bool IsBf16, int D, bool Causal>
 __global__ __launch_bounds__(kThr, 2) void bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dsum,
-    float* __restrict__ NLse, uint16_t* __restrict__ dQ, int N, int BH, int n_qblocks, float c,
-    float dq_mul, uint32_t q_sign) {
+    float* __restrict__ NLse, uint16_t* __restrict__ dQ, int N, int win, int BH, int n_qblocks,
+    float c, float dq_mul, uint32_t q_sign) {
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using T = STile<D>;
@@ -474,6 +480,9 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
 
   const int last_row = min(N, q0 + kRes) - 1;
   const int n_tiles = Causal ? last_row / kT + 1 : (N + kT - 1) / kT;
+  // first key tile any query of the block can see (sliding window)
+  const int t_lo = Causal ? max(0, q0 - win + 1) / kT : 0;
+  const int n_it = n_tiles - t_lo;
   const bool wave_live = qw0 < N;
   const uint16_t* k_h = K + head;
   const uint16_t* v_h = V + head;
@@ -504,25 +513,25 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
     for (int rr = 0; rr < 16; ++rr) {
       const int kj = ks0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
       const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c, -lse2));
-      p[rr] = (kj >= N || (Causal && kj > my_q)) ? 0.f : pr;
+      p[rr] = (kj >= N || (Causal && (kj > my_q || kj <= my_q - win))) ? 0.f : pr;
     }
   };
 
   // ---- pass 1: D = sum_j P_ij dP_ij
   float dpart = 0.f;
-  issue(0, 0);
+  issue(t_lo, 0);
   wait_copies();
   __syncthreads();
-  for (int it = 0; it < n_tiles; ++it) {
-    const int st = it & 1;
+  for (int i = 0; i < n_it; ++i) {
+    const int it = t_lo + i, st = i & 1;
     // the next tile, or (after the last one) the first tile again for pass 2
-    issue(it + 1 < n_tiles ? it + 1 : 0, st ^ 1);
+    issue(i + 1 < n_it ? it + 1 : t_lo, st ^ 1);
     const int kt0 = it * kT;
     if (wave_live) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const int ks0 = kt0 + 32 * kh;
-        if ((Causal && ks0 > qw0 + 31) || ks0 >= N) continue;
+        if ((Causal && (ks0 > qw0 + 31 || ks0 + 31 <= qw0 - win)) || ks0 >= N) continue;
         f32x16 p, dp;
         scores(st, kh, ks0, p, dp);
 #pragma unroll
@@ -538,19 +547,19 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
     NLse[(int64_t)bh * N + my_q] = -lse2;  // read by the dK/dV kernel
   }
 
-  // ---- pass 2: dQ^T += K^T dS^T; tile 0 is already in stage n_tiles & 1
+  // ---- pass 2: dQ^T += K^T dS^T; tile t_lo is already in stage n_it & 1
   f32x16 dq[kDB];
 #pragma unroll
   for (int i = 0; i < kDB; ++i) dq[i] = f32x16{};
-  for (int it = 0; it < n_tiles; ++it) {
-    const int st = (it + n_tiles) & 1;
-    if (it + 1 < n_tiles) issue(it + 1, st ^ 1);
+  for (int i = 0; i < n_it; ++i) {
+    const int it = t_lo + i, st = (i + n_it) & 1;
+    if (i + 1 < n_it) issue(it + 1, st ^ 1);
     const int kt0 = it * kT;
     if (wave_live) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const int ks0 = kt0 + 32 * kh;
-        if ((Causal && ks0 > qw0 + 31) || ks0 >= N) continue;
+        if ((Causal && (ks0 > qw0 + 31 || ks0 + 31 <= qw0 - win)) || ks0 >= N) continue;
         f32x16 p, dp;
         scores(st, kh, ks0, p, dp);
         u32x4 sw[2];
@@ -581,6 +590,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
   // |scale| * log2(e); a zero scale is run as the limit scale -> 0+
   const float c = a.scale != 0.f ? __builtin_fabsf(a.scale) * 1.4426950408889634f : 1e-30f;
   const uint32_t q_sign = a.scale < 0.f ? 0x80008000u : 0u;
+  const int win = (int)(a.window < a.N ? a.window : a.N);  // sliding window (N: plain causal)
   const auto* q = static_cast<const uint16_t*>(a.q);
   const auto* k = static_cast<const uint16_t*>(a.k);
   const auto* v = static_cast<const uint16_t*>(a.v);
@@ -590,14 +600,14 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
   float* nlse = dsum + a.B * a.H * a.N;
   // dQ (and D into the workspace) first; dK, dV read D afterwards on the same stream
   hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st, q,
-                     k, v, dout, a.lse, dsum, nlse, static_cast<uint16_t*>(a.dq), N, BH, nblk, c,
-                     a.scale, q_sign);
+                     k, v, dout, a.lse, dsum, nlse, static_cast<uint16_t*>(a.dq), N, win, BH, nblk,
+                     c, a.scale, q_sign);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dK = scale dS^T Q; a negative scale flips the resident K instead of Q
   hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
                      q, k, v, dout, nlse, dsum, static_cast<uint16_t*>(a.dk),
-                     static_cast<uint16_t*>(a.dv), N, BH, c, a.scale, q_sign);
+                     static_cast<uint16_t*>(a.dv), N, win, BH, c, a.scale, q_sign);
   return hipGetLastError();
 }
 

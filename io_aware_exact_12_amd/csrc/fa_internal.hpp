@@ -17,6 +17,9 @@ struct FwdArgs {
   int64_t B, H, N, d;
   bool causal;
   float scale;
+  // causal only: key j is visible to query i iff i - window < j <= i
+  // (window >= N is plain causal)
+  int64_t window;
 };
 
 // Arguments of one backward launch after validation.  workspace holds at
@@ -35,6 +38,7 @@ struct BwdArgs {
   bool causal;
   float scale;
   void* workspace;
+  int64_t window;  // as for FwdArgs
 };
 
 // Launchers return the hipError_t of the launch (hipSuccess when enqueued).

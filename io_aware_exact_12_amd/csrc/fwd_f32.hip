@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
                                                          const float* __restrict__ V,
                                                          float* __restrict__ O,
                                                          float* __restrict__ LSE, int N,
-                                                         int n_qblocks, float scale) {
+                                                         int win, int n_qblocks, float scale) {
   constexpr int kQStride = D + 1;  // odd stride: lanes reading their own row hit distinct banks
   __shared__ float qs[kRows * kQStride];
   __shared__ __attribute__((aligned(16))) float ks[kKeys * D];
@@ -52,6 +52,8 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   const int my_q = q0 + lane;
   const int last_row = min(N, q0 + kRows) - 1;
   const int n_keys = Causal ? last_row + 1 : N;
+  // first key any row of the block can see (sliding window; 0 without one)
+  const int key_lo = Causal ? max(0, q0 - win + 1) / kKeys * kKeys : 0;
 
   float acc[D];
 #pragma unroll
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   double m_run = -INFINITY, l_run = 0.0;
   const double dscale = (double)scale;
 
-  for (int key0 = 0; key0 < n_keys; key0 += kKeys) {
+  for (int key0 = key_lo; key0 < n_keys; key0 += kKeys) {
     __syncthreads();  // previous tile fully consumed (and Q staged on the first pass)
     for (int idx = lane; idx < kKeys * D / 4; idx += kRows) {
       const int r = (idx * 4) / D, col = (idx * 4) % D;
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
 #pragma unroll
     for (int j = 0; j < kKeys; ++j) {
       const int key = key0 + j;
-      const bool hide = key >= N || (Causal && key > my_q);
+      const bool hide = key >= N || (Causal && (key > my_q || key <= my_q - win));
       t[j] = hide ? -INFINITY : t[j] * dscale;
       tmax = fmax(tmax, t[j]);
     }
@@ -125,8 +127,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(n_qblocks * a.B * a.H));
   hipLaunchKernelGGL((fwd_f32_kernel<D, Causal>), grid, dim3(kRows), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
-                     static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, N, n_qblocks,
-                     a.scale);
+                     static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, N,
+                     (int)(a.window < a.N ? a.window : a.N), n_qblocks, a.scale);
   return hipGetLastError();
 }
 

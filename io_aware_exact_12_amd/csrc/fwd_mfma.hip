@@ -65,6 +65,13 @@ constexpr int kThreads = 64 * kWaves;
 // A block whose partial row sum (16 probabilities of one lane half) exceeds
 // this moves the reference maximum; it bounds every probability by 2^8.
 constexpr float kSumCap = 256.0f;
+// Exponent offset of a row that has no reference yet (every key seen so far
+// hidden): any visible score then gives probability +inf, so the row sum
+// exceeds kSumCap and the block moves the reference; a hidden one gives 0.
+constexpr float kNoRef = 1e30f;
+// Masks a block of scores may need: none, the causal diagonal and the
+// sequence end, or those and the left edge of a sliding window.
+constexpr int kMaskNone = 0, kMaskEdge = 1, kMaskWindow = 2;
 
 // LDS row strides (bytes).  K rows carry 16 bytes of padding: the sixteen
 // lanes of a 16-byte operand read touch sixteen consecutive rows, which then
@@ -87,8 +94,11 @@ template <int D> struct Lds {
 
 // Per-workgroup state and steps of the forward pass.  Everything here is
 // device-only; the kernel below only constructs it and runs the tile loop.
-template <bool IsBf16, int D, bool Causal>
+// Window (causal only) adds a sliding window narrower than the sequence: key
+// j is visible to query i iff i - win < j <= i.
+template <bool IsBf16, int D, bool Causal, bool Window>
 struct FwdBlock {
+  static constexpr bool kWin = Causal && Window;
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using L = Lds<D>;
@@ -113,7 +123,8 @@ struct FwdBlock {
   const uint8_t* k_ptr;  // K and V of this head (wave-uniform)
   const uint8_t* v_ptr;
   uint32_t head_bytes;
-  int N, wave, lane, l32, g, q0, my_q, n_tiles, n_sub;
+  int N, win, wave, lane, l32, g, q0, my_q, n_tiles, n_sub;
+  int u_lo;   // first 32-key block this wave computes (sliding window)
   float c;
   uint32_t src_k[kFullK], src_v[kFullV], src_x;  // per-lane source offsets of the copies
   // The extra copy writes LDS byte x_off + (K stage offset & x_kmask) +
@@ -125,7 +136,7 @@ struct FwdBlock {
   vec8 qf[kKs];       // Q^T B operands: query my_q, d = 16 ks + 8 g + 0..7
   f32x16 acc[kDB];    // O^T: d = 32 db + 8 (r/4) + 4 g + r%4 of query my_q
   float m_ref;        // reference maximum the probabilities are taken against
-  float neg_mc;       // -m_ref * c
+  float neg_mc;       // -m_ref * c, or kNoRef while m_ref = -inf
   float l_part;       // this lane half's share of the denominator
   f32x16 s_cur;       // scores of the block being exponentiated
   u32x4 p_prev[2];    // probabilities of the previous block (B operands)
@@ -146,10 +157,11 @@ struct FwdBlock {
   }
 
   __device__ __forceinline__ void init(uint8_t* lds, const uint16_t* Q, const uint16_t* K,
-                                       const uint16_t* V, int N_, int bh, int qb, float c_,
+                                       const uint16_t* V, int N_, int win_, int bh, int qb, float c_,
                                        uint32_t q_sign) {
     smem = lds;
     N = N_;
+    win = win_;
     c = c_;
     const int tid = threadIdx.x;
     lane = tid & 63;
@@ -171,6 +183,8 @@ struct FwdBlock {
     const int wave_last_row = min(N, q0 + 32) - 1;
     const int all_sub = (N + 31) / 32;
     n_sub = q0 >= N ? 0 : (Causal ? min(all_sub, wave_last_row / 32 + 1) : all_sub);
+    // blocks before the window of the wave's first query are skipped
+    u_lo = kWin ? max(0, q0 - win + 1) / 32 : 0;
 
     // Q^T fragments; rows past N read as zeros through the buffer bounds
     const __amdgpu_buffer_rsrc_t q_rs =
@@ -218,8 +232,17 @@ struct FwdBlock {
 #pragma unroll
     for (int i = 0; i < kDB; ++i) acc[i] = f32x16{};
     m_ref = -INFINITY;
-    neg_mc = 0.f;
+    neg_mc = kNoRef;
     l_part = 0.f;
+    if (kWin) {
+      // A wave whose window starts after the workgroup's first step begins
+      // with a normal block: zeros make its PV MFMAs add 0 and send it down
+      // the reference-update path.
+      s_cur = f32x16{};
+      p_prev[0] = p_prev[1] = u32x4{};
+#pragma unroll
+      for (int i = 0; i < kPV; ++i) vfr[i] = vec8{};
+    }
   }
 
   // Copy K tile jk into K stage sk and V tile jv into V stage sv (a tile at
@@ -257,17 +280,20 @@ struct FwdBlock {
     __builtin_amdgcn_s_waitcnt(0x0F70 | kCopies);
   }
 
-  __device__ __forceinline__ bool sub_masked(int u) const {
-    return (Causal && 32 * u + 31 > q0) || (32 * u + 32 > N);
-  }
-
-  // Hide keys of block u that this lane's query may not see (causal
-  // diagonal, sequence end).
+  // Hide keys of block u that this lane's query may not see: the causal
+  // diagonal and the sequence end, and with kMaskWindow also keys left of the
+  // query's sliding window.
+  template <int kMask>
   __device__ __forceinline__ void apply_mask(int u, f32x16& st) const {
     // register r of lane half g holds key 32 u + 16 (r >> 3) + 8 g + (r & 7)
     const int lim = (Causal ? min(my_q, N - 1) : N - 1) - 32 * u - 8 * g;
+    const int lo = my_q - win + 1 - 32 * u - 8 * g;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st[r] = (16 * (r >> 3) + (r & 7)) > lim ? -INFINITY : st[r];
+    for (int r = 0; r < 16; ++r) {
+      const int o = 16 * (r >> 3) + (r & 7);
+      const bool hide = (kMask == kMaskWindow && kWin) ? (o > lim || o < lo) : o > lim;
+      st[r] = hide ? -INFINITY : st[r];
+    }
   }
 
   // Probabilities of scores 2e, 2e+1 against the current reference, packed
@@ -288,7 +314,7 @@ struct FwdBlock {
     const float m_new = fmaxf(m_ref, xhalf_max(mx));
     const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
     m_ref = m_new;
-    neg_mc = (m_new == -INFINITY) ? 0.f : -m_new * c;
+    neg_mc = (m_new == -INFINITY) ? kNoRef : -m_new * c;
     l_part *= alpha;
 #pragma unroll
     for (int db = 0; db < kDB; ++db) acc[db] *= alpha;
@@ -296,14 +322,14 @@ struct FwdBlock {
 
   // Scores of block u (K tile u/2, half u&1, still resident in LDS during the
   // tile step that holds block u), masked when kMask.
-  template <bool kMask>
+  template <int kMask>
   __device__ __forceinline__ f32x16 scores(int u) const {
     const uint8_t* kt = k_stage((u >> 1) & 3) + k_base + (u & 1) * 32 * L::kKStride;
     f32x16 st = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < kKs; ++kk)
       st = E::mfma(*reinterpret_cast<const vec8*>(kt + kk * 32), qf[kk], st);
-    if (kMask) apply_mask(u, st);
+    if (kMask != kMaskNone) apply_mask<kMask>(u, st);
     return st;
   }
 
@@ -312,12 +338,12 @@ struct FwdBlock {
   // slot run in program order.
   template <int kSlots>
   static constexpr int slot_of(int e, int st) {
-    return kSlots == 16 ? e + (st == 0 ? 0 : st == 1 ? 2 : st == 2 ? 5 : 7)
+    return kSlots == 16 ? e + (st == 0 ? 0 : st == 1 ? 2 : 5)
          : kSlots == 8  ? e / 2 + st
                         : (e / 4 + st < 3 ? e / 4 + st : 3);
   }
 
-  // Block u: PV MFMAs of block u-1 (unless kFirst), score MFMAs of block u+1,
+  // Block u: PV MFMAs of block u-1 (none if kFirst), score MFMAs of block u+1,
   // and between them the probabilities of block u.  On entry s_cur holds the
   // scores of block u, p_prev / vfr the operands of block u-1.  The K operand
   // read for score MFMA i is issued right after PV MFMA i, the V operand read
@@ -326,7 +352,14 @@ struct FwdBlock {
   // operand the preceding MFMA just consumed.  On a wave's last block the
   // scores of "block u+1" are still formed from whatever the K stage holds and
   // never used, so every block runs the same code.
-  template <bool kFirst, bool kMask>
+  //
+  // A wave's first block is either kFirst (its scores were formed in the
+  // prologue and it sets the reference from them), or, for a wave whose
+  // sliding window starts after the workgroup's first tile step, a normal
+  // block: the zeros in s_cur, seen against kNoRef, send it down the
+  // reference-update path, which forms its scores from LDS, while
+  // p_prev = vfr = 0 make its PV MFMAs add 0.
+  template <int kMask, bool kFirst = false>
   __device__ __forceinline__ void block(int u) {
     static_assert(kPV == kKs, "as many PV as score MFMAs per block (d = 64 or 128)");
     constexpr int kMfmas = (kFirst ? 0 : kPV) + kKs;
@@ -341,7 +374,7 @@ struct FwdBlock {
 #pragma unroll
       for (int i = 0; i < kKs; ++i) kfr[i] = *reinterpret_cast<const vec8*>(kt + i * 32);
     }
-    if (kMask) apply_mask(u, s_cur);
+    if (kMask != kMaskNone) apply_mask<kMask>(u, s_cur);
     if (kFirst) raise_reference(s_cur);  // the first block sets the reference outright
 
     u32x4 pw[2];
@@ -389,8 +422,9 @@ struct FwdBlock {
     }
     float s_tot = sum[0] + sum[1];
     if (!kFirst && __builtin_amdgcn_ballot_w64(s_tot > kSumCap) != 0) {
-      // rare: some probability of this block may exceed the cap.  The scores
-      // are formed again from LDS rather than kept live through the block.
+      // rare: some probability of this block may exceed the cap (or a row
+      // sees its first key).  The scores are formed again from LDS rather
+      // than kept live through the block.
       const f32x16 st = scores<kMask>(u);
       raise_reference(st);
       s_tot = 0.f;
@@ -417,50 +451,64 @@ struct FwdBlock {
   // K tile j-1 left) and V tile j+2 (into the stage V tile j-2 left) and,
   // before its closing barrier, waits only for the copies issued one step
   // earlier, so every copy has two steps to land.
-  template <bool kMaskable>
+  //
+  // In the workgroup's first step (kFirstStep) a wave whose first block u_lo
+  // lies in the step runs it as kFirst; u_lo is never below 2j there.
+  template <int kMask, bool kFirstStep = false>
   __device__ __forceinline__ void step(int j) {
     load_tiles(j + 3, (j + 3) & 3, j + 2, (j + 2) & 3);
+    if (kFirstStep) {
+      if (u_lo == 2 * j && u_lo < n_sub) block<kMask, true>(2 * j);
+      if (u_lo == 2 * j + 1 && u_lo < n_sub)
+        block<kMask, true>(2 * j + 1);
+      else if (u_lo == 2 * j && 2 * j + 1 < n_sub)
+        block<kMask>(2 * j + 1);
+    } else {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int u = 2 * j + h;
-      if (u < n_sub) {
-        block<false, kMaskable>(u);
+      for (int h = 0; h < 2; ++h) {
+        const int u = 2 * j + h;
+        if (u >= u_lo && u < n_sub) block<kMask>(u);
       }
     }
     wait_older_copies();
     __syncthreads();
   }
 
-  // LDS holds rings of kStages K tiles and kStages V tiles.
+  // LDS holds rings of kStages K tiles and kStages V tiles; tile j lives in
+  // stage j & 3.  The workgroup's first tile j_lo is the first one that any of
+  // its queries can see (0 unless a sliding window starts later).
   __device__ __forceinline__ void run(int q0_blk) {
     static_assert(kStages == 4, "the ring arithmetic assumes four stages");
-    // prologue: K0, V0, K1, V1 resident; K2 in flight (its V slot copies
-    // zeros into V stage 3, which V tile 3 overwrites one step later)
-    load_tiles(0, 0, 0, 0);
-    load_tiles(1, 1, 1, 1);
-    load_tiles(2, 2, n_tiles, 3);
+    const int j_lo = kWin ? max(0, q0_blk - win + 1) / kBN : 0;
+    // prologue: K, V tiles j_lo, j_lo+1 resident; K tile j_lo+2 in flight (its
+    // V slot copies zeros into the stage V tile j_lo+3 overwrites one step later)
+    load_tiles(j_lo, j_lo & 3, j_lo, j_lo & 3);
+    load_tiles(j_lo + 1, (j_lo + 1) & 3, j_lo + 1, (j_lo + 1) & 3);
+    load_tiles(j_lo + 2, (j_lo + 2) & 3, n_tiles, (j_lo + 3) & 3);
     wait_older_copies();
     __syncthreads();
-    if (n_sub > 0) s_cur = scores<false>(0);
-    // step 0 holds the first block
-    load_tiles(3, 3, 2, 2);
-    if (n_sub > 0) block<true, true>(0);
-    if (n_sub > 1) block<false, true>(1);
-    wait_older_copies();
-    __syncthreads();
+    // scores of the first block of every wave that starts in the first step
+    // (all of them without a sliding window); K tile j_lo is resident
+    if (u_lo < 2 * j_lo + 2 && u_lo < n_sub) s_cur = scores<kMaskNone>(u_lo);
 
-    // first step in which some wave's block may need a mask
+    // Steps that may need a mask: those before j_left (some query's window
+    // starts inside one of their blocks) and from j_mask on (causal diagonal
+    // or the end of the sequence).
+    const int u_left = kWin ? (max(0, q0_blk + kBM - win) + 31) / 32 : 0;
+    const int j_left = (u_left + 1) / 2;
     const int u_mask = Causal ? q0_blk / 32 : ((N % 32) ? N / 32 : (N + 31) / 32 + 2);
-    const int j_mask = max(1, u_mask / 2);
-    int j = 1;
-    for (; j < min(j_mask, n_tiles); ++j) step<false>(j);
-    for (; j < n_tiles; ++j) step<true>(j);
-    if (n_sub > 0) drain();
+    const int j_mask = max(j_left, u_mask / 2);
+    step<kMaskWindow, true>(j_lo);
+    int j = j_lo + 1;
+    for (; j < min(j_left, n_tiles); ++j) step<kMaskWindow>(j);
+    for (; j < min(j_mask, n_tiles); ++j) step<kMaskNone>(j);
+    for (; j < n_tiles; ++j) step<kMaskEdge>(j);
+    if (n_sub > u_lo) drain();
   }
 
   // O = a / l once; LSE = ln(sum) of the scaled scores
   __device__ __forceinline__ void store(uint16_t* O, float* LSE, int bh) {
-    if (n_sub == 0) return;
+    if (n_sub <= u_lo) return;
     const float l_tot = xhalf_sum(l_part);
     const float inv = 1.0f / l_tot;
     if (my_q >= N) return;
@@ -481,23 +529,23 @@ struct FwdBlock {
   }
 };
 
-template <bool IsBf16, int D, bool Causal>
+template <bool IsBf16, int D, bool Causal, bool Window>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int BH, int n_qblocks, float c,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int win, int BH, int n_qblocks, float c,
     uint32_t q_sign) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds<D>::kBytes];
   // work item: (query block, batch*head); heaviest causal blocks first
   const int bh = blockIdx.x % BH;
   int qb = blockIdx.x / BH;
   if (Causal) qb = n_qblocks - 1 - qb;
-  FwdBlock<IsBf16, D, Causal> blk;
-  blk.init(smem, Q, K, V, N, bh, qb, c, q_sign);
+  FwdBlock<IsBf16, D, Causal, Window> blk;
+  blk.init(smem, Q, K, V, N, win, bh, qb, c, q_sign);
   blk.run(qb * kBM);
   blk.store(O, LSE, bh);
 }
 
-template <bool IsBf16, int D, bool Causal>
+template <bool IsBf16, int D, bool Causal, bool Window>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int N = (int)a.N;
   const int BH = (int)(a.B * a.H);
@@ -508,17 +556,23 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   // so all visible keys weigh exactly 1 and hidden ones (-inf) weigh 0.
   const float c = a.scale != 0.f ? __builtin_fabsf(a.scale) * 1.4426950408889634f : 1e-30f;
   const uint32_t q_sign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_kernel<IsBf16, D, Causal>), grid, dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fwd_kernel<IsBf16, D, Causal, Window>), grid, dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, N, BH,
-                     n_qblocks, c, q_sign);
+                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, N,
+                     (int)(a.window < a.N ? a.window : a.N), BH, n_qblocks, c, q_sign);
   return hipGetLastError();
+}
+
+template <bool IsBf16, int D>
+hipError_t dispatch_d(const FwdArgs& a, hipStream_t s) {
+  if (!a.causal) return launch<IsBf16, D, false, false>(a, s);
+  if (a.window < a.N) return launch<IsBf16, D, true, true>(a, s);
+  return launch<IsBf16, D, true, false>(a, s);
 }
 
 template <bool IsBf16>
 hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
-  if (a.d == 128) return a.causal ? launch<IsBf16, 128, true>(a, s) : launch<IsBf16, 128, false>(a, s);
-  return a.causal ? launch<IsBf16, 64, true>(a, s) : launch<IsBf16, 64, false>(a, s);
+  return a.d == 128 ? dispatch_d<IsBf16, 128>(a, s) : dispatch_d<IsBf16, 64>(a, s);
 }
 
 }  // namespace

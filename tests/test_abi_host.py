@@ -13,7 +13,7 @@ import pytest
 import io_aware_exact_12_amd as fa
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_DTYPE, FA_ERR_MASK, FA_ERR_SCALE, \
-    FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_ALIGN = range(10)
+    FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_ALIGN, FA_ERR_WINDOW = range(11)
 
 # fake, never-dereferenced addresses: validation fails before any use
 P = [0x10000 * (i + 1) for i in range(8)]
@@ -26,15 +26,16 @@ def fwd(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=16, d=64, mask=0, 
 
 def test_library_exports_every_declared_symbol():
     declared = fa.declared_symbols()
-    assert {"attn_fwd", "fa_status_str", "fa_abi_version"} <= set(declared)
+    assert {"attn_fwd", "attn_bwd", "attn_fwd_window", "attn_bwd_window", "attn_bwd_workspace_bytes",
+            "fa_status_str", "fa_abi_version"} <= set(declared)
     lib = ctypes.CDLL(fa._binding.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
-    assert fa.lib().fa_abi_version() >= 1
+    assert fa.lib().fa_abi_version() == 2
 
 
 def test_status_strings():
-    for st in range(10):
+    for st in range(11):
         assert fa.status_str(st)
     assert fa.status_str(123) == "unknown status"
 
@@ -131,3 +132,35 @@ def test_bwd_workspace_query():
     assert fa.bwd_workspace_bytes(4, 16, 4096, 128, fa.BF16) == 8 * 4 * 16 * 4096
     assert fa.bwd_workspace_bytes(0, 16, 4096, 128, fa.BF16) == 0
     assert fa.bwd_workspace_bytes(1, 1, 16, 96, fa.BF16) == 0
+
+
+# ---------------------------------------------------------------- sliding window
+
+def fwd_w(window, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=16, d=64, scale=0.125,
+          dtype=fa.BF16):
+    return fa.attn_fwd_window_raw(q, k, v, o, lse, B, H, N, d, window, scale, dtype, None)
+
+
+def bwd_w(window, ws_bytes=1 << 20, **kw):
+    a = dict(B=1, H=1, N=16, d=64, scale=0.125, dtype=fa.BF16)
+    a.update(kw)
+    return fa.attn_bwd_window_raw(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], a["B"],
+                                  a["H"], a["N"], a["d"], window, a["scale"], a["dtype"], P[1],
+                                  ws_bytes, None)
+
+
+@pytest.mark.parametrize("window", [0, -1, -(2**40)])
+def test_window_below_one_rejected(window):
+    assert fwd_w(window) == FA_ERR_WINDOW
+    assert bwd_w(window) == FA_ERR_WINDOW
+
+
+def test_window_checks_like_the_plain_calls():
+    assert fwd_w(4, q=None) == FA_ERR_NULL
+    assert fwd_w(4, N=0) == FA_ERR_SHAPE
+    assert fwd_w(4, d=96) == FA_ERR_UNSUPPORTED
+    assert fwd_w(4, dtype=7) == FA_ERR_DTYPE
+    assert fwd_w(4, scale=math.inf) == FA_ERR_SCALE
+    assert fwd_w(4, q=P[0] + 8) == FA_ERR_ALIGN
+    assert bwd_w(4, dtype=fa.F32) == FA_ERR_UNSUPPORTED
+    assert bwd_w(4, ws_bytes=8) == FA_ERR_WORKSPACE
