@@ -5,13 +5,16 @@ One step = one ``attn_fwd`` call over the long-context causal workload
 N(0, 1) inputs already resident in device memory.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd]
+                    [--no-window]
 
 The reported throughput counts algorithmic FLOPs only: 4 * d * (visible query-key
 pairs) * B * H, i.e. the two matrix products over the causal triangle.
 
 The same line carries, under "attn_bwd", the backward pass timed the same way
 on its own workload (B=4, H=16, N=4096, d=128, bf16, causal), counted as
-10 * d * pairs * B * H algorithmic FLOPs (S and dP recomputed, dV, dQ, dK).
+10 * d * pairs * B * H algorithmic FLOPs (S and dP recomputed, dV, dQ, dK), and
+under "attn_fwd_window" the forward of the long-context head with a causal
+sliding window of 1024 keys (4 * d * windowed pairs * B * H FLOPs).
 """
 from __future__ import annotations
 
@@ -143,6 +146,37 @@ def bwd_record(fa, workloads, torch, steps, warmup):
                          "algorithmic_flops_per_launch": flops}}
 
 
+def window_record(fa, workloads, torch, steps, warmup):
+    """Sliding-window forward on its own workload, timed like the forward."""
+    w = workloads.WORKLOADS["long_window_bf16"]
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(torch.bfloat16).contiguous() for n in "qkv")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.attn_fwd(q, k, v, causal=True, window=w.window, scale=w.scale, out=o, lse=lse,
+                    stream=torch.cuda.current_stream(dev))
+
+    ms, warm = time_graph(step, steps, warmup, torch)
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    flops = w.fwd_flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"metric": f"attention fwd TFLOP/s (bf16, causal sliding window {w.window}, "
+                      f"T={w.N}, d={w.d})",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warm,
+            "ms_per_step": round(ms, 5),
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                       "mask": "causal", "window": w.window, "scale": w.scale,
+                       "inputs": "Q, K, V i.i.d. N(0,1) rounded to bf16, seed 6"},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "kernel": "fwd_kernel<bf16, d=128, causal, window>",
+                         "algorithmic_flops_per_launch": flops}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +187,10 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--bwd-steps", type=int, default=40)
     ap.add_argument("--bwd-warmup", type=int, default=300)
+    ap.add_argument("--no-window", action="store_true",
+                    help="skip the sliding-window forward measurement")
+    ap.add_argument("--window-steps", type=int, default=200)
+    ap.add_argument("--window-warmup", type=int, default=1500)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times), "
                          "the reference kernel for scaling HBM byte counters, and exit")
@@ -228,6 +266,9 @@ def main():
     }
     if not args.no_bwd:
         record["attn_bwd"] = bwd_record(fa, workloads, torch, args.bwd_steps, args.bwd_warmup)
+    if not args.no_window:
+        record["attn_fwd_window"] = window_record(fa, workloads, torch, args.window_steps,
+                                                  args.window_warmup)
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(record), flush=True)

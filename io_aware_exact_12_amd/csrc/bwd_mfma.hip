@@ -201,8 +201,9 @@ template <int D> struct DkdvLds {
   static constexpr int kBytes = 2 * kStage;
 };
 
-template <bool IsBf16, int D, bool Causal>
+template <bool IsBf16, int D, bool Causal, bool Window>
 struct DkdvBlock {
+  static constexpr bool kWin = Causal && Window;  // sliding window narrower than N
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using T = STile<D>;
@@ -263,7 +264,7 @@ struct DkdvBlock {
     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, nl));
     if (!kMasked) return p;
     const int qi = qs0 + 16 * (r >> 3) + 8 * g + (r & 7);
-    return ((Causal && (my_k > qi || qi >= my_k + win)) || qi >= N || my_k >= N) ? 0.f : p;
+    return ((Causal && my_k > qi) || (kWin && qi >= my_k + win) || qi >= N || my_k >= N) ? 0.f : p;
   }
 
   template <bool kMasked>
@@ -334,7 +335,7 @@ struct DkdvBlock {
   }
 };
 
-template <bool IsBf16, int D, bool Causal>
+template <bool IsBf16, int D, bool Causal, bool Window>
 __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NLse, const float* __restrict__ Dsum,
@@ -350,15 +351,16 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
   const int64_t head = (int64_t)bh * N * D;
   const int k0 = kblk * kRes, kw0 = k0 + 32 * wave;
 
-  DkdvBlock<IsBf16, D, Causal> blk;
+  constexpr bool kWin = Causal && Window;
+  DkdvBlock<IsBf16, D, Causal, Window> blk;
   blk.init(lane, N, win, kw0, c);
   load_resident<IsBf16, D>(blk.kf, K + head, N, blk.my_k, blk.g, k_sign);
   load_resident<IsBf16, D>(blk.vf, V + head, N, blk.my_k, blk.g, 0u);
 
   // query tiles that can see these keys: from the diagonal to the end of the
   // last key's sliding window
-  const int n_tiles = Causal ? min((N + kT - 1) / kT, (k0 + kRes - 1 + win - 1) / kT + 1)
-                             : (N + kT - 1) / kT;
+  const int n_tiles = kWin ? min((N + kT - 1) / kT, (k0 + kRes - 1 + win - 1) / kT + 1)
+                           : (N + kT - 1) / kT;
   const int t_first = Causal ? k0 / kT : 0;  // earlier query tiles see none of these keys
   const int n_it = n_tiles - t_first;
   const uint16_t* q_h = Q + head;
@@ -383,11 +385,12 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
   };
   // wave-uniform: does tile it reach this wave's keys, and can it need a mask?
   auto live = [&](int it) {
-    return kw0 < N && !(Causal && (it * kT + kT - 1 < kw0 || it * kT > kw0 + 31 + win - 1));
+    return kw0 < N && !(Causal && it * kT + kT - 1 < kw0) && !(kWin && it * kT > kw0 + 31 + win - 1);
   };
   auto masked = [&](int it) {
     const int qt0 = it * kT;
-    return (Causal && (qt0 < kw0 + 32 || qt0 + kT - 1 >= kw0 + win)) || qt0 + kT > N || kw0 + 32 > N;
+    return (Causal && qt0 < kw0 + 32) || (kWin && qt0 + kT - 1 >= kw0 + win) || qt0 + kT > N ||
+           kw0 + 32 > N;
   };
 
   issue(t_first, 0);
@@ -451,7 +454,7 @@ template <int D> struct DqLds {
   static constexpr int kBytes = 2 * kStage;
 };
 
-template <bool IsBf16, int D, bool Causal>
+template <bool IsBf16, int D, bool Causal, bool Window>
 __global__ __launch_bounds__(kThr, 2) void bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dsum,
@@ -481,7 +484,8 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
   const int last_row = min(N, q0 + kRes) - 1;
   const int n_tiles = Causal ? last_row / kT + 1 : (N + kT - 1) / kT;
   // first key tile any query of the block can see (sliding window)
-  const int t_lo = Causal ? max(0, q0 - win + 1) / kT : 0;
+  constexpr bool kWin = Causal && Window;
+  const int t_lo = kWin ? max(0, q0 - win + 1) / kT : 0;
   const int n_it = n_tiles - t_lo;
   const bool wave_live = qw0 < N;
   const uint16_t* k_h = K + head;
@@ -513,7 +517,7 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
     for (int rr = 0; rr < 16; ++rr) {
       const int kj = ks0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
       const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c, -lse2));
-      p[rr] = (kj >= N || (Causal && (kj > my_q || kj <= my_q - win))) ? 0.f : pr;
+      p[rr] = (kj >= N || (Causal && kj > my_q) || (kWin && kj <= my_q - win)) ? 0.f : pr;
     }
   };
 
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const int ks0 = kt0 + 32 * kh;
-        if ((Causal && (ks0 > qw0 + 31 || ks0 + 31 <= qw0 - win)) || ks0 >= N) continue;
+        if ((Causal && ks0 > qw0 + 31) || (kWin && ks0 + 31 <= qw0 - win) || ks0 >= N) continue;
         f32x16 p, dp;
         scores(st, kh, ks0, p, dp);
 #pragma unroll
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const int ks0 = kt0 + 32 * kh;
-        if ((Causal && (ks0 > qw0 + 31 || ks0 + 31 <= qw0 - win)) || ks0 >= N) continue;
+        if ((Causal && ks0 > qw0 + 31) || (kWin && ks0 + 31 <= qw0 - win) || ks0 >= N) continue;
         f32x16 p, dp;
         scores(st, kh, ks0, p, dp);
         u32x4 sw[2];
@@ -582,7 +586,7 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
   store_row<IsBf16, D>(dQ + head, my_q, g, dq, dq_mul);
 }
 
-template <bool IsBf16, int D, bool Causal>
+template <bool IsBf16, int D, bool Causal, bool Window>
 hipError_t launch(const BwdArgs& a, hipStream_t st) {
   const int N = (int)a.N;
   const int BH = (int)(a.B * a.H);
@@ -599,22 +603,30 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
   float* dsum = static_cast<float*>(a.workspace);
   float* nlse = dsum + a.B * a.H * a.N;
   // dQ (and D into the workspace) first; dK, dV read D afterwards on the same stream
-  hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st, q,
+  hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal, Window>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st, q,
                      k, v, dout, a.lse, dsum, nlse, static_cast<uint16_t*>(a.dq), N, win, BH, nblk,
                      c, a.scale, q_sign);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dK = scale dS^T Q; a negative scale flips the resident K instead of Q
-  hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
+  hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal, Window>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
                      q, k, v, dout, nlse, dsum, static_cast<uint16_t*>(a.dk),
                      static_cast<uint16_t*>(a.dv), N, win, BH, c, a.scale, q_sign);
   return hipGetLastError();
 }
 
+// A causal window narrower than N runs the Window instantiations; plain causal
+// and unmasked calls run code with no window arithmetic.
+template <bool IsBf16, int D>
+hipError_t dispatch_d(const BwdArgs& a, hipStream_t s) {
+  if (!a.causal) return launch<IsBf16, D, false, false>(a, s);
+  if (a.window < a.N) return launch<IsBf16, D, true, true>(a, s);
+  return launch<IsBf16, D, true, false>(a, s);
+}
+
 template <bool IsBf16>
 hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
-  if (a.d == 128) return a.causal ? launch<IsBf16, 128, true>(a, s) : launch<IsBf16, 128, false>(a, s);
-  return a.causal ? launch<IsBf16, 64, true>(a, s) : launch<IsBf16, 64, false>(a, s);
+  return a.d == 128 ? dispatch_d<IsBf16, 128>(a, s) : dispatch_d<IsBf16, 64>(a, s);
 }
 
 }  // namespace

@@ -464,6 +464,17 @@ def test_workload_flops_and_bytes():
     assert w.fwd_bytes() == 134742016
 
 
+@pytest.mark.parametrize("n,win", [(1, 1), (7, 1), (7, 3), (7, 7), (7, 50), (64, 17)])
+def test_workload_window_pairs_count_the_mask(n, win):
+    """The pair count of a windowed workload is the number of visible entries
+    of the oracle's own mask, counted by brute force."""
+    w = workloads.Workload("t", "bf16", True, 1, 1, n, 16, seed=0, window=win)
+    probs = oracle.dense_probs(np.eye(n, 16), np.eye(n, 16), causal=True, window=win)
+    assert w.pairs() == int((probs > 0).sum())
+    full = workloads.WORKLOADS["long_window_bf16"]
+    assert full.pairs() == 1024 * 1025 // 2 + (8192 - 1024) * 1024
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def _mutant_online(q, k, v, causal, scale, qb, kb, bug):

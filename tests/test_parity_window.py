@@ -84,6 +84,18 @@ def test_window_fwd_long_sampled_rows(fa):
     fwd_case(fa, x, "bf16", w, rows=rows)
 
 
+def test_window_bench_workload_sampled_rows(fa):
+    """The benchmarked window workload at full size (B=1, H=16, N=8192, d=128,
+    W=1024, bf16), in the launch the benchmark times, on sampled rows of
+    every head: the first window, its edge, the tail and random rows."""
+    w = workloads.WORKLOADS["long_window_bf16"]
+    log(f"case window bench workload {w.name} N={w.N} W={w.window}")
+    x = workloads.make_inputs(w)
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(1016, 1032), np.arange(w.N - 8, w.N),
+                                     np.random.default_rng(7150).integers(0, w.N, 40)]))
+    fwd_case(fa, x, "bf16", w.window, rows=rows)
+
+
 def test_window_at_least_n_equals_causal(fa):
     x = workloads.random_inputs(1, 3, 333, 128, "bf16", seed=7200)
     q, k, v = (to_dev(x[n], "bf16") for n in "qkv")

@@ -12,7 +12,8 @@ float64 there).
 Shapes and value distributions follow the five workloads the method is judged
 on: a tiny fp32 unmasked head, a GPT-2-small-shaped causal layer, the long
 context causal head, a ragged-length fp16 case with sharp softmax rows, and the
-causal forward+backward case.  No public dataset is involved; the GPT-2-small
+causal forward+backward case.  A sixth, the long context head under a causal
+sliding window of 1024 keys, measures the window path.  No public dataset is involved; the GPT-2-small
 shape stands in for the GPT-2 training workload named on the pages (Road to
 Intelligence "FlashAttention", section "What it bought").
 """
@@ -39,6 +40,7 @@ class Workload:
     qk_std: float = 1.0      # Q and K ~ N(0, qk_std^2)
     v_dist: str = "normal"   # "normal" -> N(0,1), "uniform" -> U(-1, 1)
     backward: bool = False   # also draw dO ~ N(0, 1)
+    window: int | None = None  # causal sliding window: key j visible to query i iff i - W < j <= i
 
     @property
     def scale(self) -> float:
@@ -46,8 +48,12 @@ class Workload:
 
     def pairs(self) -> int:
         """Visible (query, key) pairs of one head."""
-        n = self.N
-        return n * (n + 1) // 2 if self.causal else n * n
+        n, w = self.N, self.window
+        if not self.causal:
+            return n * n
+        if w is None or w >= n:
+            return n * (n + 1) // 2
+        return w * (w + 1) // 2 + (n - w) * w  # rows 0..w-1 see i+1 keys, the rest w
 
     def fwd_flops(self) -> int:
         """Algorithmic forward FLOPs: QK^T and PV over visible pairs only."""
@@ -73,6 +79,8 @@ WORKLOADS = {
                                   qk_std=3.0, v_dist="uniform"),
     "fwd_bwd_causal_bf16": Workload("fwd_bwd_causal_bf16", "bf16", True, 4, 16, 4096, 128, seed=5,
                                     backward=True),
+    "long_window_bf16": Workload("long_window_bf16", "bf16", True, 1, 16, 8192, 128, seed=6,
+                                 window=1024),
 }
 
 
