@@ -367,8 +367,14 @@ struct FwdBlock {
     auto slot = [](int e, int st) { return slot_of<kMfmas>(e, st); };
     // K operand of block u+1: K tile (u+1)/2, half (u+1)&1
     const uint8_t* kt = k_stage(((u + 1) >> 1) & 3) + k_base + ((u + 1) & 1) * 32 * L::kKStride;
-    // V operand of block u (for the next block's PV MFMAs): V tile u/2, half u&1
-    const uint8_t* vt = v_stage((u >> 1) & 3) + v_base + (u & 1) * 32 * L::kVStride;
+    // V operand of block u (for the next block's PV MFMAs): V tile u/2, half u&1.
+    // The stage offset is hidden from the compiler (an empty asm on an SGPR)
+    // so that it is not folded into the reads' constant offsets: past 64 KB
+    // they no longer fit the 16-bit LDS offset field and every read would
+    // need an address add of its own.
+    uint32_t v_off = kStages * L::kKStage + ((u >> 1) & 3) * L::kVStage + (u & 1) * 32 * L::kVStride;
+    asm("" : "+s"(v_off));
+    const uint8_t* vt = smem + v_off + v_base;
     vec8 kfr[kKs];
     if (kFirst) {
 #pragma unroll
@@ -378,7 +384,7 @@ struct FwdBlock {
     if (kFirst) raise_reference(s_cur);  // the first block sets the reference outright
 
     u32x4 pw[2];
-    float sum[2] = {0.f, 0.f};
+    float sum[2];  // partial row sums of even and odd score pairs
     f32x16 s_next;
     float pr[16];  // scaled scores, then probabilities
 #pragma unroll
@@ -415,11 +421,16 @@ struct FwdBlock {
         }
         if (t == slot(e, 2)) {
           pw[e >> 2][e & 3] = E::pack2(pr[2 * e], pr[2 * e + 1]);
-          sum[e & 1] += pr[2 * e] + pr[2 * e + 1];
+          const float pair = pr[2 * e] + pr[2 * e + 1];
+          sum[e & 1] = e < 2 ? pair : sum[e & 1] + pair;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // Keep the packing inside the MFMA stream: the reference-update path below
+    // overwrites pw, and without this use the compiler sinks the conversions
+    // past its branch, right in front of the next block's first PV MFMA.
+    asm volatile("" ::"v"(pw[0]), "v"(pw[1]));
     float s_tot = sum[0] + sum[1];
     if (!kFirst && __builtin_amdgcn_ballot_w64(s_tot > kSumCap) != 0) {
       // rare: some probability of this block may exceed the cap (or a row
