@@ -4,5 +4,5 @@ TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the package smoke check and
 by the benchmark's ``cpu_baseline`` leg, never by the product path.  It shares no
 code with the HIP library.
 """
-from .attention import (dense_bwd, dense_fwd, dense_probs, online_fwd,  # noqa: F401
-                        transfer_ledger)
+from .attention import (dense_bwd, dense_fwd, dense_probs, loop_order_ledger,  # noqa: F401
+                        online_fwd, online_fwd_kv_outer, transfer_ledger)

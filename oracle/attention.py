@@ -15,6 +15,10 @@ Contents
                  from Q, K and the log-sum-exp.
 ``transfer_ledger``  the element-transfer count of the explorer's declared
                  dense and tiled schedules.
+``online_fwd_kv_outer``  the original key/value-outer loop order with the
+                 normalised in-place output update.
+``loop_order_ledger``  element transfers of the query-outer and the
+                 key/value-outer orders, causal skipping included.
 
 Conventions shared by all functions (readings of the pages where they are
 silent; each is also listed with the design notes):
@@ -191,6 +195,127 @@ def online_fwd(q, k, v, causal=False, scale=None, query_block=2, key_block=2, tr
             out[h, rows] = a / ell[:, None]
             lse[h, rows] = m + np.log(ell)
     return out.reshape(lead + (n_q, dv)), lse.reshape(lead + (n_q,))
+
+
+def online_fwd_kv_outer(q, k, v, causal=False, scale=None, query_block=2, key_block=2):
+    """Tiled forward in the original loop order: key/value tiles outside,
+    query blocks inside, with a normalised output updated in place.
+
+    "FlashAttention -- the same attention, made memory-aware", section 04
+    gives the loop nest (one K/V tile loaded, then every query tile visited
+    under it) and section 03 the merge of one tile into a query block's running
+    answer; "Flash Attention: IO-Aware Exact Attention", section "Loop order
+    changes which data is reloaded", names this the original algorithm, which
+    reloads Q and the row state for every K/V block.  For a query block with
+    state (O, m, l) and a tile of scores t and values V_tile:
+
+        m_t = max_j t_j,   P = exp(t - m_t),   l_t = sum_j P_j
+        m' = max(m, m_t)
+        l' = exp(m - m') l + exp(m_t - m') l_t
+        O' = (l exp(m - m') O + exp(m_t - m') P V_tile) / l'
+
+    State starts at O = 0, m = -inf, l = 0 (the exp of -inf is 0); rows whose
+    keys are all masked in a tile leave their state unchanged.  Returns (O, LSE)
+    with LSE = m + ln l, as ``dense_fwd``.
+    """
+    q = _as64(q)
+    k = _as64(k)
+    v = _as64(v)
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[-1])
+    lead = q.shape[:-2]
+    n_q, n_k = q.shape[-2], k.shape[-2]
+    dv = v.shape[-1]
+    qf = q.reshape((-1, n_q, q.shape[-1]))
+    kf = k.reshape((-1, n_k, k.shape[-1]))
+    vf = v.reshape((-1, n_k, dv))
+    out = np.zeros((qf.shape[0], n_q, dv))
+    m = np.full((qf.shape[0], n_q), -np.inf)
+    ell = np.zeros((qf.shape[0], n_q))
+    for h in range(qf.shape[0]):
+        for col0 in range(0, n_k, key_block):              # outer: key/value tiles
+            cols = np.arange(col0, min(n_k, col0 + key_block))
+            for row0 in range(0, n_q, query_block):        # inner: query tiles
+                rows = np.arange(row0, min(n_q, row0 + query_block))
+                t = (qf[h, rows] @ kf[h, cols].T) * scale
+                if causal:
+                    t = np.where(cols[None, :] <= rows[:, None], t, -np.inf)
+                m_t = t.max(axis=1)
+                hit = np.isfinite(m_t)                     # rows with a visible key here
+                if not hit.any():
+                    continue
+                r = rows[hit]
+                t, m_t = t[hit], m_t[hit]
+                p = np.exp(t - m_t[:, None])
+                l_t = p.sum(axis=1)
+                m_old, l_old = m[h, r], ell[h, r]
+                m_new = np.maximum(m_old, m_t)
+                keep = np.where(np.isfinite(m_old), np.exp(m_old - m_new), 0.0)
+                take = np.exp(m_t - m_new)
+                l_new = keep * l_old + take * l_t
+                out[h, r] = ((l_old * keep)[:, None] * out[h, r]
+                             + take[:, None] * (p @ vf[h, cols])) / l_new[:, None]
+                m[h, r], ell[h, r] = m_new, l_new
+    lse = m + np.log(ell)
+    return out.reshape(lead + (n_q, dv)), lse.reshape(lead + (n_q,))
+
+
+def loop_order_ledger(n, d, dv, query_block, key_block, order, causal=False):
+    """Element transfers between device memory and the chip for one head under
+    the two loop orders, counted by walking the loops ("Flash Attention:
+    IO-Aware Exact Attention", section "Loop order changes which data is
+    reloaded"; its counts assume the working set fits on chip and exclude
+    caches, as here).
+
+    ``order="q_outer"``: a query block is read once, its output block and
+    per-row statistic (one LSE value) written once; every K and V tile it can
+    see is read once per query block.
+    ``order="kv_outer"``: every K and V tile is read once; for every (tile,
+    query block) pair with a visible key the query block is read, the row
+    state (output block and two statistics per row, m and l) is read unless
+    this is the block's first visit, and the state is written back.
+
+    Causal skips the (query block, key tile) pairs in which no key is visible.
+    Returns a dict of element counts per transfer and their ``total``.
+    """
+    if order not in ("q_outer", "kv_outer"):
+        raise ValueError("order must be 'q_outer' or 'kv_outer'")
+    c = {"Q_read": 0, "K_read": 0, "V_read": 0, "O_read": 0, "O_write": 0,
+         "stat_read": 0, "stat_write": 0}
+    blocks = [(r0, min(n, r0 + query_block)) for r0 in range(0, n, query_block)]
+    tiles = [(c0, min(n, c0 + key_block)) for c0 in range(0, n, key_block)]
+
+    def visible(b, t):
+        return (not causal) or t[0] <= b[1] - 1   # first key <= last row
+
+    if order == "q_outer":
+        for b in blocks:
+            rows = b[1] - b[0]
+            c["Q_read"] += rows * d
+            for t in tiles:
+                if visible(b, t):
+                    c["K_read"] += (t[1] - t[0]) * d
+                    c["V_read"] += (t[1] - t[0]) * dv
+            c["O_write"] += rows * dv
+            c["stat_write"] += rows
+    else:
+        seen = set()
+        for t in tiles:
+            c["K_read"] += (t[1] - t[0]) * d
+            c["V_read"] += (t[1] - t[0]) * dv
+            for b in blocks:
+                if not visible(b, t):
+                    continue
+                rows = b[1] - b[0]
+                c["Q_read"] += rows * d
+                if b in seen:
+                    c["O_read"] += rows * dv
+                    c["stat_read"] += 2 * rows
+                seen.add(b)
+                c["O_write"] += rows * dv
+                c["stat_write"] += 2 * rows
+    c["total"] = sum(c.values())
+    return c
 
 
 def dense_bwd(q, k, v, do, causal=False, scale=None, window=None):

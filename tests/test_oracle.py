@@ -129,6 +129,134 @@ def test_transfer_ledger(golden_dir):
         assert led["dense_total"] - led["tiled_total"] == 4 * n * n
 
 
+# ---------------------------------------------------------------- key/value-outer order
+
+def test_kv_outer_two_block_worked_example(golden_dir):
+    """The two-block row of Road to Intelligence 'FlashAttention', 'The trick that
+    makes tiling possible', taken through the normalised update of
+    'FlashAttention -- the same attention, made memory-aware', section 03."""
+    g = _load(golden_dir, "two_block_row.json")
+    scores = [x for blk in g["blocks"] for x in blk]
+    q = np.array([[1.0]])
+    k = np.array(scores, dtype=np.float64)[:, None]
+    v = np.eye(len(scores))
+    o, lse = oracle.online_fwd_kv_outer(q, k, v, scale=1.0, query_block=1, key_block=2)
+    # final denominator and maximum as printed: LSE = m + ln l with m = 5
+    assert abs(math.exp(lse[0] - g["after_block_2"]["m"]) - g["after_block_2"]["l"]) <= g["printed_tolerance"]
+    np.testing.assert_allclose(o[0], scipy.special.softmax(scores), rtol=1e-14)
+    # after the first tile alone the state is the first block's softmax
+    o1, lse1 = oracle.online_fwd_kv_outer(q, k[:2], v[:2, :2], scale=1.0, query_block=1, key_block=2)
+    assert abs(math.exp(lse1[0] - g["after_block_1"]["m"]) - g["after_block_1"]["l"]) <= g["printed_tolerance"]
+
+
+def test_kv_outer_equals_dense(golden_dir):
+    """Both loop orders reach the dense result ('Loop order changes which data is
+    reloaded'): the explorer vectors and random heads, every block size."""
+    g = _load(golden_dir, "explorer_vectors.json")
+    q, k, v = (np.array(g[x], dtype=np.float64) for x in "qkv")
+    for causal in (False, True):
+        ref, ref_lse = oracle.dense_fwd(q, k, v, causal=causal)
+        for qb in range(1, 8):
+            for kb in range(1, 8):
+                o, lse = oracle.online_fwd_kv_outer(q, k, v, causal=causal, query_block=qb, key_block=kb)
+                np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+                np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+    q, k, v = _rand(2, 3, 45, 16, seed=81, std=2), _rand(2, 3, 45, 16, seed=82, std=2), _rand(2, 3, 45, 8, seed=83)
+    for causal in (False, True):
+        ref, ref_lse = oracle.dense_fwd(q, k, v, causal=causal, scale=0.3)
+        for qb, kb in [(1, 45), (45, 1), (7, 16), (64, 64), (16, 7)]:
+            o, lse = oracle.online_fwd_kv_outer(q, k, v, causal=causal, scale=0.3, query_block=qb,
+                                                key_block=kb)
+            np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_kv_outer_negative_scale_and_large_scores():
+    """The scale multiplies before the maximum; scores near 700 do not overflow."""
+    q, k, v = _rand(20, 8, seed=91, std=9), _rand(20, 8, seed=92, std=9), _rand(20, 8, seed=93)
+    for scale in (-0.7, 2.5):
+        ref, ref_lse = oracle.dense_fwd(q, k, v, causal=True, scale=scale)
+        o, lse = oracle.online_fwd_kv_outer(q, k, v, causal=True, scale=scale, query_block=3, key_block=4)
+        np.testing.assert_allclose(o, ref, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-12)
+
+
+def test_loop_order_ledger_explorer(golden_dir):
+    """'Loop order changes which data is reloaded': the query-outer order reads
+    12 Q, 36 K, 36 V and writes 12 output elements for the explorer; the
+    original order reads K and V once but reloads Q and the row state for every
+    K/V block."""
+    g = _load(golden_dir, "transfer_ledger.json")
+    n, d, dv, qb = g["N"], g["d"], g["d_v"], g["query_block"]
+    for kb in (1, 2, 3, 6):
+        led = oracle.loop_order_ledger(n, d, dv, qb, kb, "q_outer")
+        for key in ("Q_read", "K_read", "V_read", "O_write"):
+            assert led[key] == g[key]
+        assert led["O_read"] == led["stat_read"] == 0 and led["stat_write"] == n
+        kv = oracle.loop_order_ledger(n, d, dv, qb, kb, "kv_outer")
+        n_tiles = -(-n // kb)
+        assert kv["K_read"] == n * d and kv["V_read"] == n * dv        # once
+        assert kv["Q_read"] == n_tiles * n * d                         # once per K/V tile
+        assert kv["O_write"] == n_tiles * n * dv
+        assert kv["O_read"] == (n_tiles - 1) * n * dv                  # not before the first
+        assert kv["stat_write"] == 2 * n_tiles * n
+    # one query block and one K/V tile: both orders move the same data (up to
+    # the statistics)
+    a = oracle.loop_order_ledger(n, d, dv, n, n, "q_outer")
+    b = oracle.loop_order_ledger(n, d, dv, n, n, "kv_outer")
+    for key in ("Q_read", "K_read", "V_read", "O_write", "O_read"):
+        assert a[key] == b[key]
+
+
+def test_loop_order_ledger_causal_by_hand():
+    """N = 6, two-row query blocks, two-key tiles, causal: query block 0 sees
+    tile 0, block 1 tiles 0 and 1, block 2 tiles 0 to 2 (six visits, counted by
+    hand); d = d_v = 2."""
+    q = oracle.loop_order_ledger(6, 2, 2, 2, 2, "q_outer", causal=True)
+    assert (q["Q_read"], q["K_read"], q["V_read"], q["O_write"]) == (12, 24, 24, 12)
+    kv = oracle.loop_order_ledger(6, 2, 2, 2, 2, "kv_outer", causal=True)
+    assert (kv["Q_read"], kv["K_read"], kv["V_read"]) == (24, 12, 12)
+    assert (kv["O_read"], kv["O_write"], kv["stat_read"], kv["stat_write"]) == (12, 24, 12, 24)
+    with pytest.raises(ValueError):
+        oracle.loop_order_ledger(6, 2, 2, 2, 2, "diagonal")
+
+
+def _mutant_kv_outer(q, k, v, qb, kb, bug):
+    """A copy of the key/value-outer merge with one deliberate mistake."""
+    n, dv = q.shape[0], v.shape[1]
+    out, m, ell = np.zeros((n, dv)), np.full(n, -np.inf), np.zeros(n)
+    for c0 in range(0, n, kb):
+        cols = np.arange(c0, min(n, c0 + kb))
+        for r0 in range(0, n, qb):
+            r = np.arange(r0, min(n, r0 + qb))
+            t = q[r] @ k[cols].T
+            m_t = t.max(1)
+            p = np.exp(t - m_t[:, None])
+            l_t = p.sum(1)
+            m_new = np.maximum(m[r], m_t)
+            keep = np.where(np.isfinite(m[r]), np.exp(m[r] - m_new), 0.0)
+            take = np.exp(m_t - m_new)
+            l_new = keep * ell[r] + take * l_t if bug != "no_keep_on_l" else ell[r] + take * l_t
+            w_old = keep * ell[r] if bug != "no_l_old" else keep
+            w_new = take if bug != "no_take_on_pv" else np.ones_like(take)
+            out[r] = (w_old[:, None] * out[r] + w_new[:, None] * (p @ v[cols])) / l_new[:, None]
+            m[r], ell[r] = m_new, l_new
+    return out, m + np.log(ell)
+
+
+@pytest.mark.parametrize("bug", ["no_l_old", "no_keep_on_l", "no_take_on_pv"])
+def test_kv_outer_pins_catch_planted_mistakes(bug):
+    """The dense-equality pin above rejects each mistake of the merge."""
+    q, k, v = _rand(13, 4, seed=74, std=2), _rand(13, 4, seed=75, std=2), _rand(13, 4, seed=76)
+    ref, ref_lse = oracle.dense_fwd(q, k, v, scale=1.0)
+    good, good_lse = _mutant_kv_outer(q, k, v, 3, 4, bug=None)
+    np.testing.assert_allclose(good, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(good_lse, ref_lse, rtol=1e-12, atol=1e-12)
+    bad, bad_lse = _mutant_kv_outer(q, k, v, 3, 4, bug=bug)
+    assert not (np.allclose(bad, ref, rtol=1e-12, atol=1e-12)
+                and np.allclose(bad_lse, ref_lse, rtol=1e-12, atol=1e-12))
+
+
 # ---------------------------------------------------------------- closed forms
 
 @pytest.mark.parametrize("causal", [False, True])
