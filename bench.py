@@ -5,7 +5,7 @@ One step = one ``attn_fwd`` call over the long-context causal workload
 N(0, 1) inputs already resident in device memory.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd]
-                    [--no-window]
+                    [--no-window] [--no-kv-outer]
 
 The reported throughput counts algorithmic FLOPs only: 4 * d * (visible query-key
 pairs) * B * H, i.e. the two matrix products over the causal triangle.
@@ -14,7 +14,9 @@ The same line carries, under "attn_bwd", the backward pass timed the same way
 on its own workload (B=4, H=16, N=4096, d=128, bf16, causal), counted as
 10 * d * pairs * B * H algorithmic FLOPs (S and dP recomputed, dV, dQ, dK), and
 under "attn_fwd_window" the forward of the long-context head with a causal
-sliding window of 1024 keys (4 * d * windowed pairs * B * H FLOPs).
+sliding window of 1024 keys (4 * d * windowed pairs * B * H FLOPs), and under
+"attn_fwd_kv_outer" the bench workload run in the original key/value-outer loop
+order (the comparison of the two orders' memory traffic; same FLOP count).
 """
 from __future__ import annotations
 
@@ -177,6 +179,35 @@ def window_record(fa, workloads, torch, steps, warmup):
                          "algorithmic_flops_per_launch": flops}}
 
 
+def kv_outer_record(fa, workloads, torch, steps, warmup):
+    """The bench workload in the key/value-outer loop order (attn_fwd_kv_outer),
+    timed over a few calls: each is tens of milliseconds."""
+    w = workloads.WORKLOADS[WORKLOAD]
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(torch.bfloat16).contiguous() for n in "qkv")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.kv_outer_workspace_bytes(w.B, w.H, w.N, w.d, fa.BF16), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        fa.attn_fwd_kv_outer(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws,
+                             stream=torch.cuda.current_stream(dev))
+
+    ms, warm = time_graph(step, steps, warmup, torch)
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    flops = w.fwd_flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"metric": "attention fwd TFLOP/s, key/value-outer loop order (bf16, causal, T=8192, d=128)",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warm,
+            "ms_per_step": round(ms, 5),
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": "causal",
+                       "order": "kv_outer", "workgroups": w.B * w.H},
+            "kernel": "fwd_kv_outer_kernel<bf16, d=128, causal>",
+            "algorithmic_flops_per_launch": flops}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +222,12 @@ def main():
                     help="skip the sliding-window forward measurement")
     ap.add_argument("--window-steps", type=int, default=200)
     ap.add_argument("--window-warmup", type=int, default=1500)
+    ap.add_argument("--no-kv-outer", action="store_true",
+                    help="skip the key/value-outer loop-order measurement")
+    ap.add_argument("--kv-steps", type=int, default=3)
+    ap.add_argument("--kv-warmup", type=int, default=2)
+    ap.add_argument("--kv-only", action="store_true",
+                    help="run only the key/value-outer measurement (for profiling its kernel)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times), "
                          "the reference kernel for scaling HBM byte counters, and exit")
@@ -218,6 +255,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": n * 4, "launches": 3}), flush=True)
+        return
+    if args.kv_only:
+        print(json.dumps({"attn_fwd_kv_outer": kv_outer_record(fa, workloads, torch, args.kv_steps,
+                                                               args.kv_warmup)}), flush=True)
         return
     w = workloads.WORKLOADS[WORKLOAD]
     x = workloads.make_inputs(w)
@@ -269,6 +310,9 @@ def main():
     if not args.no_window:
         record["attn_fwd_window"] = window_record(fa, workloads, torch, args.window_steps,
                                                   args.window_warmup)
+    if not args.no_kv_outer:
+        record["attn_fwd_kv_outer"] = kv_outer_record(fa, workloads, torch, args.kv_steps,
+                                                      args.kv_warmup)
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(record), flush=True)

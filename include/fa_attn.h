@@ -163,6 +163,37 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
  * 0 if the sizes, d or dtype are invalid. */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
 
+/*
+ * attn_fwd_kv_outer -- the same forward pass in the original key/value-outer
+ * loop order, for comparing the two orders' memory traffic.
+ *
+ * "Flash Attention: IO-Aware Exact Attention", section "Loop order changes
+ * which data is reloaded": the original algorithm keeps one key/value block
+ * on chip and visits every query block under it, reloading Q and the row
+ * state and writing the updated state back for each key/value block.  The
+ * update is the normalised one of "FlashAttention -- the same attention, made
+ * memory-aware", sections 03 and 04.  One workgroup per (batch, head) walks
+ * the key/value tiles; its row state (O, running maximum, denominator) lives
+ * in fp32 in the workspace between tiles.  Results equal attn_fwd's up to
+ * rounding; attn_fwd is the fast path.
+ *
+ *   arguments     as for attn_fwd; dtype FA_F16 or FA_BF16
+ *                 (FA_ERR_UNSUPPORTED for FA_F32).
+ *   workspace     device memory of at least
+ *                 attn_fwd_kv_outer_workspace_bytes() bytes, 16-byte aligned,
+ *                 owned by the caller (FA_ERR_WORKSPACE if NULL or smaller).
+ *                 Overwritten; calls that share one workspace must be
+ *                 ordered on one stream.
+ */
+int attn_fwd_kv_outer(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t H, int64_t N, int64_t d,
+                      int mask, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace attn_fwd_kv_outer needs: (4 * d + 8) * B * H * N; 0 if
+ * the sizes, d or dtype are invalid or dtype is FA_F32. */
+size_t attn_fwd_kv_outer_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_str(int status);
 

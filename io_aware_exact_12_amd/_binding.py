@@ -47,6 +47,11 @@ def lib():
         L.attn_bwd_window.restype = ctypes.c_int
         L.attn_bwd_window.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, ctypes.c_float,
                                                  ctypes.c_int, vp, ctypes.c_size_t, vp]
+        L.attn_fwd_kv_outer.restype = ctypes.c_int
+        L.attn_fwd_kv_outer.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                         ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp]
+        L.attn_fwd_kv_outer_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_fwd_kv_outer_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.fa_status_str.restype = ctypes.c_char_p
@@ -94,6 +99,15 @@ def attn_bwd_window_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, window, s
 
 def bwd_workspace_bytes(B, H, N, d, dtype_code):
     return lib().attn_bwd_workspace_bytes(B, H, N, d, dtype_code)
+
+
+def attn_fwd_kv_outer_raw(q, k, v, o, lse, B, H, N, d, mask, scale, dtype, ws, ws_bytes, stream):
+    return lib().attn_fwd_kv_outer(q, k, v, o, lse, B, H, N, d, mask, scale, dtype, ws, ws_bytes,
+                                   stream)
+
+
+def kv_outer_workspace_bytes(B, H, N, d, dtype_code):
+    return lib().attn_fwd_kv_outer_workspace_bytes(B, H, N, d, dtype_code)
 
 
 def _torch_dtype_code(t):
@@ -147,6 +161,43 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=N
     if st != 0:
         raise FaError(st, "attn_fwd")
     return out, (lse if return_lse else None)
+
+
+def attn_fwd_kv_outer(q, k, v, causal: bool = False, scale: float | None = None, *, out=None,
+                      lse=None, workspace=None, stream=None):
+    """The forward in the original key/value-outer loop order (``attn_fwd_kv_outer``):
+    returns ``(o, lse)``.  Same arguments as ``attn_fwd`` (fp16/bf16 only);
+    ``workspace`` is a uint8 device tensor of at least
+    ``kv_outer_workspace_bytes`` bytes, allocated here when not given.
+    """
+    import torch
+    if q.shape != k.shape or q.shape != v.shape or q.dim() != 4:
+        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {q.shape}, {k.shape}, {v.shape}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, N, d = q.shape
+    code = _torch_dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    need = kv_outer_workspace_bytes(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = lib().attn_fwd_kv_outer(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr(), B, H, N, d, MASK_CAUSAL if causal else MASK_NONE,
+                                 float(scale), code, workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if st != 0:
+        raise FaError(st, "attn_fwd_kv_outer")
+    return out, lse
 
 
 def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, *,

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 // Largest query-block count times B*H that still indexes a 1-D grid, with the
 // smallest query block any kernel uses (64 rows).
 constexpr int64_t kMaxGrid = (int64_t)INT32_MAX;
@@ -78,6 +78,27 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int kv_outer_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                  int64_t H, int64_t N, int64_t d, int mask, float scale, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_NULL;
+  const int st = check_common(B, H, N, d, mask, scale, dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < fa::kv_outer_workspace_bytes(B, H, N, d))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace) ||
+      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, mask == FA_MASK_CAUSAL, scale, N};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_kv_outer_bf16(a, workspace, s)
+                                        : fa::launch_fwd_kv_outer_f16(a, workspace, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,6 +135,18 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
   if (window < 1) return FA_ERR_WINDOW;
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, FA_MASK_CAUSAL, window, scale, dtype,
                   workspace, workspace_bytes, stream);
+}
+
+size_t attn_fwd_kv_outer_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK || dtype == FA_F32) return 0;
+  return fa::kv_outer_workspace_bytes(B, H, N, d);
+}
+
+int attn_fwd_kv_outer(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                      int64_t H, int64_t N, int64_t d, int mask, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return kv_outer_impl(q, k, v, o, lse, B, H, N, d, mask, scale, dtype, workspace, workspace_bytes,
+                       stream);
 }
 
 const char* fa_status_str(int status) {

@@ -27,11 +27,12 @@ def fwd(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=16, d=64, mask=0, 
 def test_library_exports_every_declared_symbol():
     declared = fa.declared_symbols()
     assert {"attn_fwd", "attn_bwd", "attn_fwd_window", "attn_bwd_window", "attn_bwd_workspace_bytes",
-            "fa_status_str", "fa_abi_version"} <= set(declared)
+            "attn_fwd_kv_outer", "attn_fwd_kv_outer_workspace_bytes", "fa_status_str",
+            "fa_abi_version"} <= set(declared)
     lib = ctypes.CDLL(fa._binding.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
-    assert fa.lib().fa_abi_version() == 2
+    assert fa.lib().fa_abi_version() == 3
 
 
 def test_status_strings():
@@ -164,3 +165,37 @@ def test_window_checks_like_the_plain_calls():
     assert fwd_w(4, q=P[0] + 8) == FA_ERR_ALIGN
     assert bwd_w(4, dtype=fa.F32) == FA_ERR_UNSUPPORTED
     assert bwd_w(4, ws_bytes=8) == FA_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------- key/value-outer order
+
+def kvo(ws=P[5], ws_bytes=1 << 30, **kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=16, d=64, mask=0, scale=0.125,
+             dtype=fa.BF16)
+    a.update(kw)
+    return fa.attn_fwd_kv_outer_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                                    a["d"], a["mask"], a["scale"], a["dtype"], ws, ws_bytes, None)
+
+
+def test_kv_outer_workspace_query():
+    # fp32 (4 d bytes) output state plus fp32 maximum and denominator per row
+    assert fa.kv_outer_workspace_bytes(1, 16, 8192, 128, fa.BF16) == (4 * 128 + 8) * 16 * 8192
+    assert fa.kv_outer_workspace_bytes(2, 3, 5, 64, fa.F16) == (4 * 64 + 8) * 30
+    assert fa.kv_outer_workspace_bytes(1, 1, 16, 64, fa.F32) == 0
+    assert fa.kv_outer_workspace_bytes(1, 1, 16, 96, fa.BF16) == 0
+    assert fa.kv_outer_workspace_bytes(0, 1, 16, 64, fa.BF16) == 0
+
+
+def test_kv_outer_validation():
+    assert kvo(q=None) == FA_ERR_NULL
+    assert kvo(o=None) == FA_ERR_NULL
+    assert kvo(N=0) == FA_ERR_SHAPE
+    assert kvo(d=96) == FA_ERR_UNSUPPORTED
+    assert kvo(dtype=fa.F32) == FA_ERR_UNSUPPORTED
+    assert kvo(dtype=9) == FA_ERR_DTYPE
+    assert kvo(mask=3) == FA_ERR_MASK
+    assert kvo(scale=math.nan) == FA_ERR_SCALE
+    assert kvo(ws=None) == FA_ERR_WORKSPACE
+    assert kvo(ws_bytes=(4 * 64 + 8) * 16 - 1) == FA_ERR_WORKSPACE
+    assert kvo(ws=P[5] + 4) == FA_ERR_ALIGN
+    assert kvo(v=P[2] + 2) == FA_ERR_ALIGN
