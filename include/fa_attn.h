@@ -17,8 +17,9 @@
  *
  * Layout.  Every tensor argument is a dense, contiguous [B][H][N][d] array of
  * the element type ``dtype`` (d innermost; d_v = d), 16-byte aligned, resident
- * in device memory of the current HIP device.  ``lse`` is a dense [B][H][N]
- * float array.
+ * in device memory of the current HIP device, except in the *_strided calls,
+ * which take element strides for the batch, head and row axes.  ``lse`` is
+ * always a dense [B][H][N] float array.
  *
  * Ownership.  All pointers belong to the caller; the library never allocates,
  * frees or retains them, and holds no mutable global state.  ``o`` must not
@@ -52,7 +53,7 @@ enum fa_mask { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1 };
 enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL                         */
-  FA_ERR_SHAPE = 2,       /* B, H or N < 1, or an element count overflows       */
+  FA_ERR_SHAPE = 2,       /* B, H or N < 1, an element count overflows, or one head spans >= 2 GiB */
   FA_ERR_DTYPE = 3,       /* dtype is not one of enum fa_dtype                  */
   FA_ERR_MASK = 4,        /* mask is not one of enum fa_mask                    */
   FA_ERR_SCALE = 5,       /* scale is NaN or infinite                           */
@@ -60,7 +61,8 @@ enum fa_status {
   FA_ERR_WORKSPACE = 7,   /* backward workspace missing or too small            */
   FA_ERR_HIP = 8,         /* the HIP runtime rejected a launch                  */
   FA_ERR_ALIGN = 9,       /* a tensor pointer is not 16-byte aligned            */
-  FA_ERR_WINDOW = 10      /* sliding window < 1                                 */
+  FA_ERR_WINDOW = 10,     /* sliding window < 1                                 */
+  FA_ERR_STRIDE = 11      /* a stride is unusable (see attn_fwd_strided)        */
 };
 
 /*
@@ -162,6 +164,47 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
 /* Bytes of workspace attn_bwd needs for these sizes (8 * B * H * N today);
  * 0 if the sizes, d or dtype are invalid. */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
+
+/*
+ * attn_fwd_strided -- attn_fwd on strided views.
+ *
+ * q, k and v, and o, are [B][H][N][d] views whose d elements are contiguous,
+ * with element strides {batch, head, row} given by q_strides (q), kv_strides
+ * (k and v) and o_strides (o): host arrays of three int64_t, read during the
+ * call.  A dense [B][H][N][d] tensor has {H*N*d, N*d, d}; a [B][N][H][d] one
+ * {N*H*d, d, H*d}; q, k and v sliced out of one packed [B][N][3][H][d] tensor
+ * share {N*3*H*d, d, 3*H*d}.  A head stride of 0 in kv_strides shares one k
+ * and one v head among all query heads (multi-query attention).  The pages'
+ * interface takes (B, nh, T, hs) tensors ("FlashAttention -- the same
+ * attention, made memory-aware", section 00); these strides describe such
+ * tensors, transposed or packed, without a copy.
+ *
+ *   strides    every stride >= 0 and a multiple of 16 bytes; the row stride
+ *              >= d; one head's rows span < 2 GiB.  Output rows must not
+ *              overlap (ordered by stride, each dimension of extent > 1 steps
+ *              past what the smaller ones cover).  FA_ERR_STRIDE otherwise,
+ *              FA_ERR_NULL if an array is NULL.
+ *   lse        dense [B][H][N] fp32, may be NULL.
+ *   other arguments and errors as for attn_fwd.
+ */
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t d,
+                     const int64_t* q_strides, const int64_t* kv_strides, const int64_t* o_strides,
+                     int mask, float scale, int dtype, void* stream);
+
+/*
+ * attn_bwd_strided -- attn_bwd on strided views: q, k, v, o and dout share
+ * in_strides, dq, dk and dv share grad_strides (strides as for
+ * attn_fwd_strided; the gradient layout must not overlap, so k and v cannot
+ * be broadcast here).  lse is the dense [B][H][N] array of the forward; the
+ * workspace is as for attn_bwd.
+ */
+int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int64_t B, int64_t H, int64_t N, int64_t d,
+                     const int64_t* in_strides, const int64_t* grad_strides,
+                     int mask, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /*
  * attn_fwd_kv_outer -- the same forward pass in the original key/value-outer

@@ -47,6 +47,13 @@ def lib():
         L.attn_bwd_window.restype = ctypes.c_int
         L.attn_bwd_window.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, ctypes.c_float,
                                                  ctypes.c_int, vp, ctypes.c_size_t, vp]
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.attn_fwd_strided.restype = ctypes.c_int
+        L.attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64p, i64p, i64p,
+                                       ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+        L.attn_bwd_strided.restype = ctypes.c_int
+        L.attn_bwd_strided.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64p, i64p, ctypes.c_int,
+                                                  ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp]
         L.attn_fwd_kv_outer.restype = ctypes.c_int
         L.attn_fwd_kv_outer.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                          ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp]
@@ -101,6 +108,29 @@ def bwd_workspace_bytes(B, H, N, d, dtype_code):
     return lib().attn_bwd_workspace_bytes(B, H, N, d, dtype_code)
 
 
+def _strides(st):
+    """A host int64[3] array for the ABI (None stays None)."""
+    return None if st is None else (ctypes.c_int64 * 3)(*[int(x) for x in st])
+
+
+def attn_fwd_strided_raw(q, k, v, o, lse, B, H, N, d, q_st, kv_st, o_st, mask, scale, dtype, stream):
+    return lib().attn_fwd_strided(q, k, v, o, lse, B, H, N, d, _strides(q_st), _strides(kv_st),
+                                  _strides(o_st), mask, scale, dtype, stream)
+
+
+def attn_bwd_strided_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, in_st, grad_st, mask, scale,
+                         dtype, ws, ws_bytes, stream):
+    return lib().attn_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, _strides(in_st),
+                                  _strides(grad_st), mask, scale, dtype, ws, ws_bytes, stream)
+
+
+def _layout(t):
+    """{batch, head, row} element strides of a [B, H, N, d] tensor whose last
+    axis is contiguous; axes of extent 1 get stride 0 (their stride is never
+    used)."""
+    return tuple(0 if t.shape[i] == 1 else t.stride(i) for i in range(3))
+
+
 def attn_fwd_kv_outer_raw(q, k, v, o, lse, B, H, N, d, mask, scale, dtype, ws, ws_bytes, stream):
     return lib().attn_fwd_kv_outer(q, k, v, o, lse, B, H, N, d, mask, scale, dtype, ws, ws_bytes,
                                    stream)
@@ -134,8 +164,8 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=N
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
     for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous device tensors")
+        if not t.is_cuda or t.stride(-1) != 1:
+            raise ValueError("q, k, v must be device tensors with a contiguous last axis")
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -145,6 +175,21 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=N
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    if not all(t.is_contiguous() for t in (q, k, v, out)):
+        # strided views (transposed, packed, or k and v broadcast over heads)
+        if window is not None:
+            raise ValueError("a sliding window takes contiguous q, k, v")
+        if _layout(k) != _layout(v):
+            raise ValueError("k and v must share one layout")
+        if out.shape != q.shape or out.stride(-1) != 1:
+            raise ValueError("out must be [B, H, N, d] with a contiguous last axis")
+        st = attn_fwd_strided_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr() if return_lse else None, B, H, N, d, _layout(q),
+                                  _layout(k), _layout(out), MASK_CAUSAL if causal else MASK_NONE,
+                                  float(scale), _torch_dtype_code(q), stream.cuda_stream)
+        if st != 0:
+            raise FaError(st, "attn_fwd_strided")
+        return out, (lse if return_lse else None)
     if window is not None:
         if not causal:
             raise ValueError("a sliding window needs causal=True")
@@ -214,9 +259,11 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     for t in (k, v, o, dout):
         if t.shape != shape or t.dtype != q.dtype:
             raise ValueError("q, k, v, o, dout must share one shape and dtype")
-    for t in (q, k, v, o, dout, lse):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("inputs must be contiguous device tensors")
+    for t in (q, k, v, o, dout):
+        if not t.is_cuda or t.stride(-1) != 1:
+            raise ValueError("inputs must be device tensors with a contiguous last axis")
+    if not lse.is_cuda or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous device tensor")
     if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape[:3]):
         raise ValueError("lse must be float32 [B, H, N]")
     B, H, N, d = shape
@@ -232,6 +279,24 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
+    if not all(t.is_contiguous() for t in (q, k, v, o, dout, dq, dk, dv)):
+        # strided views: q, k, v, o, dout share one layout, dq, dk, dv another
+        if window is not None:
+            raise ValueError("a sliding window takes contiguous tensors")
+        lay = _layout(q)
+        if any(_layout(t) != lay for t in (k, v, o, dout)):
+            raise ValueError("q, k, v, o and dout must share one layout")
+        glay = _layout(dq)
+        if any(_layout(t) != glay or t.stride(-1) != 1 for t in (dq, dk, dv)):
+            raise ValueError("dq, dk and dv must share one layout with a contiguous last axis")
+        st = attn_bwd_strided_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), B, H, N, d, lay, glay,
+                                  MASK_CAUSAL if causal else MASK_NONE, float(scale), code,
+                                  workspace.data_ptr(), ws_bytes, stream.cuda_stream)
+        if st != 0:
+            raise FaError(st, "attn_bwd_strided")
+        return dq, dk, dv
     if window is not None:
         if not causal:
             raise ValueError("a sliding window needs causal=True")

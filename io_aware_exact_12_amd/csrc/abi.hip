@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 // Largest query-block count times B*H that still indexes a 1-D grid, with the
 // smallest query block any kernel uses (64 rows).
 constexpr int64_t kMaxGrid = (int64_t)INT32_MAX;
@@ -27,22 +27,69 @@ int check_common(int64_t B, int64_t H, int64_t N, int64_t d, int mask, float sca
   if (bh > INT64_MAX / N || bh * N > INT64_MAX / 128 / 4) return FA_ERR_SHAPE;
   if (((N + 63) / 64) * bh > kMaxGrid) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // one head of a dense [N][d] array must span less than 2 GiB (one buffer resource)
+  if (N * d * (dtype == FA_F32 ? 4 : 2) > INT32_MAX - 1024) return FA_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
   return FA_OK;
 }
 
+size_t elt_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+// A strided view ([B][H][N][d], d contiguous, strides {batch, head, row} in
+// elements) is usable when every stride is >= 0 and a multiple of 16 bytes,
+// rows are at least d elements apart, and one head's rows span less than
+// 2 GiB (the kernels address a head through one buffer resource).  Outputs
+// must in addition not overlap: ordered by stride, each dimension of extent
+// > 1 must step past everything the smaller ones cover.
+int check_layout(const int64_t* st, int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
+                 bool output, fa::Layout* out) {
+  if (st == nullptr) return FA_ERR_NULL;
+  const int64_t align = 16 / (int64_t)elt_bytes(dtype);
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0 || st[i] % align != 0 || st[i] > INT64_MAX / 4 / (i == 0 ? B : i == 1 ? H : N))
+      return FA_ERR_STRIDE;
+  if (st[2] < d) return FA_ERR_STRIDE;
+  if ((N - 1) * st[2] > (INT32_MAX - 1024) / (int64_t)elt_bytes(dtype) - d) return FA_ERR_SHAPE;
+  if (output) {
+    int64_t cnt[3] = {B, H, N}, str[3] = {st[0], st[1], st[2]};
+    for (int i = 0; i < 3; ++i)  // order by stride
+      for (int j = i + 1; j < 3; ++j)
+        if (str[j] < str[i]) {
+          const int64_t a = str[i], c = cnt[i];
+          str[i] = str[j], cnt[i] = cnt[j], str[j] = a, cnt[j] = c;
+        }
+    int64_t ext = d;
+    for (int i = 0; i < 3; ++i) {
+      if (cnt[i] == 1) continue;
+      if (str[i] < ext) return FA_ERR_STRIDE;
+      ext += (cnt[i] - 1) * str[i];
+    }
+  }
+  *out = fa::Layout{st[0], st[1], st[2]};
+  return FA_OK;
+}
+
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-             int64_t N, int64_t d, int mask, int64_t window, float scale, int dtype, void* stream) {
+             int64_t N, int64_t d, int mask, int64_t window, float scale, int dtype, void* stream,
+             const int64_t* q_st = nullptr, const int64_t* kv_st = nullptr,
+             const int64_t* out_st = nullptr) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_NULL;
   const int st = check_common(B, H, N, d, mask, scale, dtype);
   if (st != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, mask == FA_MASK_CAUSAL, scale, window < N ? window : N,
+                fa::dense_layout(H, N, d), fa::dense_layout(H, N, d), fa::dense_layout(H, N, d)};
+  if (q_st != nullptr || kv_st != nullptr || out_st != nullptr) {
+    int e1 = check_layout(q_st, B, H, N, d, dtype, false, &a.lq);
+    if (e1 == FA_OK) e1 = check_layout(kv_st, B, H, N, d, dtype, false, &a.in);
+    if (e1 == FA_OK) e1 = check_layout(out_st, B, H, N, d, dtype, true, &a.out);
+    if (e1 != FA_OK) return e1;
+  }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
     return FA_ERR_ALIGN;
 
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, mask == FA_MASK_CAUSAL, scale, window < N ? window : N};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (dtype) {
@@ -56,7 +103,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
              int64_t d, int mask, int64_t window, float scale, int dtype, void* workspace,
-             size_t workspace_bytes, void* stream) {
+             size_t workspace_bytes, void* stream, const int64_t* in_st = nullptr,
+             const int64_t* out_st = nullptr) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr ||
@@ -67,12 +115,19 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < fa::bwd_workspace_bytes(B, H, N))
     return FA_ERR_WORKSPACE;
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask == FA_MASK_CAUSAL, scale,
+                workspace, window < N ? window : N, fa::dense_layout(H, N, d),
+                fa::dense_layout(H, N, d)};
+  if (in_st != nullptr || out_st != nullptr) {
+    int e1 = check_layout(in_st, B, H, N, d, dtype, false, &a.in);
+    if (e1 != FA_OK) return e1;
+    e1 = check_layout(out_st, B, H, N, d, dtype, true, &a.out);
+    if (e1 != FA_OK) return e1;
+  }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
     return FA_ERR_ALIGN;
-  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask == FA_MASK_CAUSAL, scale,
-                workspace, window < N ? window : N};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f16(a, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -92,7 +147,8 @@ int kv_outer_impl(const void* q, const void* k, const void* v, void* o, float* l
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace) ||
       (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
     return FA_ERR_ALIGN;
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, mask == FA_MASK_CAUSAL, scale, N};
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, mask == FA_MASK_CAUSAL, scale, N,
+                fa::dense_layout(H, N, d), fa::dense_layout(H, N, d), fa::dense_layout(H, N, d)};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_kv_outer_bf16(a, workspace, s)
                                         : fa::launch_fwd_kv_outer_f16(a, workspace, s);
@@ -137,6 +193,24 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
                   workspace, workspace_bytes, stream);
 }
 
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                     int64_t H, int64_t N, int64_t d, const int64_t* q_strides,
+                     const int64_t* kv_strides, const int64_t* o_strides, int mask, float scale,
+                     int dtype, void* stream) {
+  if (q_strides == nullptr || kv_strides == nullptr || o_strides == nullptr) return FA_ERR_NULL;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, mask, N, scale, dtype, stream, q_strides, kv_strides,
+                  o_strides);
+}
+
+int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                     int64_t d, const int64_t* in_strides, const int64_t* grad_strides, int mask,
+                     float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (in_strides == nullptr || grad_strides == nullptr) return FA_ERR_NULL;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, N, scale, dtype, workspace,
+                  workspace_bytes, stream, in_strides, grad_strides);
+}
+
 size_t attn_fwd_kv_outer_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
   if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK || dtype == FA_F32) return 0;
   return fa::kv_outer_workspace_bytes(B, H, N, d);
@@ -162,6 +236,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_HIP: return "the HIP runtime rejected a launch";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_WINDOW: return "sliding window must be >= 1";
+    case FA_ERR_STRIDE: return "a stride is negative, not a multiple of 16 bytes, below d (rows), or makes output rows overlap";
     default: return "unknown status";
   }
 }

@@ -73,14 +73,16 @@ template <int D> struct STile {
   }
   // byte offset in the tile of 16-byte chunk c of LDS row r
   static __device__ __forceinline__ int at(int r, int c) { return r * kRowBytes + 16 * (c ^ swz(r)); }
-  // Tile-relative source offsets of this wave's copies: copy i of wave w fills
-  // LDS bytes [(w + kW i) KB, +1 KB), lane l the 16 bytes at 16 l.
-  static __device__ __forceinline__ void sources(int wave, int lane, uint32_t (&src)[kPerWave]) {
+  // Tile-relative source offsets of this wave's copies (rows row_bytes apart
+  // in device memory): copy i of wave w fills LDS bytes [(w + kW i) KB, +1 KB),
+  // lane l the 16 bytes at 16 l.
+  static __device__ __forceinline__ void sources(int wave, int lane, uint32_t row_bytes,
+                                                 uint32_t (&src)[kPerWave]) {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int byte = (wave + kW * i) * 1024 + 16 * lane;
       const int r = byte / kRowBytes, phys = (byte % kRowBytes) / 16;
-      src[i] = (uint32_t)(tile_row(r) * kRowBytes + 16 * (phys ^ swz(r)));
+      src[i] = (uint32_t)tile_row(r) * row_bytes + (uint32_t)(16 * (phys ^ swz(r)));
     }
   }
 };
@@ -100,14 +102,18 @@ __device__ __forceinline__ void dma4(const i32x4& rsrc, uint32_t lds_addr, uint3
       : "memory");
 }
 
-// Copy rows [row0, row0 + 64) of a [rows][D] tensor (zeros past `rows`) into
-// the swizzled tile at LDS address lds_addr: this wave's share.
+// Copy rows [row0, row0 + 64) of a [rows][D] view with row stride sn
+// elements (zeros past `rows`) into the swizzled tile at LDS address
+// lds_addr: this wave's share.  The buffer ends after the last row's data, so
+// rows past `rows` (at least sn >= D elements further on) read as zero.
 template <int D>
 __device__ __forceinline__ void copy_tile(uint32_t lds_addr, const uint16_t* base, int rows, int row0,
-                                          int wave, const uint32_t (&src)[STile<D>::kPerWave]) {
+                                          int64_t sn, int wave,
+                                          const uint32_t (&src)[STile<D>::kPerWave]) {
   using T = STile<D>;
   const int left = rows - row0;
-  const i32x4 rs = make_rsrc(base + (int64_t)row0 * D, left > 0 ? (uint32_t)left * T::kRowBytes : 0u);
+  const i32x4 rs = make_rsrc(base + (int64_t)row0 * sn,
+                             left > 0 ? (uint32_t)(left - 1) * (uint32_t)(2 * sn) + (uint32_t)T::kRowBytes : 0u);
 #pragma unroll
   for (int i = 0; i < T::kPerWave; ++i) dma16(rs, lds_addr + (uint32_t)((wave + kW * i) * 1024), src[i]);
 }
@@ -142,31 +148,34 @@ __device__ __forceinline__ typename Elt<IsBf16>::vec8 row_frag(const uint8_t* ti
   return *reinterpret_cast<const typename Elt<IsBf16>::vec8*>(tile + STile<D>::at(r, 2 * kk + g));
 }
 
-// Resident operand of one lane: row `row` of a [rows][D] tensor as the MFMA
-// B operand (d = 16 ks + 8 g + 0..7), zero past `rows`, optionally sign-flipped.
+// Resident operand of one lane: row `row` of a [rows][D] view with row stride
+// sn elements as the MFMA B operand (d = 16 ks + 8 g + 0..7), zero past
+// `rows`, optionally sign-flipped.
 template <bool IsBf16, int D>
 __device__ __forceinline__ void load_resident(typename Elt<IsBf16>::vec8 (&f)[D / 16],
-                                              const uint16_t* base, int rows, int row, int g,
-                                              uint32_t sign) {
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)((uint32_t)rows * 2 * D), kRsrcFlags);
+                                              const uint16_t* base, int rows, int row, int64_t sn,
+                                              int g, uint32_t sign) {
+  const uint32_t row_bytes = (uint32_t)(2 * sn);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)base, 0, (int)((uint32_t)(rows - 1) * row_bytes + 2 * D), kRsrcFlags);
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     u32x4 raw = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, row * 2 * D + (2 * ks + g) * 16, 0, 0));
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)((uint32_t)row * row_bytes) + (2 * ks + g) * 16, 0, 0));
     raw ^= sign;
     f[ks] = __builtin_bit_cast(typename Elt<IsBf16>::vec8, raw);
   }
 }
 
 // Store one lane's column of a transposed accumulator (rows = d) as row `row`
-// of a [rows][D] tensor, multiplied by `mul` and rounded to the element type.
+// of a view with row stride sn elements, multiplied by `mul` and rounded to
+// the element type.
 template <bool IsBf16, int D>
-__device__ __forceinline__ void store_row(uint16_t* base, int row, int g, const f32x16 (&acc)[D / 32],
-                                          float mul) {
+__device__ __forceinline__ void store_row(uint16_t* base, int row, int64_t sn, int g,
+                                          const f32x16 (&acc)[D / 32], float mul) {
   using E = Elt<IsBf16>;
   typedef __attribute__((ext_vector_type(4))) typename E::scalar h4_t;
-  uint16_t* orow = base + (int64_t)row * D;
+  uint16_t* orow = base + (int64_t)row * sn;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -339,8 +348,8 @@ template <bool IsBf16, int D, bool Causal, bool Window>
 __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NLse, const float* __restrict__ Dsum,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int win, int BH, float c,
-    float dk_mul, uint32_t k_sign) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int win, int H, int BH, float c,
+    float dk_mul, uint32_t k_sign, Layout in, Layout out) {
   using T = STile<D>;
   using Ld = DkdvLds<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes];
@@ -348,14 +357,15 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int bh = blockIdx.x % BH, kblk = blockIdx.x / BH;  // heaviest (earliest keys) first
-  const int64_t head = (int64_t)bh * N * D;
+  const int b = bh / H, h = bh - b * H;
+  const int64_t head = b * in.sb + h * in.sh, head_out = b * out.sb + h * out.sh;
   const int k0 = kblk * kRes, kw0 = k0 + 32 * wave;
 
   constexpr bool kWin = Causal && Window;
   DkdvBlock<IsBf16, D, Causal, Window> blk;
   blk.init(lane, N, win, kw0, c);
-  load_resident<IsBf16, D>(blk.kf, K + head, N, blk.my_k, blk.g, k_sign);
-  load_resident<IsBf16, D>(blk.vf, V + head, N, blk.my_k, blk.g, 0u);
+  load_resident<IsBf16, D>(blk.kf, K + head, N, blk.my_k, in.sn, blk.g, k_sign);
+  load_resident<IsBf16, D>(blk.vf, V + head, N, blk.my_k, in.sn, blk.g, 0u);
 
   // query tiles that can see these keys: from the diagonal to the end of the
   // last key's sliding window
@@ -368,15 +378,15 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
   const float* nl_h = NLse + (int64_t)bh * N;
   const float* d_h = Dsum + (int64_t)bh * N;
   uint32_t src[T::kPerWave];
-  T::sources(wave, lane, src);
+  T::sources(wave, lane, (uint32_t)(2 * in.sn), src);
   const uint32_t lds0 = lds_u32(smem);
 
   // the copies of query tile it into stage st (-LSE2 by wave 0, D by wave 1)
   auto issue = [&](int it, int st) {
     const int qt0 = it * kT;
     const uint32_t base = lds0 + (uint32_t)(st * Ld::kStage);
-    copy_tile<D>(base + Ld::kQ, q_h, N, qt0, wave, src);
-    copy_tile<D>(base + Ld::kDO, do_h, N, qt0, wave, src);
+    copy_tile<D>(base + Ld::kQ, q_h, N, qt0, in.sn, wave, src);
+    copy_tile<D>(base + Ld::kDO, do_h, N, qt0, in.sn, wave, src);
     const int left = N - qt0;
     if (wave < 2) {
       const i32x4 rs = make_rsrc(wave == 0 ? nl_h + qt0 : d_h + qt0, left > 0 ? (uint32_t)left * 4u : 0u);
@@ -417,7 +427,7 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
     __syncthreads();
   }
   const bool store = kw0 < N && blk.my_k < N;
-  if (store) store_row<IsBf16, D>(dV + head, blk.my_k, blk.g, blk.acc, 1.f);
+  if (store) store_row<IsBf16, D>(dV + head_out, blk.my_k, out.sn, blk.g, blk.acc, 1.f);
   // ---- pass K; tile t_first is already in stage n_it & 1
   blk.zero();
   for (int i = 0; i < n_it; ++i) {
@@ -437,7 +447,7 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
     wait_copies();
     __syncthreads();
   }
-  if (store) store_row<IsBf16, D>(dK + head, blk.my_k, blk.g, blk.acc, dk_mul);
+  if (store) store_row<IsBf16, D>(dK + head_out, blk.my_k, out.sn, blk.g, blk.acc, dk_mul);
 }
 
 // ---------------------------------------------------------------- D and dQ
@@ -458,8 +468,8 @@ template <bool IsBf16, int D, bool Causal, bool Window>
 __global__ __launch_bounds__(kThr, 2) void bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dsum,
-    float* __restrict__ NLse, uint16_t* __restrict__ dQ, int N, int win, int BH, int n_qblocks,
-    float c, float dq_mul, uint32_t q_sign) {
+    float* __restrict__ NLse, uint16_t* __restrict__ dQ, int N, int win, int H, int BH, int n_qblocks,
+    float c, float dq_mul, uint32_t q_sign, Layout in, Layout out) {
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using T = STile<D>;
@@ -472,12 +482,13 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
   const int bh = blockIdx.x % BH;
   int qb = blockIdx.x / BH;
   if (Causal) qb = n_qblocks - 1 - qb;  // heaviest first
-  const int64_t head = (int64_t)bh * N * D;
+  const int b = bh / H, h = bh - b * H;
+  const int64_t head = b * in.sb + h * in.sh;
   const int q0 = qb * kRes, qw0 = q0 + 32 * wave, my_q = qw0 + l32;
 
   vec8 qf[kKs], of[kKs];
-  load_resident<IsBf16, D>(qf, Q + head, N, my_q, g, q_sign);
-  load_resident<IsBf16, D>(of, dO + head, N, my_q, g, 0u);
+  load_resident<IsBf16, D>(qf, Q + head, N, my_q, in.sn, g, q_sign);
+  load_resident<IsBf16, D>(of, dO + head, N, my_q, in.sn, g, 0u);
   const bool q_ok = my_q < N;
   const float lse2 = q_ok ? LSE[(int64_t)bh * N + my_q] * 1.4426950408889634f : INFINITY;
 
@@ -491,13 +502,13 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
   const uint16_t* k_h = K + head;
   const uint16_t* v_h = V + head;
   uint32_t src[T::kPerWave];
-  T::sources(wave, lane, src);
+  T::sources(wave, lane, (uint32_t)(2 * in.sn), src);
   const uint32_t lds0 = lds_u32(smem);
 
   auto issue = [&](int it, int st) {
     const uint32_t base = lds0 + (uint32_t)(st * Ld::kStage);
-    copy_tile<D>(base + Ld::kK, k_h, N, it * kT, wave, src);
-    copy_tile<D>(base + Ld::kV, v_h, N, it * kT, wave, src);
+    copy_tile<D>(base + Ld::kK, k_h, N, it * kT, in.sn, wave, src);
+    copy_tile<D>(base + Ld::kV, v_h, N, it * kT, in.sn, wave, src);
   };
 
   // S^T and dP^T of key half kh of the tile in stage st, and P^T with the
@@ -583,7 +594,7 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
     __syncthreads();
   }
   if (!wave_live || !q_ok) return;
-  store_row<IsBf16, D>(dQ + head, my_q, g, dq, dq_mul);
+  store_row<IsBf16, D>(dQ + (b * out.sb + h * out.sh), my_q, out.sn, g, dq, dq_mul);
 }
 
 template <bool IsBf16, int D, bool Causal, bool Window>
@@ -604,14 +615,14 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
   float* nlse = dsum + a.B * a.H * a.N;
   // dQ (and D into the workspace) first; dK, dV read D afterwards on the same stream
   hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal, Window>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st, q,
-                     k, v, dout, a.lse, dsum, nlse, static_cast<uint16_t*>(a.dq), N, win, BH, nblk,
-                     c, a.scale, q_sign);
+                     k, v, dout, a.lse, dsum, nlse, static_cast<uint16_t*>(a.dq), N, win, (int)a.H, BH,
+                     nblk, c, a.scale, q_sign, a.in, a.out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dK = scale dS^T Q; a negative scale flips the resident K instead of Q
   hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal, Window>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
                      q, k, v, dout, nlse, dsum, static_cast<uint16_t*>(a.dk),
-                     static_cast<uint16_t*>(a.dv), N, win, BH, c, a.scale, q_sign);
+                     static_cast<uint16_t*>(a.dv), N, win, (int)a.H, BH, c, a.scale, q_sign, a.in, a.out);
   return hipGetLastError();
 }
 

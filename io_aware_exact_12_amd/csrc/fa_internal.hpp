@@ -6,8 +6,18 @@
 
 namespace fa {
 
+// Element strides of a [B][H][N][d] view whose d axis is contiguous: batch,
+// head and row.  A dense [B][H][N][d] array has {H*N*d, N*d, d}; a
+// [B][N][H][d] one {N*H*d, d, H*d}.
+struct Layout {
+  int64_t sb, sh, sn;
+};
+
+inline Layout dense_layout(int64_t H, int64_t N, int64_t d) { return Layout{H * N * d, N * d, d}; }
+
 // Arguments of one forward launch after validation.  Pointers are device
-// pointers to dense [B][H][N][d] arrays (lse: [B][H][N], may be null).
+// pointers to [B][H][N][d] views with layouts `lq` (q), `in` (k and v) and
+// `out` (o); lse is a dense [B][H][N] array (may be null).
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -20,6 +30,7 @@ struct FwdArgs {
   // causal only: key j is visible to query i iff i - window < j <= i
   // (window >= N is plain causal)
   int64_t window;
+  Layout lq, in, out;
 };
 
 // Arguments of one backward launch after validation.  workspace holds at
@@ -39,6 +50,8 @@ struct BwdArgs {
   float scale;
   void* workspace;
   int64_t window;  // as for FwdArgs
+  Layout in;       // q, k, v, o, dout
+  Layout out;      // dq, dk, dv
 };
 
 // Launchers return the hipError_t of the launch (hipSuccess when enqueued).

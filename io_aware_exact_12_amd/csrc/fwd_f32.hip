@@ -30,7 +30,8 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
                                                          const float* __restrict__ V,
                                                          float* __restrict__ O,
                                                          float* __restrict__ LSE, int N,
-                                                         int win, int n_qblocks, float scale) {
+                                                         int win, int H, int n_qblocks, float scale,
+                                                         Layout lq, Layout in, Layout out) {
   constexpr int kQStride = D + 1;  // odd stride: lanes reading their own row hit distinct banks
   __shared__ float qs[kRows * kQStride];
   __shared__ __attribute__((aligned(16))) float ks[kKeys * D];
@@ -39,14 +40,16 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   const int lane = threadIdx.x;
   const int bh = blockIdx.x / n_qblocks;
   const int q0 = (blockIdx.x % n_qblocks) * kRows;
-  const int64_t head_off = (int64_t)bh * N * D;
-  const float* Qh = Q + head_off;
+  const int b = bh / H, h = bh - b * H;
+  const int64_t head_off = b * in.sb + h * in.sh;
+  const int64_t sn = in.sn;
+  const float* Qh = Q + (b * lq.sb + h * lq.sh);
   const float* Kh = K + head_off;
   const float* Vh = V + head_off;
 
   for (int idx = lane; idx < kRows * D; idx += kRows) {
     const int r = idx / D, col = idx % D;
-    qs[r * kQStride + col] = (q0 + r < N) ? Qh[(int64_t)(q0 + r) * D + col] : 0.f;
+    qs[r * kQStride + col] = (q0 + r < N) ? Qh[(int64_t)(q0 + r) * lq.sn + col] : 0.f;
   }
 
   const int my_q = q0 + lane;
@@ -66,9 +69,9 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
     for (int idx = lane; idx < kKeys * D / 4; idx += kRows) {
       const int r = (idx * 4) / D, col = (idx * 4) % D;
       const bool ok = key0 + r < N;
-      const float4 kv = ok ? *reinterpret_cast<const float4*>(Kh + (int64_t)(key0 + r) * D + col)
+      const float4 kv = ok ? *reinterpret_cast<const float4*>(Kh + (int64_t)(key0 + r) * sn + col)
                            : float4{0.f, 0.f, 0.f, 0.f};
-      const float4 vv = ok ? *reinterpret_cast<const float4*>(Vh + (int64_t)(key0 + r) * D + col)
+      const float4 vv = ok ? *reinterpret_cast<const float4*>(Vh + (int64_t)(key0 + r) * sn + col)
                            : float4{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<float4*>(ks + r * D + col) = kv;
       *reinterpret_cast<float4*>(vs + r * D + col) = vv;
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   }
 
   if (my_q < N) {
-    float* orow = O + head_off + (int64_t)my_q * D;
+    float* orow = O + (b * out.sb + h * out.sh) + (int64_t)my_q * out.sn;
 #pragma unroll
     for (int col = 0; col < D; ++col) orow[col] = (float)((double)acc[col] / l_run);
     if (LSE != nullptr) LSE[(int64_t)bh * N + my_q] = (float)(m_run + log(l_run));
@@ -128,7 +131,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_f32_kernel<D, Causal>), grid, dim3(kRows), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, N,
-                     (int)(a.window < a.N ? a.window : a.N), n_qblocks, a.scale);
+                     (int)(a.window < a.N ? a.window : a.N), (int)a.H, n_qblocks, a.scale, a.lq, a.in, a.out);
   return hipGetLastError();
 }
 

@@ -122,7 +122,10 @@ struct FwdBlock {
   uint8_t* smem;  // K stages 0..kStages-1, then V stages, then the sink slot
   const uint8_t* k_ptr;  // K and V of this head (wave-uniform)
   const uint8_t* v_ptr;
-  uint32_t head_bytes;
+  uint32_t head_bytes;   // extent of one head's rows in q, k, v: (N - 1) rows + one row of data
+  uint32_t row_bytes;    // distance of consecutive rows of q, k, v
+  int64_t o_off;         // this head's first output element, and the output row stride
+  int64_t o_sn;
   int N, win, wave, lane, l32, g, q0, my_q, n_tiles, n_sub;
   int u_lo;   // first 32-key block this wave computes (sliding window)
   float c;
@@ -153,12 +156,13 @@ struct FwdBlock {
     const int byte = ci * 1024 + lane * 16;
     const int row = byte / stride, col = byte % stride;
     if (col >= kRowBytes) return kNoData;  // row padding
-    return (uint32_t)((is_v ? row : k_row_key(row)) * kRowBytes + col);
+    return (uint32_t)(is_v ? row : k_row_key(row)) * row_bytes + (uint32_t)col;
   }
 
   __device__ __forceinline__ void init(uint8_t* lds, const uint16_t* Q, const uint16_t* K,
-                                       const uint16_t* V, int N_, int win_, int bh, int qb, float c_,
-                                       uint32_t q_sign) {
+                                       const uint16_t* V, int N_, int win_, int H, int bh, int qb,
+                                       float c_, uint32_t q_sign, const Layout& lq, const Layout& in,
+                                       const Layout& out) {
     smem = lds;
     N = N_;
     win = win_;
@@ -168,8 +172,12 @@ struct FwdBlock {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
     l32 = lane & 31;
     g = lane >> 5;
-    const int64_t head_off = (int64_t)bh * N * D;
-    head_bytes = (uint32_t)N * kRowBytes;
+    const int b = bh / H, h = bh - b * H;
+    const int64_t head_off = b * in.sb + h * in.sh;
+    row_bytes = (uint32_t)(2 * in.sn);
+    head_bytes = (uint32_t)(N - 1) * row_bytes + (uint32_t)kRowBytes;
+    o_off = b * out.sb + h * out.sh;
+    o_sn = out.sn;
     k_ptr = reinterpret_cast<const uint8_t*>(K + head_off);
     v_ptr = reinterpret_cast<const uint8_t*>(V + head_off);
 
@@ -187,12 +195,14 @@ struct FwdBlock {
     u_lo = kWin ? max(0, q0 - win + 1) / 32 : 0;
 
     // Q^T fragments; rows past N read as zeros through the buffer bounds
-    const __amdgpu_buffer_rsrc_t q_rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Q + head_off), 0, (int)head_bytes, kRsrcFlags);
+    const uint32_t q_row_bytes = (uint32_t)(2 * lq.sn);
+    const __amdgpu_buffer_rsrc_t q_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Q + (b * lq.sb + h * lq.sh)), 0, (int)((uint32_t)(N - 1) * q_row_bytes + kRowBytes),
+        kRsrcFlags);
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
       u32x4 raw = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(q_rs, my_q * kRowBytes + (2 * ks + g) * 16, 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(q_rs, (int)((uint32_t)my_q * q_row_bytes) + (2 * ks + g) * 16, 0, 0));
       raw ^= q_sign;  // negative scale: flip the sign of q, exactly
       qf[ks] = __builtin_bit_cast(vec8, raw);
     }
@@ -250,11 +260,11 @@ struct FwdBlock {
   // exactly kCopies copies, in one asm statement that saves and restores M0
   // once.
   __device__ __forceinline__ void load_tiles(int jk, int sk, int jv, int sv) const {
-    constexpr uint32_t kTileBytes = kBN * kRowBytes;
-    const uint32_t k_left = jk < n_tiles ? head_bytes - (uint32_t)jk * kTileBytes : 0u;
-    const uint32_t v_left = jv < n_tiles ? head_bytes - (uint32_t)jv * kTileBytes : 0u;
-    const i32x4 tk = make_rsrc(k_ptr + (size_t)jk * kTileBytes, k_left);
-    const i32x4 tv = make_rsrc(v_ptr + (size_t)jv * kTileBytes, v_left);
+    const uint32_t tile_bytes = kBN * row_bytes;
+    const uint32_t k_left = jk < n_tiles ? head_bytes - (uint32_t)jk * tile_bytes : 0u;
+    const uint32_t v_left = jv < n_tiles ? head_bytes - (uint32_t)jv * tile_bytes : 0u;
+    const i32x4 tk = make_rsrc(k_ptr + (size_t)jk * tile_bytes, k_left);
+    const i32x4 tv = make_rsrc(v_ptr + (size_t)jv * tile_bytes, v_left);
     // wave-uniform by construction; readfirstlane keeps the selection in SGPRs
     i32x4 tx;
 #pragma unroll
@@ -523,7 +533,7 @@ struct FwdBlock {
     const float l_tot = xhalf_sum(l_part);
     const float inv = 1.0f / l_tot;
     if (my_q >= N) return;
-    uint16_t* orow = O + (int64_t)bh * N * D + (int64_t)my_q * D;
+    uint16_t* orow = O + o_off + (int64_t)my_q * o_sn;
     typedef __attribute__((ext_vector_type(4))) typename E::scalar h4_t;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
@@ -543,15 +553,15 @@ struct FwdBlock {
 template <bool IsBf16, int D, bool Causal, bool Window>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int win, int BH, int n_qblocks, float c,
-    uint32_t q_sign) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int win, int H, int BH, int n_qblocks,
+    float c, uint32_t q_sign, Layout lq, Layout in, Layout out) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds<D>::kBytes];
   // work item: (query block, batch*head); heaviest causal blocks first
   const int bh = blockIdx.x % BH;
   int qb = blockIdx.x / BH;
   if (Causal) qb = n_qblocks - 1 - qb;
   FwdBlock<IsBf16, D, Causal, Window> blk;
-  blk.init(smem, Q, K, V, N, win, bh, qb, c, q_sign);
+  blk.init(smem, Q, K, V, N, win, H, bh, qb, c, q_sign, lq, in, out);
   blk.run(qb * kBM);
   blk.store(O, LSE, bh);
 }
@@ -570,7 +580,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_kernel<IsBf16, D, Causal, Window>), grid, dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, N,
-                     (int)(a.window < a.N ? a.window : a.N), BH, n_qblocks, c, q_sign);
+                     (int)(a.window < a.N ? a.window : a.N), (int)a.H, BH, n_qblocks, c, q_sign, a.lq,
+                     a.in, a.out);
   return hipGetLastError();
 }
 

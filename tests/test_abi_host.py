@@ -13,7 +13,8 @@ import pytest
 import io_aware_exact_12_amd as fa
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_DTYPE, FA_ERR_MASK, FA_ERR_SCALE, \
-    FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_ALIGN, FA_ERR_WINDOW = range(11)
+    FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_ALIGN, FA_ERR_WINDOW, \
+    FA_ERR_STRIDE = range(12)
 
 # fake, never-dereferenced addresses: validation fails before any use
 P = [0x10000 * (i + 1) for i in range(8)]
@@ -27,17 +28,17 @@ def fwd(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=16, d=64, mask=0, 
 def test_library_exports_every_declared_symbol():
     declared = fa.declared_symbols()
     assert {"attn_fwd", "attn_bwd", "attn_fwd_window", "attn_bwd_window", "attn_bwd_workspace_bytes",
-            "attn_fwd_kv_outer", "attn_fwd_kv_outer_workspace_bytes", "fa_status_str",
-            "fa_abi_version"} <= set(declared)
+            "attn_fwd_kv_outer", "attn_fwd_kv_outer_workspace_bytes", "attn_fwd_strided",
+            "attn_bwd_strided", "fa_status_str", "fa_abi_version"} <= set(declared)
     lib = ctypes.CDLL(fa._binding.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
-    assert fa.lib().fa_abi_version() == 3
+    assert fa.lib().fa_abi_version() == 4
 
 
 def test_status_strings():
-    for st in range(11):
-        assert fa.status_str(st)
+    for st in range(12):
+        assert fa.status_str(st) and fa.status_str(st) != "unknown status"
     assert fa.status_str(123) == "unknown status"
 
 
@@ -91,7 +92,8 @@ def test_binding_refuses_cpu_tensors():
 def test_header_documents_each_status():
     text = open(fa._binding.HEADER).read()
     for name in ["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_DTYPE", "FA_ERR_MASK",
-                 "FA_ERR_SCALE", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_ALIGN"]:
+                 "FA_ERR_SCALE", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_ALIGN",
+                 "FA_ERR_WORKSPACE", "FA_ERR_WINDOW", "FA_ERR_STRIDE"]:
         assert name in text
 
 
@@ -199,3 +201,81 @@ def test_kv_outer_validation():
     assert kvo(ws_bytes=(4 * 64 + 8) * 16 - 1) == FA_ERR_WORKSPACE
     assert kvo(ws=P[5] + 4) == FA_ERR_ALIGN
     assert kvo(v=P[2] + 2) == FA_ERR_ALIGN
+
+
+# ---------------------------------------------------------------- strided views
+
+DENSE = (1 * 16 * 64, 16 * 64, 64)   # B=1, H=1, N=16, d=64 as [B][H][N][d]
+
+
+def fwd_s(q_st=DENSE, kv_st=DENSE, o_st=DENSE, **kw):
+    a = dict(B=1, H=1, N=16, d=64, mask=0, scale=0.125, dtype=fa.BF16)
+    a.update(kw)
+    return fa.attn_fwd_strided_raw(P[0], P[1], P[2], P[3], P[4], a["B"], a["H"], a["N"], a["d"],
+                                   q_st, kv_st, o_st, a["mask"], a["scale"], a["dtype"], None)
+
+
+def bwd_s(in_st=DENSE, g_st=DENSE, **kw):
+    a = dict(B=1, H=1, N=16, d=64, mask=0, scale=0.125, dtype=fa.BF16)
+    a.update(kw)
+    return fa.attn_bwd_strided_raw(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], a["B"],
+                                   a["H"], a["N"], a["d"], in_st, g_st, a["mask"], a["scale"],
+                                   a["dtype"], P[1], 1 << 20, None)
+
+
+def test_strided_null_arrays():
+    assert fwd_s(q_st=None) == FA_ERR_NULL
+    assert fwd_s(kv_st=None) == FA_ERR_NULL
+    assert fwd_s(o_st=None) == FA_ERR_NULL
+    assert bwd_s(in_st=None) == FA_ERR_NULL
+    assert bwd_s(g_st=None) == FA_ERR_NULL
+
+
+@pytest.mark.parametrize("st", [(-64, 1024, 64), (1024, 1024, 60), (1024, 1028, 64), (1024, 1024, 32),
+                                (8, 1024, 64 + 4)])
+def test_strided_rejects_unusable_input_strides(st):
+    """Negative, not a multiple of 16 bytes (8 bf16 elements), or rows closer than d."""
+    assert fwd_s(q_st=st) == FA_ERR_STRIDE
+    assert fwd_s(kv_st=st) == FA_ERR_STRIDE
+    assert bwd_s(in_st=st) == FA_ERR_STRIDE
+
+
+def test_strided_fp32_alignment_is_four_elements():
+    st = fa.attn_fwd_strided_raw(P[0] + 4, P[1], P[2], P[3], P[4], 1, 1, 16, 64, (0, 0, 68), DENSE,
+                                 DENSE, 0, 0.125, fa.F32, None)
+    assert st == FA_ERR_ALIGN                       # 68 floats = 272 bytes: the strides pass
+    assert fwd_s(q_st=(0, 0, 66), dtype=fa.F32) == FA_ERR_STRIDE   # 264 bytes: not 16-aligned
+
+
+def test_strided_broadcast_inputs_are_allowed_outputs_are_not():
+    """k and v may share one head across all query heads (head stride 0); an
+    output may not: its heads would overlap."""
+    H, N, d = 4, 16, 64
+    dense = (H * N * d, N * d, d)
+    mqa = (N * d, 0, d)
+    # a launch is not wanted here: check that the stride check passes by
+    # making the next check (pointer alignment) fail instead
+    st = fa.attn_fwd_strided_raw(P[0] + 2, P[1], P[2], P[3], P[4], 1, H, N, d, dense, mqa, dense, 0,
+                                 0.125, fa.BF16, None)
+    assert st == FA_ERR_ALIGN
+    assert fa.attn_fwd_strided_raw(P[0], P[1], P[2], P[3], P[4], 1, H, N, d, dense, dense, mqa, 0,
+                                   0.125, fa.BF16, None) == FA_ERR_STRIDE
+    assert bwd_s(g_st=(N * d, 0, d), H=H) == FA_ERR_STRIDE
+
+
+@pytest.mark.parametrize("o_st,ok", [((16 * 4 * 64, 64, 4 * 64), True),     # [B][N][H][d]
+                                     ((16 * 4 * 64, 16 * 64, 64), True),    # dense
+                                     ((16 * 4 * 64, 32, 4 * 64), False),    # heads overlap within a row
+                                     ((16 * 4 * 64, 64, 2 * 64), False),    # rows overlap heads
+                                     ((0, 16 * 64, 64), False)])            # batches overlap (B = 2)
+def test_strided_output_overlap_check(o_st, ok):
+    st = fa.attn_fwd_strided_raw(P[0] + 2, P[1], P[2], P[3], P[4], 2, 4, 16, 64,
+                                 (16 * 4 * 64, 16 * 64, 64), (16 * 4 * 64, 16 * 64, 64), o_st, 0,
+                                 0.125, fa.BF16, None)
+    assert st == (FA_ERR_ALIGN if ok else FA_ERR_STRIDE)
+
+
+def test_head_extent_limit():
+    """One head's rows must span less than 2 GiB (one buffer resource)."""
+    assert fwd(N=(1 << 24), d=64) == FA_ERR_SHAPE          # 2 GiB of bf16 rows
+    assert fwd_s(q_st=(0, 0, 1 << 20), N=2048) == FA_ERR_SHAPE  # rows 2 MiB apart
