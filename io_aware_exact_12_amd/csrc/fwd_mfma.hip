@@ -369,7 +369,10 @@ struct FwdBlock {
   // block: the zeros in s_cur, seen against kNoRef, send it down the
   // reference-update path, which forms its scores from LDS, while
   // p_prev = vfr = 0 make its PV MFMAs add 0.
-  template <int kMask, bool kFirst = false>
+  //
+  // kHalf (0 or 1) is the block's place in its tile step; it sets the wave's
+  // issue priority (see step()).
+  template <int kMask, bool kFirst = false, int kHalf = 0>
   __device__ __forceinline__ void block(int u) {
     static_assert(kPV == kKs, "as many PV as score MFMAs per block (d = 64 or 128)");
     constexpr int kMfmas = (kFirst ? 0 : kPV) + kKs;
@@ -435,6 +438,8 @@ struct FwdBlock {
           sum[e & 1] = e < 2 ? pair : sum[e & 1] + pair;
         }
       }
+      // half way through the block the wave's priority steps down
+      if (t == kMfmas / 2 - 1) __builtin_amdgcn_s_setprio(kHalf == 0 ? 2 : 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     // Keep the packing inside the MFMA stream: the reference-update path below
@@ -458,6 +463,7 @@ struct FwdBlock {
     p_prev[0] = pw[0];
     p_prev[1] = pw[1];
     s_cur = s_next;
+    if (kHalf == 0) __builtin_amdgcn_s_setprio(1);
   }
 
   // PV MFMAs of the wave's last block.
@@ -475,22 +481,29 @@ struct FwdBlock {
   //
   // In the workgroup's first step (kFirstStep) a wave whose first block u_lo
   // lies in the step runs it as kFirst; u_lo is never below 2j there.
+  //
+  // Issue priority.  The two waves of a SIMD run the same code, and with equal
+  // priorities the older one always issues first: it reaches the barrier well
+  // ahead and idles while the other finishes the step alone, without a second
+  // wave to overlap its MFMAs and VALU work.  So a wave's priority falls as it
+  // gets through the step (3 at the start, 2, 1, 0 at each half block): the
+  // wave that is behind issues first and the pair stays level.
   template <int kMask, bool kFirstStep = false>
   __device__ __forceinline__ void step(int j) {
+    __builtin_amdgcn_s_setprio(3);
     load_tiles(j + 3, (j + 3) & 3, j + 2, (j + 2) & 3);
     if (kFirstStep) {
-      if (u_lo == 2 * j && u_lo < n_sub) block<kMask, true>(2 * j);
+      if (u_lo == 2 * j && u_lo < n_sub) block<kMask, true, 0>(2 * j);
       if (u_lo == 2 * j + 1 && u_lo < n_sub)
-        block<kMask, true>(2 * j + 1);
+        block<kMask, true, 1>(2 * j + 1);
       else if (u_lo == 2 * j && 2 * j + 1 < n_sub)
-        block<kMask>(2 * j + 1);
+        block<kMask, false, 1>(2 * j + 1);
     } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int u = 2 * j + h;
-        if (u >= u_lo && u < n_sub) block<kMask>(u);
-      }
+      const int u = 2 * j;
+      if (u >= u_lo && u < n_sub) block<kMask, false, 0>(u);
+      if (u + 1 >= u_lo && u + 1 < n_sub) block<kMask, false, 1>(u + 1);
     }
+    __builtin_amdgcn_s_setprio(0);
     wait_older_copies();
     __syncthreads();
   }
