@@ -37,6 +37,15 @@ silent; each is also listed with the design notes):
   "Storage, arithmetic and IO are separate quantities", on skipped blocks
   changing which pairs are computed); the window's definition is a reading,
   not a page fact.
+* Block-sparse mask (``block_mask``, blocks of ``block`` = 64 queries by 64
+  keys): key j is visible to query i iff block_mask[..., i // 64, j // 64] is
+  nonzero, and-ed with the causal mask when that is on.  The pages name
+  masks that skip whole blocks only as a change of which pairs are computed
+  ("Flash Attention: IO-Aware Exact Attention", section "Storage, arithmetic
+  and IO are separate quantities"); the block size and the layout
+  [..., ceil(N / 64), ceil(N / 64)] (leading axes broadcast over batch and
+  head) are a reading.  A row that sees no key at all has O = 0 and
+  LSE = -inf (an empty sum), also a reading.
 * The saved per-row statistic is the natural-log log-sum-exp of the scaled,
   masked scores: LSE_i = m_i + ln(l_i).
 """
@@ -57,9 +66,12 @@ def _check_window(causal, window):
             raise ValueError("window must be >= 1")
 
 
-def _scores(q, k, scale, causal, rows=None, window=None):
+BLOCK = 64  # block-sparse mask granularity (queries and keys)
+
+
+def _scores(q, k, scale, causal, rows=None, window=None, block_mask=None):
     """Scaled scores S[..., i, j] = scale * q_i . k_j with the causal (and
-    sliding-window) mask applied.
+    sliding-window, or block-sparse) mask applied.
 
     ``rows`` optionally restricts the queries to the given indices (the
     definition is per row, so a subset of rows is the same computation).
@@ -69,18 +81,27 @@ def _scores(q, k, scale, causal, rows=None, window=None):
     k = _as64(k)
     qi = q if rows is None else q[..., rows, :]
     s = (qi @ np.swapaxes(k, -1, -2)) * float(scale)
+    n_k = k.shape[-2]
+    r = np.arange(q.shape[-2]) if rows is None else np.asarray(rows)
+    j = np.arange(n_k)
     if causal:
-        n_k = k.shape[-2]
-        r = np.arange(q.shape[-2]) if rows is None else np.asarray(rows)
-        j = np.arange(n_k)[None, :]
-        visible = j <= r[:, None]
+        visible = j[None, :] <= r[:, None]
         if window is not None:
-            visible &= j > r[:, None] - int(window)
+            visible = visible & (j[None, :] > r[:, None] - int(window))
+        s = np.where(visible, s, -np.inf)
+    if block_mask is not None:
+        bm = np.asarray(block_mask) != 0
+        n_qb, n_kb = -(-q.shape[-2] // BLOCK), -(-n_k // BLOCK)
+        if bm.shape[-2:] != (n_qb, n_kb):
+            raise ValueError(f"block_mask must end in ({n_qb}, {n_kb}), got {bm.shape}")
+        # visible[..., i, j] = bm[..., i // 64, j // 64]
+        rows_of = np.take(bm, r // BLOCK, axis=-2)
+        visible = np.take(rows_of, j // BLOCK, axis=-1)
         s = np.where(visible, s, -np.inf)
     return s
 
 
-def dense_fwd(q, k, v, causal=False, scale=None, rows=None, window=None):
+def dense_fwd(q, k, v, causal=False, scale=None, rows=None, window=None, block_mask=None):
     """Materialised attention O = softmax(scale * Q K^T) V and its row LSE.
 
     Follows the dense three-step path ("Flash Attention: IO-Aware Exact
@@ -95,24 +116,29 @@ def dense_fwd(q, k, v, causal=False, scale=None, rows=None, window=None):
     q = _as64(q)
     if scale is None:
         scale = 1.0 / np.sqrt(q.shape[-1])
-    s = _scores(q, k, scale, causal, rows, window)
+    s = _scores(q, k, scale, causal, rows, window, block_mask)
     m = s.max(axis=-1, keepdims=True)
-    e = np.exp(s - m)
+    seen = np.isfinite(m)                      # rows with at least one visible key
+    e = np.exp(s - np.where(seen, m, 0.0))     # hidden keys: exp(-inf) = 0
     ell = e.sum(axis=-1, keepdims=True)
-    p = e / ell
+    p = np.where(seen, e / np.where(seen, ell, 1.0), 0.0)
     o = p @ _as64(v)
-    lse = m[..., 0] + np.log(ell[..., 0])
+    with np.errstate(divide="ignore"):
+        lse = np.where(seen[..., 0], m[..., 0] + np.log(ell[..., 0]), -np.inf)
     return o, lse
 
 
-def dense_probs(q, k, causal=False, scale=None, window=None):
-    """The normalised probability matrix P of the dense path (for row-sum checks)."""
+def dense_probs(q, k, causal=False, scale=None, window=None, block_mask=None):
+    """The normalised probability matrix P of the dense path (for row-sum checks);
+    rows with no visible key are all zero."""
     q = _as64(q)
     if scale is None:
         scale = 1.0 / np.sqrt(q.shape[-1])
-    s = _scores(q, k, scale, causal, window=window)
-    e = np.exp(s - s.max(axis=-1, keepdims=True))
-    return e / e.sum(axis=-1, keepdims=True)
+    s = _scores(q, k, scale, causal, window=window, block_mask=block_mask)
+    m = s.max(axis=-1, keepdims=True)
+    seen = np.isfinite(m)
+    e = np.exp(s - np.where(seen, m, 0.0))
+    return np.where(seen, e / np.where(seen, e.sum(axis=-1, keepdims=True), 1.0), 0.0)
 
 
 def online_fwd(q, k, v, causal=False, scale=None, query_block=2, key_block=2, trace=None,
@@ -318,7 +344,7 @@ def loop_order_ledger(n, d, dv, query_block, key_block, order, causal=False):
     return c
 
 
-def dense_bwd(q, k, v, do, causal=False, scale=None, window=None):
+def dense_bwd(q, k, v, do, causal=False, scale=None, window=None, block_mask=None):
     """Gradients of L = sum(O * dO) for O = softmax(scale * Q K^T) V.
 
     The pages state only that the backward pass recomputes the score and
@@ -345,9 +371,10 @@ def dense_bwd(q, k, v, do, causal=False, scale=None, window=None):
     do = _as64(do)
     if scale is None:
         scale = 1.0 / np.sqrt(q.shape[-1])
-    o, lse = dense_fwd(q, k, v, causal, scale, window=window)
-    s = _scores(q, k, scale, causal, window=window)
-    p = np.exp(s - lse[..., None])
+    o, lse = dense_fwd(q, k, v, causal, scale, window=window, block_mask=block_mask)
+    s = _scores(q, k, scale, causal, window=window, block_mask=block_mask)
+    seen = np.isfinite(lse)[..., None]         # a row with no visible key has P = 0
+    p = np.where(seen, np.exp(s - np.where(seen, lse[..., None], 0.0)), 0.0)
     kt = np.swapaxes
     dv = kt(p, -1, -2) @ do
     dp = do @ kt(v, -1, -2)

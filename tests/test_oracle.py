@@ -129,6 +129,109 @@ def test_transfer_ledger(golden_dir):
         assert led["dense_total"] - led["tiled_total"] == 4 * n * n
 
 
+# ---------------------------------------------------------------- block-sparse masks
+
+def _bm(n_qb, n_kb, seed, density=0.4, lead=()):
+    return (np.random.default_rng(seed).random(lead + (n_qb, n_kb)) < density).astype(np.uint8)
+
+
+def test_block_mask_all_ones_is_the_plain_mask():
+    q, k, v = _rand(2, 150, 16, seed=101), _rand(2, 150, 16, seed=102), _rand(2, 150, 16, seed=103)
+    ones = np.ones((3, 3), np.uint8)
+    for causal in (False, True):
+        ref = oracle.dense_fwd(q, k, v, causal=causal)
+        got = oracle.dense_fwd(q, k, v, causal=causal, block_mask=ones)
+        np.testing.assert_array_equal(got[0], ref[0])
+        np.testing.assert_array_equal(got[1], ref[1])
+
+
+def test_block_mask_one_block_is_attention_on_that_block():
+    """Query block I seeing only key block J is plain attention of q_I on
+    (k_J, v_J); the mask is deliberately not symmetric."""
+    n = 200
+    q, k, v = _rand(n, 8, seed=111, std=2), _rand(n, 8, seed=112, std=2), _rand(n, 8, seed=113)
+    bm = np.zeros((4, 4), np.uint8)
+    pairs = [(0, 3), (1, 0), (2, 2), (3, 1)]
+    for i, j in pairs:
+        bm[i, j] = 1
+    o, lse = oracle.dense_fwd(q, k, v, block_mask=bm)
+    for i, j in pairs:
+        r = slice(64 * i, min(n, 64 * i + 64))
+        c = slice(64 * j, min(n, 64 * j + 64))
+        s = (q[r] @ k[c].T) / math.sqrt(8)
+        np.testing.assert_allclose(o[r], scipy.special.softmax(s, axis=1) @ v[c], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[r], scipy.special.logsumexp(s, axis=1), rtol=1e-14)
+
+
+def test_block_mask_block_diagonal_splits_the_sequence():
+    """A block-diagonal mask is attention on each 64-row chunk separately
+    (causal inside each chunk as well)."""
+    n = 230
+    q, k, v = _rand(2, n, 16, seed=121), _rand(2, n, 16, seed=122), _rand(2, n, 16, seed=123)
+    bm = np.eye(4, dtype=np.uint8)
+    for causal in (False, True):
+        o, lse = oracle.dense_fwd(q, k, v, causal=causal, block_mask=bm)
+        for c0 in range(0, n, 64):
+            c = slice(c0, min(n, c0 + 64))
+            ro, rl = oracle.dense_fwd(q[:, c], k[:, c], v[:, c], causal=causal)
+            np.testing.assert_allclose(o[:, c], ro, rtol=1e-14, atol=1e-15)
+            np.testing.assert_allclose(lse[:, c], rl, rtol=1e-14)
+
+
+def test_block_mask_against_torch_sdpa_and_autograd():
+    """Element mask built from the blocks, handed to torch's attention and
+    autograd in float64 (rows that see a key)."""
+    b, h, n, d = 1, 2, 170, 16
+    q, k, v = (_rand(b, h, n, d, seed=130 + i) for i in range(3))
+    do = _rand(b, h, n, d, seed=134)
+    bm = _bm(3, 3, seed=135, density=0.6, lead=(1, h))
+    bm[..., :, 0] = 1   # every row sees block 0, so no row is empty
+    for causal in (False, True):
+        o, lse = oracle.dense_fwd(q, k, v, causal=causal, block_mask=bm)
+        vis = np.take(np.take(bm != 0, np.arange(n) // 64, axis=-2), np.arange(n) // 64, axis=-1)
+        if causal:
+            vis = vis & np.tril(np.ones((n, n), bool))
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.tensor(vis))
+        np.testing.assert_allclose(o, ref.detach().numpy(), rtol=1e-12, atol=1e-13)
+        ref.backward(torch.tensor(do))
+        dq, dk, dv, _, _ = oracle.dense_bwd(q, k, v, do, causal=causal, block_mask=bm)
+        np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_block_mask_empty_rows_give_zero_and_minus_inf():
+    n = 130
+    q, k, v = _rand(n, 8, seed=141), _rand(n, 8, seed=142), _rand(n, 8, seed=143)
+    do = _rand(n, 8, seed=144)
+    bm = np.ones((3, 3), np.uint8)
+    bm[1, :] = 0              # rows 64..127 see nothing
+    o, lse = oracle.dense_fwd(q, k, v, block_mask=bm)
+    assert np.all(o[64:128] == 0) and np.all(lse[64:128] == -np.inf)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse[:64]))
+    dq, dk, dv, _, _ = oracle.dense_bwd(q, k, v, do, block_mask=bm)
+    assert np.all(np.isfinite(dq)) and np.all(dq[64:128] == 0)
+    # the other rows are untouched by the empty ones
+    keep = np.r_[0:64, 128:n]
+    ref = oracle.dense_fwd(q[keep], k, v, block_mask=None)
+    np.testing.assert_allclose(o[keep], ref[0], rtol=1e-14, atol=1e-15)
+    with pytest.raises(ValueError):
+        oracle.dense_fwd(q, k, v, block_mask=np.ones((2, 3)))
+
+
+def test_block_mask_catches_a_transposed_mask():
+    """Reading the mask as [key block, query block] fails the single-block pin."""
+    n = 128
+    q, k, v = _rand(n, 8, seed=151), _rand(n, 8, seed=152), _rand(n, 8, seed=153)
+    bm = np.array([[1, 0], [1, 1]], np.uint8)
+    good = oracle.dense_fwd(q, k, v, block_mask=bm)[0]
+    bad = oracle.dense_fwd(q, k, v, block_mask=bm.T)[0]
+    assert not np.allclose(good, bad)
+    s = (q[:64] @ k[:64].T) / math.sqrt(8)
+    np.testing.assert_allclose(good[:64], scipy.special.softmax(s, axis=1) @ v[:64], rtol=1e-13, atol=1e-14)
+
+
 # ---------------------------------------------------------------- key/value-outer order
 
 def test_kv_outer_two_block_worked_example(golden_dir):
