@@ -5,7 +5,7 @@ One step = one ``attn_fwd`` call over the long-context causal workload
 N(0, 1) inputs already resident in device memory.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd]
-                    [--no-window] [--no-kv-outer]
+                    [--no-window] [--no-sparse] [--no-kv-outer]
 
 The reported throughput counts algorithmic FLOPs only: 4 * d * (visible query-key
 pairs) * B * H, i.e. the two matrix products over the causal triangle.
@@ -16,7 +16,9 @@ on its own workload (B=4, H=16, N=4096, d=128, bf16, causal), counted as
 under "attn_fwd_window" the forward of the long-context head with a causal
 sliding window of 1024 keys (4 * d * windowed pairs * B * H FLOPs), and under
 "attn_fwd_kv_outer" the bench workload run in the original key/value-outer loop
-order (the comparison of the two orders' memory traffic; same FLOP count).
+order (the comparison of the two orders' memory traffic; same FLOP count),
+and under "attn_fwd_block_sparse" the head under a band + global + random
+64x64 block mask (4 * d * visible pairs FLOPs).
 """
 from __future__ import annotations
 
@@ -179,6 +181,43 @@ def window_record(fa, workloads, torch, steps, warmup):
                          "algorithmic_flops_per_launch": flops}}
 
 
+def sparse_record(fa, workloads, torch, steps, warmup):
+    """Block-sparse forward on its own workload (the bench head under a band +
+    global + random block mask), timed like the forward."""
+    w = workloads.WORKLOADS["long_sparse_bf16"]
+    x = workloads.make_inputs(w)
+    mask = workloads.block_sparse_mask(w.N, w.H, *w.sparse)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(torch.bfloat16).contiguous() for n in "qkv")
+    bm = torch.from_numpy(mask).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, block_mask=bm,
+                    stream=torch.cuda.current_stream(dev))
+
+    ms, warm = time_graph(step, steps, warmup, torch)
+    assert torch.isfinite(o).all().item()
+    flops = 4 * w.d * workloads.sparse_pairs(mask, w.N, w.causal) * w.B
+    tflops = flops / (ms * 1e-3) / 1e12
+    band, n_global, n_random, _ = w.sparse
+    return {"metric": f"attention fwd TFLOP/s (bf16, block-sparse {100 * float(mask.mean()):.1f} % of "
+                      f"64x64 blocks, T={w.N}, d={w.d})",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warm,
+            "ms_per_step": round(ms, 5),
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                       "mask": "causal" if w.causal else "none",
+                       "block_mask": f"band {band}, {n_global} global, {n_random} random blocks per "
+                                     f"query block, per head",
+                       "scale": w.scale, "inputs": "Q, K, V i.i.d. N(0,1) rounded to bf16, seed 7"},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "kernel": "fwd_kernel<bf16, d=128, block-sparse>",
+                         "algorithmic_flops_per_launch": flops}}
+
+
 def kv_outer_record(fa, workloads, torch, steps, warmup):
     """The bench workload in the key/value-outer loop order (attn_fwd_kv_outer),
     timed over a few calls: each is tens of milliseconds."""
@@ -222,6 +261,8 @@ def main():
                     help="skip the sliding-window forward measurement")
     ap.add_argument("--window-steps", type=int, default=200)
     ap.add_argument("--window-warmup", type=int, default=1500)
+    ap.add_argument("--no-sparse", action="store_true",
+                    help="skip the block-sparse forward measurement")
     ap.add_argument("--no-kv-outer", action="store_true",
                     help="skip the key/value-outer loop-order measurement")
     ap.add_argument("--kv-steps", type=int, default=3)
@@ -310,6 +351,9 @@ def main():
     if not args.no_window:
         record["attn_fwd_window"] = window_record(fa, workloads, torch, args.window_steps,
                                                   args.window_warmup)
+    if not args.no_sparse:
+        record["attn_fwd_block_sparse"] = sparse_record(fa, workloads, torch, args.window_steps,
+                                                        args.window_warmup)
     if not args.no_kv_outer:
         record["attn_fwd_kv_outer"] = kv_outer_record(fa, workloads, torch, args.kv_steps,
                                                       args.kv_warmup)

@@ -207,6 +207,31 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
                      void* stream);
 
 /*
+ * attn_fwd_block_sparse -- forward pass with a block-sparse mask.
+ *
+ * As attn_fwd, except that key j is visible to query i only if the mask
+ * block of (query block i / 64, key block j / 64) is nonzero (and, with
+ * FA_MASK_CAUSAL, also j <= i).  Key tiles that no query of a block of 256
+ * rows may see are not read or computed at all, the way causal attention
+ * skips the tiles above the diagonal ("Flash Attention: IO-Aware Exact
+ * Attention", section "Storage, arithmetic and IO are separate quantities":
+ * blocks that are skipped change which pairs are computed).  A row that
+ * sees no key at all gets O = 0 and LSE = -inf.
+ *
+ *   block_mask    device uint8 array [mask_batches][mask_heads][nb][nb],
+ *                 nb = ceil(N / 64), dense; nonzero = visible.
+ *   mask_batches  1 (one pattern for all batches) or B; FA_ERR_SHAPE else.
+ *   mask_heads    1 (one pattern for all heads) or H; FA_ERR_SHAPE else.
+ *   N             at most 2048 * 64 = 131072 (FA_ERR_UNSUPPORTED above).
+ *   other arguments and errors as for attn_fwd; FA_ERR_NULL if block_mask
+ *   is NULL.
+ */
+int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t H, int64_t N, int64_t d,
+                          const uint8_t* block_mask, int64_t mask_batches, int64_t mask_heads,
+                          int mask, float scale, int dtype, void* stream);
+
+/*
  * attn_fwd_kv_outer -- the same forward pass in the original key/value-outer
  * loop order, for comparing the two orders' memory traffic.
  *

@@ -54,6 +54,9 @@ def lib():
         L.attn_bwd_strided.restype = ctypes.c_int
         L.attn_bwd_strided.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64p, i64p, ctypes.c_int,
                                                   ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp]
+        L.attn_fwd_block_sparse.restype = ctypes.c_int
+        L.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i64, i64,
+                                            ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
         L.attn_fwd_kv_outer.restype = ctypes.c_int
         L.attn_fwd_kv_outer.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                          ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp]
@@ -124,6 +127,12 @@ def attn_bwd_strided_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, in_st, g
                                   _strides(grad_st), mask, scale, dtype, ws, ws_bytes, stream)
 
 
+def attn_fwd_block_sparse_raw(q, k, v, o, lse, B, H, N, d, block_mask, mask_batches, mask_heads,
+                              mask, scale, dtype, stream):
+    return lib().attn_fwd_block_sparse(q, k, v, o, lse, B, H, N, d, block_mask, mask_batches,
+                                       mask_heads, mask, scale, dtype, stream)
+
+
 def _layout(t):
     """{batch, head, row} element strides of a [B, H, N, d] tensor whose last
     axis is contiguous; axes of extent 1 get stride 0 (their stride is never
@@ -149,14 +158,16 @@ def _torch_dtype_code(t):
 
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=None, lse=None,
-             return_lse: bool = True, stream=None, window: int | None = None):
+             return_lse: bool = True, stream=None, window: int | None = None, block_mask=None):
     """Exact attention forward on the GPU: returns ``(o, lse)`` (lse None if not requested).
 
     q, k, v: contiguous device tensors [B, H, N, d] of one dtype (float32,
     float16 or bfloat16), d in {64, 128}.  ``scale`` defaults to 1/sqrt(d).
     ``window`` (causal only) calls ``attn_fwd_window``: query i sees keys
-    i - window < j <= i.  Work is enqueued on ``stream`` (default: torch's
-    current stream).
+    i - window < j <= i.  ``block_mask`` (uint8 device tensor
+    [1 or B, 1 or H, ceil(N/64), ceil(N/64)]) calls ``attn_fwd_block_sparse``.
+    Non-contiguous q, k, v (last axis contiguous) call ``attn_fwd_strided``.
+    Work is enqueued on ``stream`` (default: torch's current stream).
     """
     import torch
     if q.shape != k.shape or q.shape != v.shape or q.dim() != 4:
@@ -175,6 +186,25 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=N
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    if block_mask is not None:
+        import torch as _t
+        nb = -(-N // 64)
+        bm = block_mask
+        if bm.dim() != 4 or bm.shape[-2:] != (nb, nb) or bm.shape[0] not in (1, B) or \
+                bm.shape[1] not in (1, H):
+            raise ValueError(f"block_mask must be [1 or B, 1 or H, {nb}, {nb}], got {tuple(bm.shape)}")
+        if bm.dtype != _t.uint8 or not bm.is_cuda or not bm.is_contiguous():
+            raise ValueError("block_mask must be a contiguous uint8 device tensor")
+        if window is not None or not all(t.is_contiguous() for t in (q, k, v, out)):
+            raise ValueError("a block-sparse mask takes contiguous q, k, v, out and no window")
+        st = attn_fwd_block_sparse_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       lse.data_ptr() if return_lse else None, B, H, N, d,
+                                       bm.data_ptr(), bm.shape[0], bm.shape[1],
+                                       MASK_CAUSAL if causal else MASK_NONE, float(scale),
+                                       _torch_dtype_code(q), stream.cuda_stream)
+        if st != 0:
+            raise FaError(st, "attn_fwd_block_sparse")
+        return out, (lse if return_lse else None)
     if not all(t.is_contiguous() for t in (q, k, v, out)):
         # strided views (transposed, packed, or k and v broadcast over heads)
         if window is not None:

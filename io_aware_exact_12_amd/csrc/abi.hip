@@ -9,7 +9,10 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
+// Block-sparse: mask blocks of 64 x 64; a query block of the forward lists at
+// most this many key tiles (its LDS list).
+constexpr int64_t kMaxSparseTiles = 2048;
 // Largest query-block count times B*H that still indexes a 1-D grid, with the
 // smallest query block any kernel uses (64 rows).
 constexpr int64_t kMaxGrid = (int64_t)INT32_MAX;
@@ -72,7 +75,8 @@ int check_layout(const int64_t* st, int64_t B, int64_t H, int64_t N, int64_t d, 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
              int64_t N, int64_t d, int mask, int64_t window, float scale, int dtype, void* stream,
              const int64_t* q_st = nullptr, const int64_t* kv_st = nullptr,
-             const int64_t* out_st = nullptr) {
+             const int64_t* out_st = nullptr, const uint8_t* block_mask = nullptr,
+             int64_t mask_b = 0, int64_t mask_h = 0) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_NULL;
@@ -85,6 +89,14 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     if (e1 == FA_OK) e1 = check_layout(kv_st, B, H, N, d, dtype, false, &a.in);
     if (e1 == FA_OK) e1 = check_layout(out_st, B, H, N, d, dtype, true, &a.out);
     if (e1 != FA_OK) return e1;
+  }
+  if (block_mask != nullptr) {
+    const int64_t nb = (N + 63) / 64;
+    if ((mask_b != 1 && mask_b != B) || (mask_h != 1 && mask_h != H)) return FA_ERR_SHAPE;
+    if (nb > kMaxSparseTiles) return FA_ERR_UNSUPPORTED;
+    a.block_mask = block_mask;
+    a.mask_sh = mask_h == 1 ? 0 : nb * nb;
+    a.mask_sb = mask_b == 1 ? 0 : mask_h * nb * nb;
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
@@ -209,6 +221,15 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
   if (in_strides == nullptr || grad_strides == nullptr) return FA_ERR_NULL;
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, N, scale, dtype, workspace,
                   workspace_bytes, stream, in_strides, grad_strides);
+}
+
+int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t H, int64_t N, int64_t d, const uint8_t* block_mask,
+                          int64_t mask_batches, int64_t mask_heads, int mask, float scale, int dtype,
+                          void* stream) {
+  if (block_mask == nullptr) return FA_ERR_NULL;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, mask, N, scale, dtype, stream, nullptr, nullptr,
+                  nullptr, block_mask, mask_batches, mask_heads);
 }
 
 size_t attn_fwd_kv_outer_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {

@@ -31,6 +31,10 @@ struct FwdArgs {
   // (window >= N is plain causal)
   int64_t window;
   Layout lq, in, out;
+  // block-sparse mask (or null): uint8 [mask batch][mask head][ceil(N/64)][ceil(N/64)]
+  // with element strides mask_sb, mask_sh (0 broadcasts over batch or head)
+  const uint8_t* block_mask;
+  int64_t mask_sb, mask_sh;
 };
 
 // Arguments of one backward launch after validation.  workspace holds at

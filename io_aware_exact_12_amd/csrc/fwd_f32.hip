@@ -31,7 +31,9 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
                                                          float* __restrict__ O,
                                                          float* __restrict__ LSE, int N,
                                                          int win, int H, int n_qblocks, float scale,
-                                                         Layout lq, Layout in, Layout out) {
+                                                         Layout lq, Layout in, Layout out,
+                                                         const uint8_t* __restrict__ bmask,
+                                                         int64_t m_sb, int64_t m_sh) {
   constexpr int kQStride = D + 1;  // odd stride: lanes reading their own row hit distinct banks
   __shared__ float qs[kRows * kQStride];
   __shared__ __attribute__((aligned(16))) float ks[kKeys * D];
@@ -53,6 +55,11 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   }
 
   const int my_q = q0 + lane;
+  // block-sparse mask row of this query (64 x 64 blocks), if any
+  const int n_kb = (N + 63) / 64;
+  const uint8_t* mrow = (bmask != nullptr && my_q < N)
+                            ? bmask + b * m_sb + h * m_sh + (int64_t)(my_q / 64) * n_kb
+                            : nullptr;
   const int last_row = min(N, q0 + kRows) - 1;
   const int n_keys = Causal ? last_row + 1 : N;
   // first key any row of the block can see (sliding window; 0 without one)
@@ -90,7 +97,8 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
 #pragma unroll
     for (int j = 0; j < kKeys; ++j) {
       const int key = key0 + j;
-      const bool hide = key >= N || (Causal && (key > my_q || key <= my_q - win));
+      const bool hide = key >= N || (Causal && (key > my_q || key <= my_q - win)) ||
+                        (bmask != nullptr && (mrow == nullptr || mrow[key / 64] == 0));
       t[j] = hide ? -INFINITY : t[j] * dscale;
       tmax = fmax(tmax, t[j]);
     }
@@ -118,7 +126,8 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   if (my_q < N) {
     float* orow = O + (b * out.sb + h * out.sh) + (int64_t)my_q * out.sn;
 #pragma unroll
-    for (int col = 0; col < D; ++col) orow[col] = (float)((double)acc[col] / l_run);
+    // a row that saw no key (block-sparse) stores O = 0 and LSE = -inf
+    for (int col = 0; col < D; ++col) orow[col] = l_run > 0.0 ? (float)((double)acc[col] / l_run) : 0.f;
     if (LSE != nullptr) LSE[(int64_t)bh * N + my_q] = (float)(m_run + log(l_run));
   }
 }
@@ -131,7 +140,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_f32_kernel<D, Causal>), grid, dim3(kRows), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, N,
-                     (int)(a.window < a.N ? a.window : a.N), (int)a.H, n_qblocks, a.scale, a.lq, a.in, a.out);
+                     (int)(a.window < a.N ? a.window : a.N), (int)a.H, n_qblocks, a.scale, a.lq, a.in, a.out,
+                     a.block_mask, a.mask_sb, a.mask_sh);
   return hipGetLastError();
 }
 

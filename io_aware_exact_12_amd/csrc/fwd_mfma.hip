@@ -71,7 +71,15 @@ constexpr float kSumCap = 256.0f;
 constexpr float kNoRef = 1e30f;
 // Masks a block of scores may need: none, the causal diagonal and the
 // sequence end, or those and the left edge of a sliding window.
-constexpr int kMaskNone = 0, kMaskEdge = 1, kMaskWindow = 2;
+constexpr int kMaskNone = 0, kMaskEdge = 1, kMaskWindow = 2, kMaskSparse = 3;
+// Kernel modes: plain (causal or not), causal sliding window, block-sparse.
+constexpr int kModePlain = 0, kModeWindow = 1, kModeSparse = 2;
+// Block-sparse: 64 x 64 mask blocks; a workgroup's list of key tiles lives
+// in LDS after the rings (one 32-bit entry per tile: index | query-block bits
+// << 16), with room for this many tiles, plus 8 wave counts.
+constexpr int kSparseBlock = 64;
+constexpr int kMaxSparseTiles = 2048;
+constexpr int kSparseBytes = 4 * kMaxSparseTiles + 64;
 
 // LDS row strides (bytes).  K rows carry 16 bytes of padding: the sixteen
 // lanes of a 16-byte operand read touch sixteen consecutive rows, which then
@@ -94,11 +102,15 @@ template <int D> struct Lds {
 
 // Per-workgroup state and steps of the forward pass.  Everything here is
 // device-only; the kernel below only constructs it and runs the tile loop.
-// Window (causal only) adds a sliding window narrower than the sequence: key
-// j is visible to query i iff i - win < j <= i.
-template <bool IsBf16, int D, bool Causal, bool Window>
+// Mode kModeWindow (causal only) adds a sliding window narrower than the
+// sequence: key j is visible to query i iff i - win < j <= i.  Mode
+// kModeSparse adds a block-sparse mask: key j is visible to query i iff the
+// mask byte of (query block i / 64, key block j / 64) is nonzero.
+template <bool IsBf16, int D, bool Causal, int Mode>
 struct FwdBlock {
-  static constexpr bool kWin = Causal && Window;
+  static constexpr bool kWin = Causal && Mode == kModeWindow;
+  static constexpr bool kSparse = Mode == kModeSparse;
+  static_assert(kBN == kSparseBlock && kBM % kSparseBlock == 0, "mask blocks are key tiles");
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using L = Lds<D>;
@@ -128,6 +140,10 @@ struct FwdBlock {
   int64_t o_sn;
   int N, win, wave, lane, l32, g, q0, my_q, n_tiles, n_sub;
   int u_lo;   // first 32-key block this wave computes (sliding window)
+  // block-sparse: the workgroup's key tiles in LDS, their count, and the bit
+  // of this wave's 64-row query block in a list entry
+  const uint32_t* tiles;
+  int n_pos, qbit;
   float c;
   uint32_t src_k[kFullK], src_v[kFullV], src_x;  // per-lane source offsets of the copies
   // The extra copy writes LDS byte x_off + (K stage offset & x_kmask) +
@@ -290,14 +306,29 @@ struct FwdBlock {
     __builtin_amdgcn_s_waitcnt(0x0F70 | kCopies);
   }
 
+  // Key tile at list position p (block-sparse), or n_tiles (zeros) past its end.
+  __device__ __forceinline__ int tile_at(int p) const {
+    return p < n_pos ? __builtin_amdgcn_readfirstlane((int)(tiles[p] & 0xFFFFu)) : n_tiles;
+  }
+  // First key of 32-key block u (block-sparse: block u is half u & 1 of the
+  // tile at list position u / 2).
+  __device__ __forceinline__ int kpos(int u) const {
+    return kSparse ? kBN * tile_at(u >> 1) + 32 * (u & 1) : 32 * u;
+  }
+
   // Hide keys of block u that this lane's query may not see: the causal
-  // diagonal and the sequence end, and with kMaskWindow also keys left of the
-  // query's sliding window.
+  // diagonal and the sequence end; with kMaskWindow also keys left of the
+  // query's sliding window; with kMaskSparse the whole block when the mask
+  // hides its tile from this wave's query block.
   template <int kMask>
   __device__ __forceinline__ void apply_mask(int u, f32x16& st) const {
-    // register r of lane half g holds key 32 u + 16 (r >> 3) + 8 g + (r & 7)
-    const int lim = (Causal ? min(my_q, N - 1) : N - 1) - 32 * u - 8 * g;
-    const int lo = my_q - win + 1 - 32 * u - 8 * g;
+    // register r of lane half g holds key kpos(u) + 16 (r >> 3) + 8 g + (r & 7)
+    const int k0 = kpos(u);
+    int lim = (Causal ? min(my_q, N - 1) : N - 1) - k0 - 8 * g;
+    if (kMask == kMaskSparse && (u >> 1) < n_pos &&
+        ((tiles[u >> 1] >> qbit) & 1u) == 0)
+      lim = -1;  // the whole block is hidden from this wave
+    const int lo = my_q - win + 1 - k0 - 8 * g;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int o = 16 * (r >> 3) + (r & 7);
@@ -488,10 +519,16 @@ struct FwdBlock {
   // wave to overlap its MFMAs and VALU work.  So a wave's priority falls as it
   // gets through the step (3 at the start, 2, 1, 0 at each half block): the
   // wave that is behind issues first and the pair stays level.
+  //
+  // Block-sparse: j is the position in the workgroup's tile list; stages
+  // follow positions, and the copies fetch the listed tiles.
   template <int kMask, bool kFirstStep = false>
   __device__ __forceinline__ void step(int j) {
     __builtin_amdgcn_s_setprio(3);
-    load_tiles(j + 3, (j + 3) & 3, j + 2, (j + 2) & 3);
+    if (kSparse)
+      load_tiles(tile_at(j + 3), (j + 3) & 3, tile_at(j + 2), (j + 2) & 3);
+    else
+      load_tiles(j + 3, (j + 3) & 3, j + 2, (j + 2) & 3);
     if (kFirstStep) {
       if (u_lo == 2 * j && u_lo < n_sub) block<kMask, true, 0>(2 * j);
       if (u_lo == 2 * j + 1 && u_lo < n_sub)
@@ -511,8 +548,61 @@ struct FwdBlock {
   // LDS holds rings of kStages K tiles and kStages V tiles; tile j lives in
   // stage j & 3.  The workgroup's first tile j_lo is the first one that any of
   // its queries can see (0 unless a sliding window starts later).
-  __device__ __forceinline__ void run(int q0_blk) {
+  // Block-sparse: list the key tiles that some query block of this workgroup
+  // may see (the causal limit included), in order, each with one bit per
+  // 64-row query block; rows of the mask past N read as hidden.
+  __device__ __forceinline__ void build_tile_list(uint32_t* list, const uint8_t* mask, int q0_blk) {
+    const int tid = threadIdx.x;
+    const int n_kb = (N + kBN - 1) / kBN, n_qb = (N + kSparseBlock - 1) / kSparseBlock;
+    const int qb0 = q0_blk / kSparseBlock;
+    uint32_t* counts = list + kMaxSparseTiles;
+    int base = 0;
+    for (int c0 = 0; c0 < n_tiles; c0 += kThreads) {
+      const int jt = c0 + tid;
+      uint32_t bits = 0;
+      if (jt < n_tiles) {
+#pragma unroll
+        for (int i = 0; i < kBM / kSparseBlock; ++i) {
+          const int qb = qb0 + i;
+          if (qb < n_qb && (!Causal || jt <= qb) && mask[(int64_t)qb * n_kb + jt] != 0) bits |= 1u << i;
+        }
+      }
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(bits != 0);
+      const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      if (lane == 0) counts[wave] = (uint32_t)__builtin_popcountll(bal);
+      __syncthreads();
+      int off = base, total = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int cw = (int)counts[w];
+        off += w < wave ? cw : 0;
+        total += cw;
+      }
+      if (bits != 0) list[off + rank] = (uint32_t)jt | (bits << 16);
+      base += total;
+      __syncthreads();  // counts are rewritten by the next chunk; the list is complete
+    }
+    n_pos = __builtin_amdgcn_readfirstlane(base);
+  }
+
+  __device__ __forceinline__ void run(int q0_blk, uint32_t* list = nullptr, const uint8_t* mask = nullptr) {
     static_assert(kStages == 4, "the ring arithmetic assumes four stages");
+    if constexpr (kSparse) {
+      build_tile_list(list, mask, q0_blk);
+      tiles = list;
+      n_sub = q0 >= N ? 0 : 2 * n_pos;  // every wave walks the whole list
+      // prologue as below, by list position
+      load_tiles(tile_at(0), 0, tile_at(0), 0);
+      load_tiles(tile_at(1), 1, tile_at(1), 1);
+      load_tiles(tile_at(2), 2, n_tiles, 3);
+      wait_older_copies();
+      __syncthreads();
+      if (n_sub > 0) s_cur = scores<kMaskNone>(0);
+      if (n_pos > 0) step<kMaskSparse, true>(0);
+      for (int j = 1; j < n_pos; ++j) step<kMaskSparse>(j);
+      if (n_sub > 0) drain();
+      return;
+    }
     const int j_lo = kWin ? max(0, q0_blk - win + 1) / kBN : 0;
     // prologue: K, V tiles j_lo, j_lo+1 resident; K tile j_lo+2 in flight (its
     // V slot copies zeros into the stage V tile j_lo+3 overwrites one step later)
@@ -540,11 +630,12 @@ struct FwdBlock {
     if (n_sub > u_lo) drain();
   }
 
-  // O = a / l once; LSE = ln(sum) of the scaled scores
+  // O = a / l once; LSE = ln(sum) of the scaled scores.  Block-sparse rows
+  // that see no key store O = 0 and LSE = -inf.
   __device__ __forceinline__ void store(uint16_t* O, float* LSE, int bh) {
-    if (n_sub <= u_lo) return;
+    if (!kSparse && n_sub <= u_lo) return;
     const float l_tot = xhalf_sum(l_part);
-    const float inv = 1.0f / l_tot;
+    const float inv = (!kSparse || l_tot > 0.f) ? 1.0f / l_tot : 0.f;
     if (my_q >= N) return;
     uint16_t* orow = O + o_off + (int64_t)my_q * o_sn;
     typedef __attribute__((ext_vector_type(4))) typename E::scalar h4_t;
@@ -563,23 +654,31 @@ struct FwdBlock {
   }
 };
 
-template <bool IsBf16, int D, bool Causal, bool Window>
+template <bool IsBf16, int D, bool Causal, int Mode>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int win, int H, int BH, int n_qblocks,
-    float c, uint32_t q_sign, Layout lq, Layout in, Layout out) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds<D>::kBytes];
+    float c, uint32_t q_sign, Layout lq, Layout in, Layout out, const uint8_t* __restrict__ bmask,
+    int64_t m_sb, int64_t m_sh) {
+  static_assert(Lds<D>::kBytes + kSparseBytes <= 160 * 1024, "the tile list fits beside the rings");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds<D>::kBytes + (Mode == kModeSparse ? kSparseBytes : 0)];
   // work item: (query block, batch*head); heaviest causal blocks first
   const int bh = blockIdx.x % BH;
   int qb = blockIdx.x / BH;
   if (Causal) qb = n_qblocks - 1 - qb;
-  FwdBlock<IsBf16, D, Causal, Window> blk;
+  FwdBlock<IsBf16, D, Causal, Mode> blk;
   blk.init(smem, Q, K, V, N, win, H, bh, qb, c, q_sign, lq, in, out);
-  blk.run(qb * kBM);
+  if constexpr (Mode == kModeSparse) {
+    const int b = bh / H, h = bh - b * H;
+    blk.qbit = 16 + blk.wave / 2;  // 32-row waves, 64-row mask blocks
+    blk.run(qb * kBM, reinterpret_cast<uint32_t*>(smem + Lds<D>::kBytes), bmask + b * m_sb + h * m_sh);
+  } else {
+    blk.run(qb * kBM);
+  }
   blk.store(O, LSE, bh);
 }
 
-template <bool IsBf16, int D, bool Causal, bool Window>
+template <bool IsBf16, int D, bool Causal, int Mode>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int N = (int)a.N;
   const int BH = (int)(a.B * a.H);
@@ -590,19 +689,21 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   // so all visible keys weigh exactly 1 and hidden ones (-inf) weigh 0.
   const float c = a.scale != 0.f ? __builtin_fabsf(a.scale) * 1.4426950408889634f : 1e-30f;
   const uint32_t q_sign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_kernel<IsBf16, D, Causal, Window>), grid, dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fwd_kernel<IsBf16, D, Causal, Mode>), grid, dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, N,
                      (int)(a.window < a.N ? a.window : a.N), (int)a.H, BH, n_qblocks, c, q_sign, a.lq,
-                     a.in, a.out);
+                     a.in, a.out, a.block_mask, a.mask_sb, a.mask_sh);
   return hipGetLastError();
 }
 
 template <bool IsBf16, int D>
 hipError_t dispatch_d(const FwdArgs& a, hipStream_t s) {
-  if (!a.causal) return launch<IsBf16, D, false, false>(a, s);
-  if (a.window < a.N) return launch<IsBf16, D, true, true>(a, s);
-  return launch<IsBf16, D, true, false>(a, s);
+  if (a.block_mask != nullptr)
+    return a.causal ? launch<IsBf16, D, true, kModeSparse>(a, s) : launch<IsBf16, D, false, kModeSparse>(a, s);
+  if (!a.causal) return launch<IsBf16, D, false, kModePlain>(a, s);
+  if (a.window < a.N) return launch<IsBf16, D, true, kModeWindow>(a, s);
+  return launch<IsBf16, D, true, kModePlain>(a, s);
 }
 
 template <bool IsBf16>

@@ -29,11 +29,12 @@ def test_library_exports_every_declared_symbol():
     declared = fa.declared_symbols()
     assert {"attn_fwd", "attn_bwd", "attn_fwd_window", "attn_bwd_window", "attn_bwd_workspace_bytes",
             "attn_fwd_kv_outer", "attn_fwd_kv_outer_workspace_bytes", "attn_fwd_strided",
-            "attn_bwd_strided", "fa_status_str", "fa_abi_version"} <= set(declared)
+            "attn_bwd_strided", "attn_fwd_block_sparse", "fa_status_str",
+            "fa_abi_version"} <= set(declared)
     lib = ctypes.CDLL(fa._binding.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
-    assert fa.lib().fa_abi_version() == 4
+    assert fa.lib().fa_abi_version() == 5
 
 
 def test_status_strings():
@@ -279,3 +280,27 @@ def test_head_extent_limit():
     """One head's rows must span less than 2 GiB (one buffer resource)."""
     assert fwd(N=(1 << 24), d=64) == FA_ERR_SHAPE          # 2 GiB of bf16 rows
     assert fwd_s(q_st=(0, 0, 1 << 20), N=2048) == FA_ERR_SHAPE  # rows 2 MiB apart
+
+
+# ---------------------------------------------------------------- block-sparse
+
+def fwd_bs(mask_ptr=P[7], mb=1, mh=1, **kw):
+    a = dict(q=P[0], B=2, H=3, N=200, d=64, mask=0, scale=0.125, dtype=fa.BF16)
+    a.update(kw)
+    return fa.attn_fwd_block_sparse_raw(a["q"], P[1], P[2], P[3], P[4], a["B"], a["H"], a["N"], a["d"],
+                                        mask_ptr, mb, mh, a["mask"], a["scale"], a["dtype"], None)
+
+
+def test_block_sparse_validation():
+    assert fwd_bs(mask_ptr=None) == FA_ERR_NULL
+    assert fwd_bs(mb=0) == FA_ERR_SHAPE
+    assert fwd_bs(mb=3) == FA_ERR_SHAPE      # neither 1 nor B
+    assert fwd_bs(mh=2) == FA_ERR_SHAPE      # neither 1 nor H
+    assert fwd_bs(N=2048 * 64 + 1) == FA_ERR_UNSUPPORTED   # more key tiles than the list holds
+    assert fwd_bs(d=96) == FA_ERR_UNSUPPORTED
+    assert fwd_bs(dtype=5) == FA_ERR_DTYPE
+    assert fwd_bs(mask=2) == FA_ERR_MASK
+    # accepted shapes reach the pointer checks (no launch here)
+    for mb, mh in ((1, 1), (2, 1), (1, 3), (2, 3)):
+        assert fwd_bs(q=P[0] + 2, mb=mb, mh=mh) == FA_ERR_ALIGN
+    assert fwd_bs(q=P[0] + 2, N=2048 * 64) == FA_ERR_ALIGN

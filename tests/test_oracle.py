@@ -695,6 +695,16 @@ def test_workload_flops_and_bytes():
     assert w.fwd_bytes() == 134742016
 
 
+@pytest.mark.parametrize("n,causal", [(1, False), (64, True), (300, False), (300, True), (257, True)])
+def test_workload_sparse_pairs_count_the_mask(n, causal):
+    """The pair count of a block-sparse launch is the number of visible entries
+    of the oracle's own mask, counted by brute force."""
+    m = workloads.block_sparse_mask(n, 2, 1, 1, 1, seed=5)
+    q = np.ones((1, 2, n, 4))
+    probs = oracle.dense_probs(q, q, causal=causal, block_mask=m)
+    assert workloads.sparse_pairs(m, n, causal) == int((probs > 0).sum())
+
+
 @pytest.mark.parametrize("n,win", [(1, 1), (7, 1), (7, 3), (7, 7), (7, 50), (64, 17)])
 def test_workload_window_pairs_count_the_mask(n, win):
     """The pair count of a windowed workload is the number of visible entries

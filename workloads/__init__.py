@@ -13,7 +13,10 @@ Shapes and value distributions follow the five workloads the method is judged
 on: a tiny fp32 unmasked head, a GPT-2-small-shaped causal layer, the long
 context causal head, a ragged-length fp16 case with sharp softmax rows, and the
 causal forward+backward case.  A sixth, the long context head under a causal
-sliding window of 1024 keys, measures the window path.  No public dataset is involved; the GPT-2-small
+sliding window of 1024 keys, measures the window path; a seventh, the same
+head under a block-sparse mask (``block_sparse_mask``: a band of neighbouring
+64-key blocks, global blocks and random blocks per query block, as sparse
+long-context patterns use), measures the block-sparse path.  No public dataset is involved; the GPT-2-small
 shape stands in for the GPT-2 training workload named on the pages (Road to
 Intelligence "FlashAttention", section "What it bought").
 """
@@ -41,6 +44,7 @@ class Workload:
     v_dist: str = "normal"   # "normal" -> N(0,1), "uniform" -> U(-1, 1)
     backward: bool = False   # also draw dO ~ N(0, 1)
     window: int | None = None  # causal sliding window: key j visible to query i iff i - W < j <= i
+    sparse: tuple | None = None  # block-sparse pattern: (band, n_global, n_random, mask seed)
 
     @property
     def scale(self) -> float:
@@ -49,6 +53,8 @@ class Workload:
     def pairs(self) -> int:
         """Visible (query, key) pairs of one head."""
         n, w = self.N, self.window
+        if self.sparse is not None:
+            raise ValueError("block-sparse pairs depend on the mask: use sparse_pairs(mask)")
         if not self.causal:
             return n * n
         if w is None or w >= n:
@@ -81,7 +87,45 @@ WORKLOADS = {
                                     backward=True),
     "long_window_bf16": Workload("long_window_bf16", "bf16", True, 1, 16, 8192, 128, seed=6,
                                  window=1024),
+    "long_sparse_bf16": Workload("long_sparse_bf16", "bf16", False, 1, 16, 8192, 128, seed=7,
+                                 sparse=(1, 2, 3, 70)),
 }
+
+
+def block_sparse_mask(n, heads, band, n_global, n_random, seed):
+    """A uint8 [1, heads, nb, nb] block mask (nb = ceil(n / 64)): query block i
+    sees key blocks i - band .. i + band, the first ``n_global`` blocks, and
+    ``n_random`` further blocks drawn per (head, query block)."""
+    nb = -(-n // 64)
+    rng = np.random.default_rng(seed)
+    m = np.zeros((1, heads, nb, nb), np.uint8)
+    for h in range(heads):
+        for i in range(nb):
+            m[0, h, i, max(0, i - band):min(nb, i + band + 1)] = 1
+            m[0, h, i, :min(nb, n_global)] = 1
+            if n_random:
+                m[0, h, i, rng.choice(nb, size=min(nb, n_random), replace=False)] = 1
+    return m
+
+
+def sparse_pairs(mask, n, causal=False):
+    """Visible (query, key) pairs summed over the heads of a [1, H, nb, nb]
+    block mask for sequence length n (the FLOP count of a block-sparse launch
+    is 4 d times this, times the batch)."""
+    nb = mask.shape[-1]
+    size = np.full(nb, 64)
+    size[-1] = n - 64 * (nb - 1)
+    total = 0
+    for h in range(mask.shape[1]):
+        for i in range(nb):
+            for j in np.nonzero(mask[0, h, i])[0]:
+                if causal and j > i:
+                    continue
+                if causal and j == i:
+                    total += size[i] * (size[i] + 1) // 2
+                else:
+                    total += int(size[i]) * int(size[j])
+    return total
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
