@@ -232,6 +232,20 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, 
                           int mask, float scale, int dtype, void* stream);
 
 /*
+ * attn_bwd_block_sparse -- backward pass of attn_fwd_block_sparse: as attn_bwd
+ * with the block mask of the forward (same block_mask, mask_batches,
+ * mask_heads and mask).  Tiles hidden from every block of a workgroup are
+ * skipped; rows that saw no key get dq = 0, keys no query saw get
+ * dk = dv = 0.
+ */
+int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          int64_t B, int64_t H, int64_t N, int64_t d,
+                          const uint8_t* block_mask, int64_t mask_batches, int64_t mask_heads,
+                          int mask, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * attn_fwd_kv_outer -- the same forward pass in the original key/value-outer
  * loop order, for comparing the two orders' memory traffic.
  *

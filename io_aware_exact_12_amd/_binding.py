@@ -57,6 +57,10 @@ def lib():
         L.attn_fwd_block_sparse.restype = ctypes.c_int
         L.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i64, i64,
                                             ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+        L.attn_bwd_block_sparse.restype = ctypes.c_int
+        L.attn_bwd_block_sparse.argtypes = [vp] * 9 + [i64, i64, i64, i64, vp, i64, i64, ctypes.c_int,
+                                                       ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t,
+                                                       vp]
         L.attn_fwd_kv_outer.restype = ctypes.c_int
         L.attn_fwd_kv_outer.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                          ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp]
@@ -133,6 +137,23 @@ def attn_fwd_block_sparse_raw(q, k, v, o, lse, B, H, N, d, block_mask, mask_batc
                                        mask_heads, mask, scale, dtype, stream)
 
 
+def attn_bwd_block_sparse_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, block_mask,
+                              mask_batches, mask_heads, mask, scale, dtype, ws, ws_bytes, stream):
+    return lib().attn_bwd_block_sparse(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, block_mask,
+                                       mask_batches, mask_heads, mask, scale, dtype, ws, ws_bytes,
+                                       stream)
+
+
+def _check_block_mask(bm, B, H, N):
+    import torch
+    nb = -(-N // 64)
+    if bm.dim() != 4 or tuple(bm.shape[-2:]) != (nb, nb) or bm.shape[0] not in (1, B) or \
+            bm.shape[1] not in (1, H):
+        raise ValueError(f"block_mask must be [1 or B, 1 or H, {nb}, {nb}], got {tuple(bm.shape)}")
+    if bm.dtype != torch.uint8 or not bm.is_cuda or not bm.is_contiguous():
+        raise ValueError("block_mask must be a contiguous uint8 device tensor")
+
+
 def _layout(t):
     """{batch, head, row} element strides of a [B, H, N, d] tensor whose last
     axis is contiguous; axes of extent 1 get stride 0 (their stride is never
@@ -187,14 +208,8 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=N
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     if block_mask is not None:
-        import torch as _t
-        nb = -(-N // 64)
         bm = block_mask
-        if bm.dim() != 4 or bm.shape[-2:] != (nb, nb) or bm.shape[0] not in (1, B) or \
-                bm.shape[1] not in (1, H):
-            raise ValueError(f"block_mask must be [1 or B, 1 or H, {nb}, {nb}], got {tuple(bm.shape)}")
-        if bm.dtype != _t.uint8 or not bm.is_cuda or not bm.is_contiguous():
-            raise ValueError("block_mask must be a contiguous uint8 device tensor")
+        _check_block_mask(bm, B, H, N)
         if window is not None or not all(t.is_contiguous() for t in (q, k, v, out)):
             raise ValueError("a block-sparse mask takes contiguous q, k, v, out and no window")
         st = attn_fwd_block_sparse_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -276,7 +291,8 @@ def attn_fwd_kv_outer(q, k, v, causal: bool = False, scale: float | None = None,
 
 
 def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, *,
-             dq=None, dk=None, dv=None, workspace=None, stream=None, window: int | None = None):
+             dq=None, dk=None, dv=None, workspace=None, stream=None, window: int | None = None,
+             block_mask=None):
     """Gradients (dq, dk, dv) of sum(o * dout) for o, lse = attn_fwd(q, k, v, causal, scale,
     window=window) (``window`` calls ``attn_bwd_window``).
 
@@ -309,6 +325,19 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
+    if block_mask is not None:
+        _check_block_mask(block_mask, B, H, N)
+        if window is not None or not all(t.is_contiguous() for t in (q, k, v, o, dout, dq, dk, dv)):
+            raise ValueError("a block-sparse mask takes contiguous tensors and no window")
+        st = attn_bwd_block_sparse_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                       dv.data_ptr(), B, H, N, d, block_mask.data_ptr(),
+                                       block_mask.shape[0], block_mask.shape[1],
+                                       MASK_CAUSAL if causal else MASK_NONE, float(scale), code,
+                                       workspace.data_ptr(), ws_bytes, stream.cuda_stream)
+        if st != 0:
+            raise FaError(st, "attn_bwd_block_sparse")
+        return dq, dk, dv
     if not all(t.is_contiguous() for t in (q, k, v, o, dout, dq, dk, dv)):
         # strided views: q, k, v, o, dout share one layout, dq, dk, dv another
         if window is not None:

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 // Block-sparse: mask blocks of 64 x 64; a query block of the forward lists at
 // most this many key tiles (its LDS list).
 constexpr int64_t kMaxSparseTiles = 2048;
@@ -116,7 +116,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
              int64_t d, int mask, int64_t window, float scale, int dtype, void* workspace,
              size_t workspace_bytes, void* stream, const int64_t* in_st = nullptr,
-             const int64_t* out_st = nullptr) {
+             const int64_t* out_st = nullptr, const uint8_t* block_mask = nullptr,
+             int64_t mask_b = 0, int64_t mask_h = 0) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr ||
@@ -135,6 +136,14 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
     if (e1 != FA_OK) return e1;
     e1 = check_layout(out_st, B, H, N, d, dtype, true, &a.out);
     if (e1 != FA_OK) return e1;
+  }
+  if (block_mask != nullptr) {
+    const int64_t nb = (N + 63) / 64;
+    if ((mask_b != 1 && mask_b != B) || (mask_h != 1 && mask_h != H)) return FA_ERR_SHAPE;
+    if (nb > kMaxSparseTiles) return FA_ERR_UNSUPPORTED;
+    a.block_mask = block_mask;
+    a.mask_sh = mask_h == 1 ? 0 : nb * nb;
+    a.mask_sb = mask_b == 1 ? 0 : mask_h * nb * nb;
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
@@ -230,6 +239,16 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, 
   if (block_mask == nullptr) return FA_ERR_NULL;
   return fwd_impl(q, k, v, o, lse, B, H, N, d, mask, N, scale, dtype, stream, nullptr, nullptr,
                   nullptr, block_mask, mask_batches, mask_heads);
+}
+
+int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv, int64_t B,
+                          int64_t H, int64_t N, int64_t d, const uint8_t* block_mask,
+                          int64_t mask_batches, int64_t mask_heads, int mask, float scale, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (block_mask == nullptr) return FA_ERR_NULL;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, N, scale, dtype, workspace,
+                  workspace_bytes, stream, nullptr, nullptr, block_mask, mask_batches, mask_heads);
 }
 
 size_t attn_fwd_kv_outer_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {

@@ -210,9 +210,9 @@ template <int D> struct DkdvLds {
   static constexpr int kBytes = 2 * kStage;
 };
 
-template <bool IsBf16, int D, bool Causal, bool Window>
+template <bool IsBf16, int D, bool Causal, int Mode>
 struct DkdvBlock {
-  static constexpr bool kWin = Causal && Window;  // sliding window narrower than N
+  static constexpr bool kWin = Causal && Mode == kModeWindow;  // sliding window narrower than N
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using T = STile<D>;
@@ -344,15 +344,18 @@ struct DkdvBlock {
   }
 };
 
-template <bool IsBf16, int D, bool Causal, bool Window>
+template <bool IsBf16, int D, bool Causal, int Mode>
 __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NLse, const float* __restrict__ Dsum,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int win, int H, int BH, float c,
-    float dk_mul, uint32_t k_sign, Layout in, Layout out) {
+    float dk_mul, uint32_t k_sign, Layout in, Layout out, const uint8_t* __restrict__ bmask,
+    int64_t m_sb, int64_t m_sh) {
   using T = STile<D>;
   using Ld = DkdvLds<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes];
+  constexpr bool kSparse = Mode == kModeSparse;
+  static_assert(kT == kSparseBlock && kRes % kSparseBlock == 0, "mask blocks are tiles");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes + (kSparse ? kSparseBytes : 0)];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -361,8 +364,8 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
   const int64_t head = b * in.sb + h * in.sh, head_out = b * out.sb + h * out.sh;
   const int k0 = kblk * kRes, kw0 = k0 + 32 * wave;
 
-  constexpr bool kWin = Causal && Window;
-  DkdvBlock<IsBf16, D, Causal, Window> blk;
+  constexpr bool kWin = Causal && Mode == kModeWindow;
+  DkdvBlock<IsBf16, D, Causal, Mode> blk;
   blk.init(lane, N, win, kw0, c);
   load_resident<IsBf16, D>(blk.kf, K + head, N, blk.my_k, in.sn, blk.g, k_sign);
   load_resident<IsBf16, D>(blk.vf, V + head, N, blk.my_k, in.sn, blk.g, 0u);
@@ -372,7 +375,34 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
   const int n_tiles = kWin ? min((N + kT - 1) / kT, (k0 + kRes - 1 + win - 1) / kT + 1)
                            : (N + kT - 1) / kT;
   const int t_first = Causal ? k0 / kT : 0;  // earlier query tiles see none of these keys
-  const int n_it = n_tiles - t_first;
+  // Block-sparse: the query tiles some key block of this workgroup may be
+  // seen by, listed in LDS with one bit per 64-key block; a wave skips the
+  // tiles its own key block is hidden from.
+  uint32_t* const list = reinterpret_cast<uint32_t*>(smem + Ld::kBytes);
+  int n_it = n_tiles - t_first;
+  if constexpr (kSparse) {
+    const int nb = (N + kT - 1) / kT, kb0 = k0 / kSparseBlock;
+    const uint8_t* m = bmask + (bh / H) * m_sb + (bh % H) * m_sh;
+    n_it = compact_tiles<kW>(list, n_tiles, [&](int it) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int i = 0; i < kRes / kSparseBlock; ++i) {
+        const int kb = kb0 + i;
+        if (it >= t_first && kb < nb && (!Causal || kb <= it) && m[(int64_t)it * nb + kb] != 0)
+          bits |= 1u << i;
+      }
+      return bits;
+    });
+  }
+  // query tile at position i, and whether this wave's keys may be seen from it
+  auto tile_of = [&](int i) {
+    if constexpr (kSparse) return i < n_it ? __builtin_amdgcn_readfirstlane((int)(list[i] & 0xFFFFu)) : n_tiles;
+    else return t_first + i;
+  };
+  auto wave_sees = [&](int i) {
+    if constexpr (kSparse) return ((list[i] >> (16 + wave / 2)) & 1u) != 0;
+    else return true;
+  };
   const uint16_t* q_h = Q + head;
   const uint16_t* do_h = dO + head;
   const float* nl_h = NLse + (int64_t)bh * N;
@@ -403,16 +433,16 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
            kw0 + 32 > N;
   };
 
-  issue(t_first, 0);
+  issue(tile_of(0), 0);
   wait_copies();
   __syncthreads();
   // ---- pass V
   blk.zero();
   for (int i = 0; i < n_it; ++i) {
-    const int it = t_first + i, st = i & 1;
+    const int it = tile_of(i), st = i & 1;
     // the next tile, or (after the last one) the first tile again for pass K
-    issue(i + 1 < n_it ? it + 1 : t_first, st ^ 1);
-    if (live(it)) {
+    issue(tile_of(i + 1 < n_it ? i + 1 : 0), st ^ 1);
+    if (live(it) && wave_sees(i)) {
       const uint8_t* sb = smem + st * Ld::kStage;
       const bool m = masked(it);
 #pragma unroll
@@ -428,12 +458,12 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
   }
   const bool store = kw0 < N && blk.my_k < N;
   if (store) store_row<IsBf16, D>(dV + head_out, blk.my_k, out.sn, blk.g, blk.acc, 1.f);
-  // ---- pass K; tile t_first is already in stage n_it & 1
+  // ---- pass K; the first tile is already in stage n_it & 1
   blk.zero();
   for (int i = 0; i < n_it; ++i) {
-    const int it = t_first + i, st = (i + n_it) & 1;
-    if (i + 1 < n_it) issue(it + 1, st ^ 1);
-    if (live(it)) {
+    const int it = tile_of(i), st = (i + n_it) & 1;
+    if (i + 1 < n_it) issue(tile_of(i + 1), st ^ 1);
+    if (live(it) && wave_sees(i)) {
       const uint8_t* sb = smem + st * Ld::kStage;
       const bool m = masked(it);
 #pragma unroll
@@ -464,18 +494,20 @@ template <int D> struct DqLds {
   static constexpr int kBytes = 2 * kStage;
 };
 
-template <bool IsBf16, int D, bool Causal, bool Window>
+template <bool IsBf16, int D, bool Causal, int Mode>
 __global__ __launch_bounds__(kThr, 2) void bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dsum,
     float* __restrict__ NLse, uint16_t* __restrict__ dQ, int N, int win, int H, int BH, int n_qblocks,
-    float c, float dq_mul, uint32_t q_sign, Layout in, Layout out) {
+    float c, float dq_mul, uint32_t q_sign, Layout in, Layout out, const uint8_t* __restrict__ bmask,
+    int64_t m_sb, int64_t m_sh) {
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using T = STile<D>;
   using Ld = DqLds<D>;
   constexpr int kKs = D / 16, kDB = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes];
+  constexpr bool kSparse = Mode == kModeSparse;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes + (kSparse ? kSparseBytes : 0)];
 
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -495,9 +527,34 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
   const int last_row = min(N, q0 + kRes) - 1;
   const int n_tiles = Causal ? last_row / kT + 1 : (N + kT - 1) / kT;
   // first key tile any query of the block can see (sliding window)
-  constexpr bool kWin = Causal && Window;
+  constexpr bool kWin = Causal && Mode == kModeWindow;
   const int t_lo = kWin ? max(0, q0 - win + 1) / kT : 0;
-  const int n_it = n_tiles - t_lo;
+  // Block-sparse: the key tiles some query block of this workgroup may see,
+  // listed in LDS with one bit per 64-row query block; a wave skips the tiles
+  // hidden from its own query block.
+  uint32_t* const list = reinterpret_cast<uint32_t*>(smem + Ld::kBytes);
+  int n_it = n_tiles - t_lo;
+  if constexpr (kSparse) {
+    const int nb = (N + kT - 1) / kT, qb0 = q0 / kSparseBlock;
+    const uint8_t* m = bmask + (bh / H) * m_sb + (bh % H) * m_sh;
+    n_it = compact_tiles<kW>(list, n_tiles, [&](int jt) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int i = 0; i < kRes / kSparseBlock; ++i) {
+        const int qbk = qb0 + i;
+        if (qbk < nb && (!Causal || jt <= qbk) && m[(int64_t)qbk * nb + jt] != 0) bits |= 1u << i;
+      }
+      return bits;
+    });
+  }
+  auto tile_of = [&](int i) {
+    if constexpr (kSparse) return i < n_it ? __builtin_amdgcn_readfirstlane((int)(list[i] & 0xFFFFu)) : n_tiles;
+    else return t_lo + i;
+  };
+  auto wave_sees = [&](int i) {
+    if constexpr (kSparse) return ((list[i] >> (16 + wave / 2)) & 1u) != 0;
+    else return true;
+  };
   const bool wave_live = qw0 < N;
   const uint16_t* k_h = K + head;
   const uint16_t* v_h = V + head;
@@ -534,15 +591,15 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
 
   // ---- pass 1: D = sum_j P_ij dP_ij
   float dpart = 0.f;
-  issue(t_lo, 0);
+  issue(tile_of(0), 0);
   wait_copies();
   __syncthreads();
   for (int i = 0; i < n_it; ++i) {
-    const int it = t_lo + i, st = i & 1;
+    const int it = tile_of(i), st = i & 1;
     // the next tile, or (after the last one) the first tile again for pass 2
-    issue(i + 1 < n_it ? it + 1 : t_lo, st ^ 1);
+    issue(tile_of(i + 1 < n_it ? i + 1 : 0), st ^ 1);
     const int kt0 = it * kT;
-    if (wave_live) {
+    if (wave_live && wave_sees(i)) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const int ks0 = kt0 + 32 * kh;
@@ -562,15 +619,15 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
     NLse[(int64_t)bh * N + my_q] = -lse2;  // read by the dK/dV kernel
   }
 
-  // ---- pass 2: dQ^T += K^T dS^T; tile t_lo is already in stage n_it & 1
+  // ---- pass 2: dQ^T += K^T dS^T; the first tile is already in stage n_it & 1
   f32x16 dq[kDB];
 #pragma unroll
   for (int i = 0; i < kDB; ++i) dq[i] = f32x16{};
   for (int i = 0; i < n_it; ++i) {
-    const int it = t_lo + i, st = (i + n_it) & 1;
-    if (i + 1 < n_it) issue(it + 1, st ^ 1);
+    const int it = tile_of(i), st = (i + n_it) & 1;
+    if (i + 1 < n_it) issue(tile_of(i + 1), st ^ 1);
     const int kt0 = it * kT;
-    if (wave_live) {
+    if (wave_live && wave_sees(i)) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const int ks0 = kt0 + 32 * kh;
@@ -597,7 +654,7 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
   store_row<IsBf16, D>(dQ + (b * out.sb + h * out.sh), my_q, out.sn, g, dq, dq_mul);
 }
 
-template <bool IsBf16, int D, bool Causal, bool Window>
+template <bool IsBf16, int D, bool Causal, int Mode>
 hipError_t launch(const BwdArgs& a, hipStream_t st) {
   const int N = (int)a.N;
   const int BH = (int)(a.B * a.H);
@@ -614,15 +671,16 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
   float* dsum = static_cast<float*>(a.workspace);
   float* nlse = dsum + a.B * a.H * a.N;
   // dQ (and D into the workspace) first; dK, dV read D afterwards on the same stream
-  hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal, Window>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st, q,
+  hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal, Mode>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st, q,
                      k, v, dout, a.lse, dsum, nlse, static_cast<uint16_t*>(a.dq), N, win, (int)a.H, BH,
-                     nblk, c, a.scale, q_sign, a.in, a.out);
+                     nblk, c, a.scale, q_sign, a.in, a.out, a.block_mask, a.mask_sb, a.mask_sh);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dK = scale dS^T Q; a negative scale flips the resident K instead of Q
-  hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal, Window>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
+  hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal, Mode>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
                      q, k, v, dout, nlse, dsum, static_cast<uint16_t*>(a.dk),
-                     static_cast<uint16_t*>(a.dv), N, win, (int)a.H, BH, c, a.scale, q_sign, a.in, a.out);
+                     static_cast<uint16_t*>(a.dv), N, win, (int)a.H, BH, c, a.scale, q_sign, a.in, a.out,
+                     a.block_mask, a.mask_sb, a.mask_sh);
   return hipGetLastError();
 }
 
@@ -630,9 +688,11 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
 // and unmasked calls run code with no window arithmetic.
 template <bool IsBf16, int D>
 hipError_t dispatch_d(const BwdArgs& a, hipStream_t s) {
-  if (!a.causal) return launch<IsBf16, D, false, false>(a, s);
-  if (a.window < a.N) return launch<IsBf16, D, true, true>(a, s);
-  return launch<IsBf16, D, true, false>(a, s);
+  if (a.block_mask != nullptr)
+    return a.causal ? launch<IsBf16, D, true, kModeSparse>(a, s) : launch<IsBf16, D, false, kModeSparse>(a, s);
+  if (!a.causal) return launch<IsBf16, D, false, kModePlain>(a, s);
+  if (a.window < a.N) return launch<IsBf16, D, true, kModeWindow>(a, s);
+  return launch<IsBf16, D, true, kModePlain>(a, s);
 }
 
 template <bool IsBf16>

@@ -56,6 +56,8 @@ struct BwdArgs {
   int64_t window;  // as for FwdArgs
   Layout in;       // q, k, v, o, dout
   Layout out;      // dq, dk, dv
+  const uint8_t* block_mask;  // as for FwdArgs
+  int64_t mask_sb, mask_sh;
 };
 
 // Launchers return the hipError_t of the launch (hipSuccess when enqueued).

@@ -72,14 +72,8 @@ constexpr float kNoRef = 1e30f;
 // Masks a block of scores may need: none, the causal diagonal and the
 // sequence end, or those and the left edge of a sliding window.
 constexpr int kMaskNone = 0, kMaskEdge = 1, kMaskWindow = 2, kMaskSparse = 3;
-// Kernel modes: plain (causal or not), causal sliding window, block-sparse.
-constexpr int kModePlain = 0, kModeWindow = 1, kModeSparse = 2;
-// Block-sparse: 64 x 64 mask blocks; a workgroup's list of key tiles lives
-// in LDS after the rings (one 32-bit entry per tile: index | query-block bits
-// << 16), with room for this many tiles, plus 8 wave counts.
-constexpr int kSparseBlock = 64;
-constexpr int kMaxSparseTiles = 2048;
-constexpr int kSparseBytes = 4 * kMaxSparseTiles + 64;
+// Block-sparse: a workgroup's list of key tiles (index | query-block bits <<
+// 16, see compact_tiles) lives in LDS after the rings.
 
 // LDS row strides (bytes).  K rows carry 16 bytes of padding: the sixteen
 // lanes of a 16-byte operand read touch sixteen consecutive rows, which then
@@ -552,37 +546,18 @@ struct FwdBlock {
   // may see (the causal limit included), in order, each with one bit per
   // 64-row query block; rows of the mask past N read as hidden.
   __device__ __forceinline__ void build_tile_list(uint32_t* list, const uint8_t* mask, int q0_blk) {
-    const int tid = threadIdx.x;
     const int n_kb = (N + kBN - 1) / kBN, n_qb = (N + kSparseBlock - 1) / kSparseBlock;
     const int qb0 = q0_blk / kSparseBlock;
-    uint32_t* counts = list + kMaxSparseTiles;
-    int base = 0;
-    for (int c0 = 0; c0 < n_tiles; c0 += kThreads) {
-      const int jt = c0 + tid;
+    const int nt = n_tiles;
+    n_pos = compact_tiles<kWaves>(list, nt, [&](int jt) {
       uint32_t bits = 0;
-      if (jt < n_tiles) {
 #pragma unroll
-        for (int i = 0; i < kBM / kSparseBlock; ++i) {
-          const int qb = qb0 + i;
-          if (qb < n_qb && (!Causal || jt <= qb) && mask[(int64_t)qb * n_kb + jt] != 0) bits |= 1u << i;
-        }
+      for (int i = 0; i < kBM / kSparseBlock; ++i) {
+        const int qb = qb0 + i;
+        if (qb < n_qb && (!Causal || jt <= qb) && mask[(int64_t)qb * n_kb + jt] != 0) bits |= 1u << i;
       }
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(bits != 0);
-      const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-      if (lane == 0) counts[wave] = (uint32_t)__builtin_popcountll(bal);
-      __syncthreads();
-      int off = base, total = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const int cw = (int)counts[w];
-        off += w < wave ? cw : 0;
-        total += cw;
-      }
-      if (bits != 0) list[off + rank] = (uint32_t)jt | (bits << 16);
-      base += total;
-      __syncthreads();  // counts are rewritten by the next chunk; the list is complete
-    }
-    n_pos = __builtin_amdgcn_readfirstlane(base);
+      return bits;
+    });
   }
 
   __device__ __forceinline__ void run(int q0_blk, uint32_t* list = nullptr, const uint8_t* mask = nullptr) {

@@ -159,6 +159,45 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// Kernel modes: plain (causal or not), causal sliding window, block-sparse.
+constexpr int kModePlain = 0, kModeWindow = 1, kModeSparse = 2;
+// Block-sparse masks have blocks of 64 x 64; a workgroup's list of tiles
+// holds at most kMaxSparseTiles entries of 32 bits (tile index | bits << 16)
+// plus 16 words of per-wave counts.
+constexpr int kSparseBlock = 64;
+constexpr int kMaxSparseTiles = 2048;
+constexpr int kSparseBytes = 4 * kMaxSparseTiles + 64;
+
+// Compact, in order, the items i in [0, n) whose bits_of(i) is nonzero into
+// list[] as i | bits << 16 (bits < 2^16); every thread of the workgroup
+// (kWaves waves) calls this, and its barriers.  counts: kWaves words of LDS
+// after the list.  Returns the number of entries (wave-uniform).
+template <int kWaves, typename F>
+__device__ __forceinline__ int compact_tiles(uint32_t* list, int n, F bits_of) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t* counts = list + kMaxSparseTiles;
+  int base = 0;
+  for (int c0 = 0; c0 < n; c0 += 64 * kWaves) {
+    const int i = c0 + tid;
+    const uint32_t bits = i < n ? bits_of(i) : 0u;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(bits != 0);
+    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+    if (lane == 0) counts[wave] = (uint32_t)__builtin_popcountll(bal);
+    __syncthreads();
+    int off = base, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int cw = (int)counts[w];
+      off += w < wave ? cw : 0;
+      total += cw;
+    }
+    if (bits != 0) list[off + rank] = (uint32_t)i | (bits << 16);
+    base += total;
+    __syncthreads();  // counts are rewritten by the next chunk; the list is complete
+  }
+  return __builtin_amdgcn_readfirstlane(base);
+}
 
 }  // namespace mfma
 }  // namespace fa

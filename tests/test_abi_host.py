@@ -29,12 +29,12 @@ def test_library_exports_every_declared_symbol():
     declared = fa.declared_symbols()
     assert {"attn_fwd", "attn_bwd", "attn_fwd_window", "attn_bwd_window", "attn_bwd_workspace_bytes",
             "attn_fwd_kv_outer", "attn_fwd_kv_outer_workspace_bytes", "attn_fwd_strided",
-            "attn_bwd_strided", "attn_fwd_block_sparse", "fa_status_str",
+            "attn_bwd_strided", "attn_fwd_block_sparse", "attn_bwd_block_sparse", "fa_status_str",
             "fa_abi_version"} <= set(declared)
     lib = ctypes.CDLL(fa._binding.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
-    assert fa.lib().fa_abi_version() == 5
+    assert fa.lib().fa_abi_version() == 6
 
 
 def test_status_strings():
@@ -304,3 +304,19 @@ def test_block_sparse_validation():
     for mb, mh in ((1, 1), (2, 1), (1, 3), (2, 3)):
         assert fwd_bs(q=P[0] + 2, mb=mb, mh=mh) == FA_ERR_ALIGN
     assert fwd_bs(q=P[0] + 2, N=2048 * 64) == FA_ERR_ALIGN
+
+
+def test_block_sparse_backward_validation():
+    def bb(mask_ptr=P[7], mb=1, mh=1, **kw):
+        a = dict(q=P[0], B=2, H=3, N=200, d=64, mask=0, scale=0.125, dtype=fa.BF16, ws=1 << 20)
+        a.update(kw)
+        return fa.attn_bwd_block_sparse_raw(a["q"], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0],
+                                            a["B"], a["H"], a["N"], a["d"], mask_ptr, mb, mh, a["mask"],
+                                            a["scale"], a["dtype"], P[1], a["ws"], None)
+    assert bb(mask_ptr=None) == FA_ERR_NULL
+    assert bb(mb=3) == FA_ERR_SHAPE
+    assert bb(mh=2) == FA_ERR_SHAPE
+    assert bb(N=2048 * 64 + 1, ws=1 << 40) == FA_ERR_UNSUPPORTED
+    assert bb(dtype=fa.F32) == FA_ERR_UNSUPPORTED
+    assert bb(ws=8) == FA_ERR_WORKSPACE
+    assert bb(q=P[0] + 2, mb=2, mh=3) == FA_ERR_ALIGN   # accepted shapes reach the pointer checks

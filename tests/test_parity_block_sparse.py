@@ -118,3 +118,29 @@ def test_block_sparse_bench_workload_sampled_rows(fa):
                                      np.random.default_rng(9800).integers(0, w.N, 40)]))
     log(f"case block-sparse bench workload {w.name}")
     run_case(fa, x, "bf16", w.causal, mask, rows=rows)
+
+
+def bwd_case(fa, x, dtype, causal, mask):
+    q, k, v, do = (torch.from_numpy(x[n]).to("cuda").to(TORCH_DT[dtype]).contiguous()
+                   for n in ("q", "k", "v", "do"))
+    bm = torch.from_numpy(np.ascontiguousarray(mask)).to("cuda")
+    o, lse = fa.attn_fwd(q, k, v, causal=causal, block_mask=bm)
+    dq, dk, dv = fa.attn_bwd(q, k, v, o, lse, do, causal=causal, block_mask=bm)
+    torch.cuda.synchronize()
+    rq, rk, rv, _, _ = oracle.dense_bwd(x["q"], x["k"], x["v"], x["do"], causal=causal, block_mask=mask)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        compare(name, g.float().cpu().numpy(), r, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_backward_sweep(fa, dtype, d, causal):
+    cases = [(1, (1, 1), 0.5), (65, (2, 1), 0.6), (300, (1, 3), 0.4), (777, (1, 2), 0.3)]
+    for i, (n, (b, h), dens) in enumerate(cases):
+        seed = 9900 + n + d + int(causal)
+        mb, mh = (1 if i % 2 else b), (h if i % 3 else 1)
+        log(f"case block-sparse bwd dtype={dtype} d={d} causal={causal} B,H={b, h} N={n} "
+            f"mask {mb}x{mh} density={dens} seed={seed}")
+        x = workloads.random_inputs(b, h, n, d, dtype, seed, with_do=True)
+        bwd_case(fa, x, dtype, causal, random_mask(mb, mh, n, dens, seed + 1, empty_row=(i == 2)))
