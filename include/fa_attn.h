@@ -57,7 +57,7 @@ enum fa_status {
   FA_ERR_DTYPE = 3,       /* dtype is not one of enum fa_dtype                  */
   FA_ERR_MASK = 4,        /* mask is not one of enum fa_mask                    */
   FA_ERR_SCALE = 5,       /* scale is NaN or infinite                           */
-  FA_ERR_UNSUPPORTED = 6, /* head dimension d is not 64 or 128 (or fp32 backward) */
+  FA_ERR_UNSUPPORTED = 6, /* head dimension d is not 64, 96 or 128 (or fp32 backward) */
   FA_ERR_WORKSPACE = 7,   /* backward workspace missing or too small            */
   FA_ERR_HIP = 8,         /* the HIP runtime rejected a launch                  */
   FA_ERR_ALIGN = 9,       /* a tensor pointer is not 16-byte aligned            */
@@ -79,7 +79,7 @@ enum fa_status {
  *            separate quantities").  May be NULL, in which case it is not
  *            written.
  *   B, H, N  batch, heads, sequence length (queries and keys), each >= 1.
- *   d        head dimension of q, k and v: 64 or 128.
+ *   d        head dimension of q, k and v: 64, 96 or 128.
  *   mask     enum fa_mask.
  *   scale    finite multiplier of the raw dot products (any sign; usually
  *            1/sqrt(d)).

@@ -29,7 +29,7 @@ int check_common(int64_t B, int64_t H, int64_t N, int64_t d, int mask, float sca
   const int64_t bh = B * H;
   if (bh > INT64_MAX / N || bh * N > INT64_MAX / 128 / 4) return FA_ERR_SHAPE;
   if (((N + 63) / 64) * bh > kMaxGrid) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
   // one head of a dense [N][d] array must span less than 2 GiB (one buffer resource)
   if (N * d * (dtype == FA_F32 ? 4 : 2) > INT32_MAX - 1024) return FA_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
@@ -271,7 +271,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_MASK: return "unknown mask";
     case FA_ERR_SCALE: return "scale is not finite";
-    case FA_ERR_UNSUPPORTED: return "unsupported: head dimension must be 64 or 128 (backward: fp16/bf16 only)";
+    case FA_ERR_UNSUPPORTED: return "unsupported: head dimension must be 64, 96 or 128 (backward: fp16/bf16 only)";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "the HIP runtime rejected a launch";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";

@@ -63,13 +63,17 @@ __device__ __forceinline__ int tile_row(int idx) {
 // one chunk of 16 consecutive rows (row operands), and 32 lanes reading 64
 // contiguous bytes of 4 consecutive rows (transpose reads).
 template <int D> struct STile {
-  static constexpr int kRowBytes = 2 * D;
+  // LDS row pitch and the data of a row: d = 96 rows (12 chunks) sit in rows
+  // of 16 chunks, so the 16-chunk swizzle of d = 128 applies; their last four
+  // chunks are filled from past the row's data and never read.
+  static constexpr int kDataBytes = 2 * D;
+  static constexpr int kRowBytes = D == 96 ? 256 : 2 * D;
   static constexpr int kBytes = kT * kRowBytes;
   static constexpr int kCopies = kBytes / 1024;  // wave-wide 1 KB copies per tile
   static constexpr int kPerWave = kCopies / kW;
   static_assert(kPerWave * kW == kCopies, "tile copies split evenly over the waves");
   static __device__ __forceinline__ int swz(int r) {
-    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    return D != 64 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
   }
   // byte offset in the tile of 16-byte chunk c of LDS row r
   static __device__ __forceinline__ int at(int r, int c) { return r * kRowBytes + 16 * (c ^ swz(r)); }
@@ -113,7 +117,7 @@ __device__ __forceinline__ void copy_tile(uint32_t lds_addr, const uint16_t* bas
   using T = STile<D>;
   const int left = rows - row0;
   const i32x4 rs = make_rsrc(base + (int64_t)row0 * sn,
-                             left > 0 ? (uint32_t)(left - 1) * (uint32_t)(2 * sn) + (uint32_t)T::kRowBytes : 0u);
+                             left > 0 ? (uint32_t)(left - 1) * (uint32_t)(2 * sn) + (uint32_t)T::kDataBytes : 0u);
 #pragma unroll
   for (int i = 0; i < T::kPerWave; ++i) dma16(rs, lds_addr + (uint32_t)((wave + kW * i) * 1024), src[i]);
 }
@@ -697,7 +701,8 @@ hipError_t dispatch_d(const BwdArgs& a, hipStream_t s) {
 
 template <bool IsBf16>
 hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
-  return a.d == 128 ? dispatch_d<IsBf16, 128>(a, s) : dispatch_d<IsBf16, 64>(a, s);
+  if (a.d == 128) return dispatch_d<IsBf16, 128>(a, s);
+  return a.d == 96 ? dispatch_d<IsBf16, 96>(a, s) : dispatch_d<IsBf16, 64>(a, s);
 }
 
 }  // namespace

@@ -149,6 +149,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
   if (a.d == 128) return a.causal ? launch<128, true>(a, s) : launch<128, false>(a, s);
+  if (a.d == 96) return a.causal ? launch<96, true>(a, s) : launch<96, false>(a, s);
   return a.causal ? launch<64, true>(a, s) : launch<64, false>(a, s);
 }
 

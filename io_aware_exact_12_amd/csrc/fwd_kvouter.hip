@@ -255,6 +255,7 @@ hipError_t launch(const FwdArgs& a, void* ws, hipStream_t stream) {
 template <bool IsBf16>
 hipError_t dispatch(const FwdArgs& a, void* ws, hipStream_t s) {
   if (a.d == 128) return a.causal ? launch<IsBf16, 128, true>(a, ws, s) : launch<IsBf16, 128, false>(a, ws, s);
+  if (a.d == 96) return a.causal ? launch<IsBf16, 96, true>(a, ws, s) : launch<IsBf16, 96, false>(a, ws, s);
   return a.causal ? launch<IsBf16, 64, true>(a, ws, s) : launch<IsBf16, 64, false>(a, ws, s);
 }
 

@@ -82,10 +82,12 @@ constexpr int kMaskNone = 0, kMaskEdge = 1, kMaskWindow = 2, kMaskSparse = 3;
 // contiguous bytes per 16-lane group; a 64-byte pad puts those four rows in
 // four disjoint 16-bank ranges.  One extra 1 KB slot at the end absorbs the
 // copies of waves that have no real chunk for their last copy slot.
+// d = 96 takes the strides of d = 128: they keep both reads conflict-free and
+// split each stage into whole 1 KB copies that the waves share evenly.
 template <int D> struct Lds {
   static constexpr int kRowBytes = 2 * D;
-  static constexpr int kKStride = kRowBytes + 16;
-  static constexpr int kVStride = kRowBytes + 64;
+  static constexpr int kKStride = (D == 96 ? 256 : kRowBytes) + 16;
+  static constexpr int kVStride = (D == 96 ? 256 : kRowBytes) + 64;
   static constexpr int kKStage = kBN * kKStride;  // multiple of 1 KB
   static constexpr int kVStage = kBN * kVStride;  // multiple of 1 KB
   static constexpr int kSink = kStages * (kKStage + kVStage);
@@ -369,12 +371,13 @@ struct FwdBlock {
   }
 
   // MFMA slot of step st (0 scale, 1 exp2, 2 pack and partial sum) of score
-  // pair e, for blocks of 16, 8 or 4 MFMA slots.  Steps that land in the same
-  // slot run in program order.
+  // pair e, for blocks of 16, 12 (d = 96), 8, 6 or 4 MFMA slots.  Steps that
+  // land in the same slot run in program order.
   template <int kSlots>
   static constexpr int slot_of(int e, int st) {
     return kSlots == 16 ? e + (st == 0 ? 0 : st == 1 ? 2 : 5)
-         : kSlots == 8  ? e / 2 + st
+         : kSlots == 12 ? (3 * e) / 4 + (st == 0 ? 0 : st == 1 ? 2 : 4)
+         : (kSlots == 8 || kSlots == 6) ? e / 2 + st
                         : (e / 4 + st < 3 ? e / 4 + st : 3);
   }
 
@@ -399,9 +402,10 @@ struct FwdBlock {
   // issue priority (see step()).
   template <int kMask, bool kFirst = false, int kHalf = 0>
   __device__ __forceinline__ void block(int u) {
-    static_assert(kPV == kKs, "as many PV as score MFMAs per block (d = 64 or 128)");
+    static_assert(kPV == kKs, "as many PV as score MFMAs per block (d = 64, 96 or 128)");
     constexpr int kMfmas = (kFirst ? 0 : kPV) + kKs;
-    static_assert(kMfmas == 16 || kMfmas == 8 || kMfmas == 4, "slot schedules exist for 4, 8, 16 MFMAs");
+    static_assert(kMfmas == 16 || kMfmas == 12 || kMfmas == 8 || kMfmas == 6 || kMfmas == 4,
+                  "slot schedules exist for 4, 6, 8, 12 and 16 MFMAs");
     auto slot = [](int e, int st) { return slot_of<kMfmas>(e, st); };
     // K operand of block u+1: K tile (u+1)/2, half (u+1)&1
     const uint8_t* kt = k_stage(((u + 1) >> 1) & 3) + k_base + ((u + 1) & 1) * 32 * L::kKStride;
@@ -683,7 +687,8 @@ hipError_t dispatch_d(const FwdArgs& a, hipStream_t s) {
 
 template <bool IsBf16>
 hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
-  return a.d == 128 ? dispatch_d<IsBf16, 128>(a, s) : dispatch_d<IsBf16, 64>(a, s);
+  if (a.d == 128) return dispatch_d<IsBf16, 128>(a, s);
+  return a.d == 96 ? dispatch_d<IsBf16, 96>(a, s) : dispatch_d<IsBf16, 64>(a, s);
 }
 
 }  // namespace

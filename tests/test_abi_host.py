@@ -54,7 +54,7 @@ def test_bad_shapes(kw):
     assert fwd(**kw) == FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("d", [1, 32, 96, 127, 256])
+@pytest.mark.parametrize("d", [1, 32, 80, 127, 256])
 def test_unsupported_head_dim(d):
     assert fwd(d=d) == FA_ERR_UNSUPPORTED
 
@@ -122,7 +122,7 @@ def test_bwd_null_pointers(which):
 
 
 @pytest.mark.parametrize("kw,status", [(dict(B=0), FA_ERR_SHAPE), (dict(N=-1), FA_ERR_SHAPE),
-                                       (dict(d=96), FA_ERR_UNSUPPORTED), (dict(dtype=7), FA_ERR_DTYPE),
+                                       (dict(d=80), FA_ERR_UNSUPPORTED), (dict(dtype=7), FA_ERR_DTYPE),
                                        (dict(mask=3), FA_ERR_MASK), (dict(scale=math.nan), FA_ERR_SCALE),
                                        (dict(dtype=fa.F32), FA_ERR_UNSUPPORTED),
                                        (dict(ws=None), FA_ERR_WORKSPACE),
@@ -135,7 +135,8 @@ def test_bwd_validation(kw, status):
 def test_bwd_workspace_query():
     assert fa.bwd_workspace_bytes(4, 16, 4096, 128, fa.BF16) == 8 * 4 * 16 * 4096
     assert fa.bwd_workspace_bytes(0, 16, 4096, 128, fa.BF16) == 0
-    assert fa.bwd_workspace_bytes(1, 1, 16, 96, fa.BF16) == 0
+    assert fa.bwd_workspace_bytes(1, 1, 16, 80, fa.BF16) == 0
+    assert fa.bwd_workspace_bytes(1, 1, 16, 96, fa.BF16) == 8 * 16
 
 
 # ---------------------------------------------------------------- sliding window
@@ -162,7 +163,7 @@ def test_window_below_one_rejected(window):
 def test_window_checks_like_the_plain_calls():
     assert fwd_w(4, q=None) == FA_ERR_NULL
     assert fwd_w(4, N=0) == FA_ERR_SHAPE
-    assert fwd_w(4, d=96) == FA_ERR_UNSUPPORTED
+    assert fwd_w(4, d=80) == FA_ERR_UNSUPPORTED
     assert fwd_w(4, dtype=7) == FA_ERR_DTYPE
     assert fwd_w(4, scale=math.inf) == FA_ERR_SCALE
     assert fwd_w(4, q=P[0] + 8) == FA_ERR_ALIGN
@@ -185,7 +186,7 @@ def test_kv_outer_workspace_query():
     assert fa.kv_outer_workspace_bytes(1, 16, 8192, 128, fa.BF16) == (4 * 128 + 8) * 16 * 8192
     assert fa.kv_outer_workspace_bytes(2, 3, 5, 64, fa.F16) == (4 * 64 + 8) * 30
     assert fa.kv_outer_workspace_bytes(1, 1, 16, 64, fa.F32) == 0
-    assert fa.kv_outer_workspace_bytes(1, 1, 16, 96, fa.BF16) == 0
+    assert fa.kv_outer_workspace_bytes(1, 1, 16, 80, fa.BF16) == 0
     assert fa.kv_outer_workspace_bytes(0, 1, 16, 64, fa.BF16) == 0
 
 
@@ -193,7 +194,7 @@ def test_kv_outer_validation():
     assert kvo(q=None) == FA_ERR_NULL
     assert kvo(o=None) == FA_ERR_NULL
     assert kvo(N=0) == FA_ERR_SHAPE
-    assert kvo(d=96) == FA_ERR_UNSUPPORTED
+    assert kvo(d=80) == FA_ERR_UNSUPPORTED
     assert kvo(dtype=fa.F32) == FA_ERR_UNSUPPORTED
     assert kvo(dtype=9) == FA_ERR_DTYPE
     assert kvo(mask=3) == FA_ERR_MASK
@@ -297,7 +298,7 @@ def test_block_sparse_validation():
     assert fwd_bs(mb=3) == FA_ERR_SHAPE      # neither 1 nor B
     assert fwd_bs(mh=2) == FA_ERR_SHAPE      # neither 1 nor H
     assert fwd_bs(N=2048 * 64 + 1) == FA_ERR_UNSUPPORTED   # more key tiles than the list holds
-    assert fwd_bs(d=96) == FA_ERR_UNSUPPORTED
+    assert fwd_bs(d=80) == FA_ERR_UNSUPPORTED
     assert fwd_bs(dtype=5) == FA_ERR_DTYPE
     assert fwd_bs(mask=2) == FA_ERR_MASK
     # accepted shapes reach the pointer checks (no launch here)

@@ -72,7 +72,7 @@ def random_mask(b, h, n, density, seed, empty_row=False):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_block_sparse_sweep(fa, dtype, d, causal):
     cases = [(1, (1, 1), 0.5), (64, (1, 2), 0.5), (65, (2, 1), 0.6), (300, (1, 3), 0.4),
@@ -133,7 +133,7 @@ def bwd_case(fa, x, dtype, causal, mask):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_block_sparse_backward_sweep(fa, dtype, d, causal):
     cases = [(1, (1, 1), 0.5), (65, (2, 1), 0.6), (300, (1, 3), 0.4), (777, (1, 2), 0.3)]

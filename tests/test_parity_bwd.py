@@ -81,7 +81,7 @@ def test_fwd_bwd_causal_workload_sampled_heads(fa):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_sweep(fa, dtype, d, causal):
     for i, n in enumerate([1, 15, 64, 65, 127, 128, 129, 300, 777]):

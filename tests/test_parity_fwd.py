@@ -116,7 +116,7 @@ SWEEP_N = [1, 2, 15, 63, 64, 65, 127, 128, 129, 200, 1000]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_sweep(fa, dtype, d, causal):
     for i, n in enumerate(SWEEP_N):

@@ -63,7 +63,7 @@ def run_case(fa, x, dtype, causal, scale=None, rows=None):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_kv_outer_sweep(fa, dtype, d, causal):
     for i, n in enumerate([1, 31, 64, 65, 257, 300, 777]):

@@ -59,7 +59,7 @@ def host(t):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bshd_forward(fa, dtype, d, causal):
     for n, (b, h) in [(1, (1, 3)), (65, (2, 3)), (300, (1, 4)), (777, (2, 2))]:
@@ -92,7 +92,7 @@ def test_packed_qkv_forward(fa, dtype):
     compare("LSE", lse.cpu().numpy(), rl, "lse")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 def test_multi_query_forward(fa, d):
     """One k and one v head shared by all query heads (head stride 0)."""
     b, h, n = 2, 4, 300
@@ -130,7 +130,7 @@ def test_dense_strides_match_the_plain_call_bitwise(fa):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bshd_backward(fa, dtype, d, causal):
     for n, (b, h) in [(1, (1, 2)), (65, (2, 2)), (300, (1, 3)), (777, (1, 2))]:

@@ -64,7 +64,7 @@ def fwd_case(fa, x, dtype, w, rows=None):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 def test_window_fwd_sweep(fa, dtype, d):
     for i, (n, w) in enumerate([(1, 1), (31, 1), (64, 17), (257, 32), (257, 33), (600, 64),
                                 (600, 65), (1000, 100), (1000, 256), (777, 300), (300, 299), (300, 300),
@@ -131,7 +131,7 @@ def bwd_case(fa, x, dtype, w):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 def test_window_bwd_sweep(fa, dtype, d):
     for i, (n, w) in enumerate([(1, 1), (65, 1), (65, 33), (300, 64), (300, 100), (777, 129),
                                 (777, 300), (500, 500)]):
