@@ -207,6 +207,20 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
                      void* stream);
 
 /*
+ * attn_fwd_dv -- forward pass with values of another width than the keys.
+ *
+ * As attn_fwd, except that v and o are dense [B][H][N][dv] arrays while q and
+ * k are [B][H][N][d]: the pages define V as N x d_v ("Flash Attention:
+ * IO-Aware Exact Attention", section "Why intermediate matrices cost memory
+ * traffic"), and the scores only need q and k to share d.  Supported
+ * (d, dv): (128, 64), (64, 128), and dv == d (the attn_fwd kernels);
+ * FA_ERR_UNSUPPORTED for other pairs, FA_ERR_SHAPE for dv < 1.
+ */
+int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse,
+                int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
+                int mask, float scale, int dtype, void* stream);
+
+/*
  * attn_fwd_block_sparse -- forward pass with a block-sparse mask.
  *
  * As attn_fwd, except that key j is visible to query i only if the mask

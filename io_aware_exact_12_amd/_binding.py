@@ -54,6 +54,9 @@ def lib():
         L.attn_bwd_strided.restype = ctypes.c_int
         L.attn_bwd_strided.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64p, i64p, ctypes.c_int,
                                                   ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp]
+        L.attn_fwd_dv.restype = ctypes.c_int
+        L.attn_fwd_dv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                  ctypes.c_float, ctypes.c_int, vp]
         L.attn_fwd_block_sparse.restype = ctypes.c_int
         L.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i64, i64,
                                             ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
@@ -131,6 +134,10 @@ def attn_bwd_strided_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, in_st, g
                                   _strides(grad_st), mask, scale, dtype, ws, ws_bytes, stream)
 
 
+def attn_fwd_dv_raw(q, k, v, o, lse, B, H, N, d, dv, mask, scale, dtype, stream):
+    return lib().attn_fwd_dv(q, k, v, o, lse, B, H, N, d, dv, mask, scale, dtype, stream)
+
+
 def attn_fwd_block_sparse_raw(q, k, v, o, lse, B, H, N, d, block_mask, mask_batches, mask_heads,
                               mask, scale, dtype, stream):
     return lib().attn_fwd_block_sparse(q, k, v, o, lse, B, H, N, d, block_mask, mask_batches,
@@ -191,22 +198,37 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=N
     Work is enqueued on ``stream`` (default: torch's current stream).
     """
     import torch
-    if q.shape != k.shape or q.shape != v.shape or q.dim() != 4:
-        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {q.shape}, {k.shape}, {v.shape}")
+    if q.shape != k.shape or q.shape[:3] != v.shape[:3] or q.dim() != 4 or v.dim() != 4:
+        raise ValueError(f"q, k must share one [B, H, N, d] shape and v be [B, H, N, dv], "
+                         f"got {q.shape}, {k.shape}, {v.shape}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
     for t in (q, k, v):
         if not t.is_cuda or t.stride(-1) != 1:
             raise ValueError("q, k, v must be device tensors with a contiguous last axis")
     B, H, N, d = q.shape
+    dv = v.shape[-1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(q) if dv == d else torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    if dv != d:
+        # values of another width (v, o: [B, H, N, dv], all contiguous)
+        if window is not None or block_mask is not None:
+            raise ValueError("dv != d takes no window or block mask")
+        if not all(t.is_contiguous() for t in (q, k, v, out)) or tuple(out.shape) != (B, H, N, dv):
+            raise ValueError("dv != d takes contiguous q, k, v and a contiguous [B, H, N, dv] out")
+        st = attn_fwd_dv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr() if return_lse else None, B, H, N, d, dv,
+                             MASK_CAUSAL if causal else MASK_NONE, float(scale), _torch_dtype_code(q),
+                             stream.cuda_stream)
+        if st != 0:
+            raise FaError(st, "attn_fwd_dv")
+        return out, (lse if return_lse else None)
     if block_mask is not None:
         bm = block_mask
         _check_block_mask(bm, B, H, N)

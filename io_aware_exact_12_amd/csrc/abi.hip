@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 // Block-sparse: mask blocks of 64 x 64; a query block of the forward lists at
 // most this many key tiles (its LDS list).
 constexpr int64_t kMaxSparseTiles = 2048;
@@ -76,7 +76,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
              int64_t N, int64_t d, int mask, int64_t window, float scale, int dtype, void* stream,
              const int64_t* q_st = nullptr, const int64_t* kv_st = nullptr,
              const int64_t* out_st = nullptr, const uint8_t* block_mask = nullptr,
-             int64_t mask_b = 0, int64_t mask_h = 0) {
+             int64_t mask_b = 0, int64_t mask_h = 0, int64_t dv = 0) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_NULL;
@@ -84,6 +84,12 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (st != FA_OK) return st;
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, mask == FA_MASK_CAUSAL, scale, window < N ? window : N,
                 fa::dense_layout(H, N, d), fa::dense_layout(H, N, d), fa::dense_layout(H, N, d)};
+  a.dv = d;
+  if (dv != 0 && dv != d) {  // v and o rows of dv elements, dense
+    if (!((d == 128 && dv == 64) || (d == 64 && dv == 128))) return FA_ERR_UNSUPPORTED;
+    a.dv = dv;
+    a.out = fa::dense_layout(H, N, dv);
+  }
   if (q_st != nullptr || kv_st != nullptr || out_st != nullptr) {
     int e1 = check_layout(q_st, B, H, N, d, dtype, false, &a.lq);
     if (e1 == FA_OK) e1 = check_layout(kv_st, B, H, N, d, dtype, false, &a.in);
@@ -98,6 +104,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.mask_sh = mask_h == 1 ? 0 : nb * nb;
     a.mask_sb = mask_b == 1 ? 0 : mask_h * nb * nb;
   }
+  a.lv = a.dv == d ? a.in : fa::dense_layout(H, N, a.dv);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
     return FA_ERR_ALIGN;
@@ -170,6 +177,8 @@ int kv_outer_impl(const void* q, const void* k, const void* v, void* o, float* l
     return FA_ERR_ALIGN;
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, mask == FA_MASK_CAUSAL, scale, N,
                 fa::dense_layout(H, N, d), fa::dense_layout(H, N, d), fa::dense_layout(H, N, d)};
+  a.dv = d;
+  a.lv = a.in;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_kv_outer_bf16(a, workspace, s)
                                         : fa::launch_fwd_kv_outer_f16(a, workspace, s);
@@ -230,6 +239,16 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
   if (in_strides == nullptr || grad_strides == nullptr) return FA_ERR_NULL;
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, N, scale, dtype, workspace,
                   workspace_bytes, stream, in_strides, grad_strides);
+}
+
+int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                int64_t H, int64_t N, int64_t d, int64_t dv, int mask, float scale, int dtype,
+                void* stream) {
+  if (dv < 1) return FA_ERR_SHAPE;
+  if (dv != 64 && dv != 96 && dv != 128) return FA_ERR_UNSUPPORTED;
+  if (N > 0 && N * dv * (dtype == FA_F32 ? 4 : 2) > INT32_MAX - 1024) return FA_ERR_SHAPE;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, mask, N, scale, dtype, stream, nullptr, nullptr,
+                  nullptr, nullptr, 0, 0, dv);
 }
 
 int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,

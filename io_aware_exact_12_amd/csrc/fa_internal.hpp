@@ -35,6 +35,9 @@ struct FwdArgs {
   // with element strides mask_sb, mask_sh (0 broadcasts over batch or head)
   const uint8_t* block_mask;
   int64_t mask_sb, mask_sh;
+  // width of v and o rows (d_v; equal to d except in the d_v != d call) and v's layout
+  int64_t dv;
+  Layout lv;
 };
 
 // Arguments of one backward launch after validation.  workspace holds at

@@ -24,20 +24,20 @@ namespace {
 constexpr int kRows = 64;   // query rows per workgroup (one wave, one row per lane)
 constexpr int kKeys = 16;   // keys per LDS tile
 
-template <int D, bool Causal>
+template <int D, int DV, bool Causal>
 __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict__ Q,
                                                          const float* __restrict__ K,
                                                          const float* __restrict__ V,
                                                          float* __restrict__ O,
                                                          float* __restrict__ LSE, int N,
                                                          int win, int H, int n_qblocks, float scale,
-                                                         Layout lq, Layout in, Layout out,
+                                                         Layout lq, Layout in, Layout lv, Layout out,
                                                          const uint8_t* __restrict__ bmask,
                                                          int64_t m_sb, int64_t m_sh) {
   constexpr int kQStride = D + 1;  // odd stride: lanes reading their own row hit distinct banks
   __shared__ float qs[kRows * kQStride];
   __shared__ __attribute__((aligned(16))) float ks[kKeys * D];
-  __shared__ __attribute__((aligned(16))) float vs[kKeys * D];
+  __shared__ __attribute__((aligned(16))) float vs[kKeys * DV];
 
   const int lane = threadIdx.x;
   const int bh = blockIdx.x / n_qblocks;
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   const int64_t sn = in.sn;
   const float* Qh = Q + (b * lq.sb + h * lq.sh);
   const float* Kh = K + head_off;
-  const float* Vh = V + head_off;
+  const float* Vh = V + (b * lv.sb + h * lv.sh);
 
   for (int idx = lane; idx < kRows * D; idx += kRows) {
     const int r = idx / D, col = idx % D;
@@ -65,9 +65,9 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   // first key any row of the block can see (sliding window; 0 without one)
   const int key_lo = Causal ? max(0, q0 - win + 1) / kKeys * kKeys : 0;
 
-  float acc[D];
+  float acc[DV];
 #pragma unroll
-  for (int i = 0; i < D; ++i) acc[i] = 0.f;
+  for (int i = 0; i < DV; ++i) acc[i] = 0.f;
   double m_run = -INFINITY, l_run = 0.0;
   const double dscale = (double)scale;
 
@@ -78,10 +78,14 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
       const bool ok = key0 + r < N;
       const float4 kv = ok ? *reinterpret_cast<const float4*>(Kh + (int64_t)(key0 + r) * sn + col)
                            : float4{0.f, 0.f, 0.f, 0.f};
-      const float4 vv = ok ? *reinterpret_cast<const float4*>(Vh + (int64_t)(key0 + r) * sn + col)
-                           : float4{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<float4*>(ks + r * D + col) = kv;
-      *reinterpret_cast<float4*>(vs + r * D + col) = vv;
+    }
+    for (int idx = lane; idx < kKeys * DV / 4; idx += kRows) {
+      const int r = (idx * 4) / DV, col = (idx * 4) % DV;
+      const bool ok = key0 + r < N;
+      const float4 vv = ok ? *reinterpret_cast<const float4*>(Vh + (int64_t)(key0 + r) * lv.sn + col)
+                           : float4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<float4*>(vs + r * DV + col) = vv;
     }
     __syncthreads();
 
@@ -115,10 +119,10 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
     l_run = (double)alpha * l_run + psum;
     m_run = m_new;
 #pragma unroll
-    for (int col = 0; col < D; ++col) {
+    for (int col = 0; col < DV; ++col) {
       float a = alpha * acc[col];
 #pragma unroll
-      for (int j = 0; j < kKeys; ++j) a = __builtin_fmaf(p[j], vs[j * D + col], a);
+      for (int j = 0; j < kKeys; ++j) a = __builtin_fmaf(p[j], vs[j * DV + col], a);
       acc[col] = a;
     }
   }
@@ -127,20 +131,20 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
     float* orow = O + (b * out.sb + h * out.sh) + (int64_t)my_q * out.sn;
 #pragma unroll
     // a row that saw no key (block-sparse) stores O = 0 and LSE = -inf
-    for (int col = 0; col < D; ++col) orow[col] = l_run > 0.0 ? (float)((double)acc[col] / l_run) : 0.f;
+    for (int col = 0; col < DV; ++col) orow[col] = l_run > 0.0 ? (float)((double)acc[col] / l_run) : 0.f;
     if (LSE != nullptr) LSE[(int64_t)bh * N + my_q] = (float)(m_run + log(l_run));
   }
 }
 
-template <int D, bool Causal>
+template <int D, bool Causal, int DV = D>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int N = (int)a.N;
   const int n_qblocks = (N + kRows - 1) / kRows;
   const dim3 grid((unsigned)(n_qblocks * a.B * a.H));
-  hipLaunchKernelGGL((fwd_f32_kernel<D, Causal>), grid, dim3(kRows), 0, stream,
+  hipLaunchKernelGGL((fwd_f32_kernel<D, DV, Causal>), grid, dim3(kRows), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, N,
-                     (int)(a.window < a.N ? a.window : a.N), (int)a.H, n_qblocks, a.scale, a.lq, a.in, a.out,
+                     (int)(a.window < a.N ? a.window : a.N), (int)a.H, n_qblocks, a.scale, a.lq, a.in, a.lv, a.out,
                      a.block_mask, a.mask_sb, a.mask_sh);
   return hipGetLastError();
 }
@@ -148,6 +152,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
+  if (a.dv == 64 && a.d == 128) return a.causal ? launch<128, true, 64>(a, s) : launch<128, false, 64>(a, s);
+  if (a.dv == 128 && a.d == 64) return a.causal ? launch<64, true, 128>(a, s) : launch<64, false, 128>(a, s);
   if (a.d == 128) return a.causal ? launch<128, true>(a, s) : launch<128, false>(a, s);
   if (a.d == 96) return a.causal ? launch<96, true>(a, s) : launch<96, false>(a, s);
   return a.causal ? launch<64, true>(a, s) : launch<64, false>(a, s);

@@ -84,10 +84,13 @@ constexpr int kMaskNone = 0, kMaskEdge = 1, kMaskWindow = 2, kMaskSparse = 3;
 // copies of waves that have no real chunk for their last copy slot.
 // d = 96 takes the strides of d = 128: they keep both reads conflict-free and
 // split each stage into whole 1 KB copies that the waves share evenly.
-template <int D> struct Lds {
-  static constexpr int kRowBytes = 2 * D;
+// DV is the width of V (and O) rows; it differs from D only in the d_v != d
+// launches.
+template <int D, int DV = D> struct Lds {
+  static constexpr int kRowBytes = 2 * D;    // a K (and Q) row
+  static constexpr int kVRowBytes = 2 * DV;  // a V (and O) row
   static constexpr int kKStride = (D == 96 ? 256 : kRowBytes) + 16;
-  static constexpr int kVStride = (D == 96 ? 256 : kRowBytes) + 64;
+  static constexpr int kVStride = (DV == 96 ? 256 : kVRowBytes) + 64;
   static constexpr int kKStage = kBN * kKStride;  // multiple of 1 KB
   static constexpr int kVStage = kBN * kVStride;  // multiple of 1 KB
   static constexpr int kSink = kStages * (kKStage + kVStage);
@@ -102,17 +105,17 @@ template <int D> struct Lds {
 // sequence: key j is visible to query i iff i - win < j <= i.  Mode
 // kModeSparse adds a block-sparse mask: key j is visible to query i iff the
 // mask byte of (query block i / 64, key block j / 64) is nonzero.
-template <bool IsBf16, int D, bool Causal, int Mode>
+template <bool IsBf16, int D, bool Causal, int Mode, int DV = D>
 struct FwdBlock {
   static constexpr bool kWin = Causal && Mode == kModeWindow;
   static constexpr bool kSparse = Mode == kModeSparse;
   static_assert(kBN == kSparseBlock && kBM % kSparseBlock == 0, "mask blocks are key tiles");
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
-  using L = Lds<D>;
-  static constexpr int kKs = D / 16;  // score MFMAs of one 32x32 block (k-steps over d)
-  static constexpr int kDB = D / 32;  // 32-row blocks of O^T
-  static constexpr int kPV = 2 * kDB; // PV MFMAs of one 32-key block
+  using L = Lds<D, DV>;
+  static constexpr int kKs = D / 16;   // score MFMAs of one 32x32 block (k-steps over d)
+  static constexpr int kDB = DV / 32;  // 32-row blocks of O^T
+  static constexpr int kPV = 2 * kDB;  // PV MFMAs of one 32-key block
   static constexpr int kRowBytes = L::kRowBytes;
   // HBM -> LDS copies: a K tile is kKLoads and a V tile kVLoads wave-wide
   // 1 KB copies.  Wave w copies K chunks w + 8 i and V chunks w + 8 i of the
@@ -125,13 +128,15 @@ struct FwdBlock {
   static constexpr int kRemK = kKLoads % kWaves, kRemV = kVLoads % kWaves;
   static_assert(kRemK + kRemV <= kWaves, "one extra copy per wave covers the remainders");
   static constexpr int kCopies = kFullK + kFullV + 1;  // copies per wave per tile step
+  static_assert(kFullK >= 1 && kFullK <= 2 && kFullV >= 1 && kFullV <= 2, "copy groups of 3 to 5");
   static constexpr uint32_t kNoData = 0x80000000u;    // past any buffer end: reads as zero
 
   uint8_t* smem;  // K stages 0..kStages-1, then V stages, then the sink slot
   const uint8_t* k_ptr;  // K and V of this head (wave-uniform)
   const uint8_t* v_ptr;
-  uint32_t head_bytes;   // extent of one head's rows in q, k, v: (N - 1) rows + one row of data
-  uint32_t row_bytes;    // distance of consecutive rows of q, k, v
+  uint32_t head_bytes;   // extent of one head's rows in k: (N - 1) rows + one row of data
+  uint32_t row_bytes;    // distance of consecutive rows of k
+  uint32_t v_head_bytes, v_row_bytes;  // the same for v
   int64_t o_off;         // this head's first output element, and the output row stride
   int64_t o_sn;
   int N, win, wave, lane, l32, g, q0, my_q, n_tiles, n_sub;
@@ -167,14 +172,15 @@ struct FwdBlock {
     const int stride = is_v ? L::kVStride : L::kKStride;
     const int byte = ci * 1024 + lane * 16;
     const int row = byte / stride, col = byte % stride;
-    if (col >= kRowBytes) return kNoData;  // row padding
-    return (uint32_t)(is_v ? row : k_row_key(row)) * row_bytes + (uint32_t)col;
+    if (col >= (is_v ? L::kVRowBytes : kRowBytes)) return kNoData;  // row padding
+    return is_v ? (uint32_t)row * v_row_bytes + (uint32_t)col
+                : (uint32_t)k_row_key(row) * row_bytes + (uint32_t)col;
   }
 
   __device__ __forceinline__ void init(uint8_t* lds, const uint16_t* Q, const uint16_t* K,
                                        const uint16_t* V, int N_, int win_, int H, int bh, int qb,
                                        float c_, uint32_t q_sign, const Layout& lq, const Layout& in,
-                                       const Layout& out) {
+                                       const Layout& lv, const Layout& out) {
     smem = lds;
     N = N_;
     win = win_;
@@ -188,10 +194,12 @@ struct FwdBlock {
     const int64_t head_off = b * in.sb + h * in.sh;
     row_bytes = (uint32_t)(2 * in.sn);
     head_bytes = (uint32_t)(N - 1) * row_bytes + (uint32_t)kRowBytes;
+    v_row_bytes = (uint32_t)(2 * lv.sn);
+    v_head_bytes = (uint32_t)(N - 1) * v_row_bytes + (uint32_t)L::kVRowBytes;
     o_off = b * out.sb + h * out.sh;
     o_sn = out.sn;
     k_ptr = reinterpret_cast<const uint8_t*>(K + head_off);
-    v_ptr = reinterpret_cast<const uint8_t*>(V + head_off);
+    v_ptr = reinterpret_cast<const uint8_t*>(V + (b * lv.sb + h * lv.sh));
 
     const int q0_blk = qb * kBM;
     q0 = q0_blk + 32 * wave;
@@ -272,11 +280,11 @@ struct FwdBlock {
   // exactly kCopies copies, in one asm statement that saves and restores M0
   // once.
   __device__ __forceinline__ void load_tiles(int jk, int sk, int jv, int sv) const {
-    const uint32_t tile_bytes = kBN * row_bytes;
+    const uint32_t tile_bytes = kBN * row_bytes, v_tile_bytes = kBN * v_row_bytes;
     const uint32_t k_left = jk < n_tiles ? head_bytes - (uint32_t)jk * tile_bytes : 0u;
-    const uint32_t v_left = jv < n_tiles ? head_bytes - (uint32_t)jv * tile_bytes : 0u;
+    const uint32_t v_left = jv < n_tiles ? v_head_bytes - (uint32_t)jv * v_tile_bytes : 0u;
     const i32x4 tk = make_rsrc(k_ptr + (size_t)jk * tile_bytes, k_left);
-    const i32x4 tv = make_rsrc(v_ptr + (size_t)jv * tile_bytes, v_left);
+    const i32x4 tv = make_rsrc(v_ptr + (size_t)jv * v_tile_bytes, v_left);
     // wave-uniform by construction; readfirstlane keeps the selection in SGPRs
     i32x4 tx;
 #pragma unroll
@@ -288,10 +296,15 @@ struct FwdBlock {
     const uint32_t x_lds = (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)((uint32_t)(uintptr_t)(lds_void*)smem + x_off + ((uint32_t)(sk * L::kKStage) & x_kmask) +
               ((uint32_t)(kStages * L::kKStage + sv * L::kVStage) & x_vmask)));
-    static_assert(kFullK == kFullV && (kFullK == 1 || kFullK == 2), "copy groups of 3 or 5");
-    if constexpr (kFullK == 2)
+    if constexpr (kFullK == 2 && kFullV == 2)
       dma_group5(tk, tv, tx, k_st, k_st + kWaves * 1024, v_st, v_st + kWaves * 1024, x_lds,
                  src_k[0], src_k[1], src_v[0], src_v[1], src_x);
+    else if constexpr (kFullK == 2)
+      dma_group4a(tk, tv, tx, k_st, k_st + kWaves * 1024, v_st, x_lds, src_k[0], src_k[1],
+                  src_v[0], src_x);
+    else if constexpr (kFullV == 2)
+      dma_group4b(tk, tv, tx, k_st, v_st, v_st + kWaves * 1024, x_lds, src_k[0], src_v[0],
+                  src_v[1], src_x);
     else
       dma_group3(tk, tv, tx, k_st, v_st, x_lds, src_k[0], src_v[0], src_x);
   }
@@ -402,7 +415,6 @@ struct FwdBlock {
   // issue priority (see step()).
   template <int kMask, bool kFirst = false, int kHalf = 0>
   __device__ __forceinline__ void block(int u) {
-    static_assert(kPV == kKs, "as many PV as score MFMAs per block (d = 64, 96 or 128)");
     constexpr int kMfmas = (kFirst ? 0 : kPV) + kKs;
     static_assert(kMfmas == 16 || kMfmas == 12 || kMfmas == 8 || kMfmas == 6 || kMfmas == 4,
                   "slot schedules exist for 4, 6, 8, 12 and 16 MFMAs");
@@ -436,16 +448,21 @@ struct FwdBlock {
         // accumulator, and the operands of the second key half come last
         const int f = (t < kPV / 2) ? 2 * t : 2 * (t - kPV / 2) + 1;
         acc[f >> 1] = E::mfma(vfr[f], __builtin_bit_cast(vec8, p_prev[f & 1]), acc[f >> 1]);
-        kfr[t] = *reinterpret_cast<const vec8*>(kt + t * 32);
+        // K operands r = t, t + kPV, ..: all are read in the PV phase
+#pragma unroll
+        for (int r = t; r < kKs; r += kPV) kfr[r] = *reinterpret_cast<const vec8*>(kt + r * 32);
       } else {
         const int i = kFirst ? t : t - kPV;  // score k-step
         s_next = E::mfma(kfr[i], qf[i], i == 0 ? f32x16{} : s_next);
-        // V^T operand i of block u: two transpose reads
-        const int db = i >> 1, tt = i & 1;
-        const uint8_t* vp = vt + 16 * tt * L::kVStride + 64 * db;
-        const auto lo = E::read_tr((const lds_void*)vp);
-        const auto hi = E::read_tr((const lds_void*)(vp + 4 * L::kVStride));
-        vfr[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        // V^T operands f = i, i + kKs, .. of block u: two transpose reads each
+#pragma unroll
+        for (int f = i; f < kPV; f += kKs) {
+          const int db = f >> 1, tt = f & 1;
+          const uint8_t* vp = vt + 16 * tt * L::kVStride + 64 * db;
+          const auto lo = E::read_tr((const lds_void*)vp);
+          const auto hi = E::read_tr((const lds_void*)(vp + 4 * L::kVStride));
+          vfr[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
       }
       // Probabilities of the 8 score pairs, software-pipelined so that each
       // step of a pair (scale, exp2, then pack and fp32 partial sum) runs a
@@ -633,31 +650,32 @@ struct FwdBlock {
   }
 };
 
-template <bool IsBf16, int D, bool Causal, int Mode>
+template <bool IsBf16, int D, bool Causal, int Mode, int DV>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int win, int H, int BH, int n_qblocks,
-    float c, uint32_t q_sign, Layout lq, Layout in, Layout out, const uint8_t* __restrict__ bmask,
-    int64_t m_sb, int64_t m_sh) {
-  static_assert(Lds<D>::kBytes + kSparseBytes <= 160 * 1024, "the tile list fits beside the rings");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds<D>::kBytes + (Mode == kModeSparse ? kSparseBytes : 0)];
+    float c, uint32_t q_sign, Layout lq, Layout in, Layout lv, Layout out,
+    const uint8_t* __restrict__ bmask, int64_t m_sb, int64_t m_sh) {
+  using L = Lds<D, DV>;
+  static_assert(L::kBytes + kSparseBytes <= 160 * 1024, "the tile list fits beside the rings");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[L::kBytes + (Mode == kModeSparse ? kSparseBytes : 0)];
   // work item: (query block, batch*head); heaviest causal blocks first
   const int bh = blockIdx.x % BH;
   int qb = blockIdx.x / BH;
   if (Causal) qb = n_qblocks - 1 - qb;
-  FwdBlock<IsBf16, D, Causal, Mode> blk;
-  blk.init(smem, Q, K, V, N, win, H, bh, qb, c, q_sign, lq, in, out);
+  FwdBlock<IsBf16, D, Causal, Mode, DV> blk;
+  blk.init(smem, Q, K, V, N, win, H, bh, qb, c, q_sign, lq, in, lv, out);
   if constexpr (Mode == kModeSparse) {
     const int b = bh / H, h = bh - b * H;
     blk.qbit = 16 + blk.wave / 2;  // 32-row waves, 64-row mask blocks
-    blk.run(qb * kBM, reinterpret_cast<uint32_t*>(smem + Lds<D>::kBytes), bmask + b * m_sb + h * m_sh);
+    blk.run(qb * kBM, reinterpret_cast<uint32_t*>(smem + L::kBytes), bmask + b * m_sb + h * m_sh);
   } else {
     blk.run(qb * kBM);
   }
   blk.store(O, LSE, bh);
 }
 
-template <bool IsBf16, int D, bool Causal, int Mode>
+template <bool IsBf16, int D, bool Causal, int Mode, int DV = D>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int N = (int)a.N;
   const int BH = (int)(a.B * a.H);
@@ -668,11 +686,11 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   // so all visible keys weigh exactly 1 and hidden ones (-inf) weigh 0.
   const float c = a.scale != 0.f ? __builtin_fabsf(a.scale) * 1.4426950408889634f : 1e-30f;
   const uint32_t q_sign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_kernel<IsBf16, D, Causal, Mode>), grid, dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fwd_kernel<IsBf16, D, Causal, Mode, DV>), grid, dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, N,
                      (int)(a.window < a.N ? a.window : a.N), (int)a.H, BH, n_qblocks, c, q_sign, a.lq,
-                     a.in, a.out, a.block_mask, a.mask_sb, a.mask_sh);
+                     a.in, a.lv, a.out, a.block_mask, a.mask_sb, a.mask_sh);
   return hipGetLastError();
 }
 
@@ -687,6 +705,11 @@ hipError_t dispatch_d(const FwdArgs& a, hipStream_t s) {
 
 template <bool IsBf16>
 hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
+  // d_v != d (plain masks only): q, k rows of d, v, o rows of d_v
+  if (a.dv == 64 && a.d == 128)
+    return a.causal ? launch<IsBf16, 128, true, kModePlain, 64>(a, s) : launch<IsBf16, 128, false, kModePlain, 64>(a, s);
+  if (a.dv == 128 && a.d == 64)
+    return a.causal ? launch<IsBf16, 64, true, kModePlain, 128>(a, s) : launch<IsBf16, 64, false, kModePlain, 128>(a, s);
   if (a.d == 128) return dispatch_d<IsBf16, 128>(a, s);
   return a.d == 96 ? dispatch_d<IsBf16, 96>(a, s) : dispatch_d<IsBf16, 64>(a, s);
 }

@@ -89,6 +89,39 @@ __device__ __forceinline__ void dma_group3(const i32x4& a, const i32x4& b, const
       : "memory");
 }
 
+// Four copies: two with rsrc a, one with b, the last with x (l0, l1 -> a).
+__device__ __forceinline__ void dma_group4a(const i32x4& a, const i32x4& b, const i32x4& x,
+                                            uint32_t l0, uint32_t l1, uint32_t l2, uint32_t l3,
+                                            uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\tbuffer_load_dwordx4 %8, %1, 0 offen lds\n\t"
+      "s_mov_b32 m0, %5\n\tbuffer_load_dwordx4 %9, %1, 0 offen lds\n\t"
+      "s_mov_b32 m0, %6\n\tbuffer_load_dwordx4 %10, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %7\n\tbuffer_load_dwordx4 %11, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(a), "s"(b), "s"(x), "s"(l0), "s"(l1), "s"(l2), "s"(l3), "v"(v0), "v"(v1), "v"(v2), "v"(v3)
+      : "memory");
+}
+// Four copies: one with rsrc a, two with b, the last with x (l1, l2 -> b).
+__device__ __forceinline__ void dma_group4b(const i32x4& a, const i32x4& b, const i32x4& x,
+                                            uint32_t l0, uint32_t l1, uint32_t l2, uint32_t l3,
+                                            uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\tbuffer_load_dwordx4 %8, %1, 0 offen lds\n\t"
+      "s_mov_b32 m0, %5\n\tbuffer_load_dwordx4 %9, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %6\n\tbuffer_load_dwordx4 %10, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %7\n\tbuffer_load_dwordx4 %11, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(a), "s"(b), "s"(x), "s"(l0), "s"(l1), "s"(l2), "s"(l3), "v"(v0), "v"(v1), "v"(v2), "v"(v3)
+      : "memory");
+}
+
 // Buffer resource (base, size in bytes) for raw, bounds-checked access.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);

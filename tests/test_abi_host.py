@@ -29,12 +29,13 @@ def test_library_exports_every_declared_symbol():
     declared = fa.declared_symbols()
     assert {"attn_fwd", "attn_bwd", "attn_fwd_window", "attn_bwd_window", "attn_bwd_workspace_bytes",
             "attn_fwd_kv_outer", "attn_fwd_kv_outer_workspace_bytes", "attn_fwd_strided",
-            "attn_bwd_strided", "attn_fwd_block_sparse", "attn_bwd_block_sparse", "fa_status_str",
+            "attn_bwd_strided", "attn_fwd_block_sparse", "attn_bwd_block_sparse", "attn_fwd_dv",
+            "fa_status_str",
             "fa_abi_version"} <= set(declared)
     lib = ctypes.CDLL(fa._binding.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
-    assert fa.lib().fa_abi_version() == 6
+    assert fa.lib().fa_abi_version() == 7
 
 
 def test_status_strings():
@@ -321,3 +322,18 @@ def test_block_sparse_backward_validation():
     assert bb(dtype=fa.F32) == FA_ERR_UNSUPPORTED
     assert bb(ws=8) == FA_ERR_WORKSPACE
     assert bb(q=P[0] + 2, mb=2, mh=3) == FA_ERR_ALIGN   # accepted shapes reach the pointer checks
+
+
+def test_dv_validation():
+    def fdv(d, dv, q=P[0], **kw):
+        a = dict(B=1, H=1, N=16, mask=0, scale=0.125, dtype=fa.BF16)
+        a.update(kw)
+        return fa.attn_fwd_dv_raw(q, P[1], P[2], P[3], P[4], a["B"], a["H"], a["N"], d, dv, a["mask"],
+                                  a["scale"], a["dtype"], None)
+    assert fdv(128, 0) == FA_ERR_SHAPE
+    for d, dv in ((128, 96), (96, 64), (64, 96), (128, 32), (64, 256)):
+        assert fdv(d, dv) == FA_ERR_UNSUPPORTED, (d, dv)
+    for d, dv in ((128, 64), (64, 128), (128, 128), (96, 96)):
+        assert fdv(d, dv, q=P[0] + 2) == FA_ERR_ALIGN, (d, dv)  # accepted: reaches the pointer checks
+    assert fdv(128, 64, q=None) == FA_ERR_NULL
+    assert fdv(64, 128, N=(1 << 23)) == FA_ERR_SHAPE           # v rows of a head span 2 GiB

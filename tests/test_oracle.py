@@ -129,6 +129,27 @@ def test_transfer_ledger(golden_dir):
         assert led["dense_total"] - led["tiled_total"] == 4 * n * n
 
 
+# ---------------------------------------------------------------- values of another width
+
+@pytest.mark.parametrize("d,dv", [(8, 4), (4, 12)])
+def test_dv_differs_from_d(d, dv):
+    """V of width d_v != d ("Flash Attention: IO-Aware Exact Attention" defines V
+    as N x d_v): the dense oracle against torch's attention, and the online
+    recurrence of both loop orders against the dense oracle."""
+    q, k = _rand(2, 70, d, seed=171, std=2), _rand(2, 70, d, seed=172, std=2)
+    v = _rand(2, 70, dv, seed=173)
+    for causal in (False, True):
+        o, lse = oracle.dense_fwd(q, k, v, causal=causal)
+        assert o.shape == (2, 70, dv)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(q), torch.tensor(k), torch.tensor(v), is_causal=causal)
+        np.testing.assert_allclose(o, ref.numpy(), rtol=1e-12, atol=1e-13)
+        for f in (oracle.online_fwd, oracle.online_fwd_kv_outer):
+            o2, l2 = f(q, k, v, causal=causal, query_block=9, key_block=16)
+            np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(l2, lse, rtol=1e-13)
+
+
 # ---------------------------------------------------------------- block-sparse masks
 
 def _bm(n_qb, n_kb, seed, density=0.4, lead=()):
