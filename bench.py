@@ -5,7 +5,7 @@ One step = one ``attn_fwd`` call over the long-context causal workload
 N(0, 1) inputs already resident in device memory.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd]
-                    [--no-window] [--no-sparse] [--no-kv-outer]
+                    [--no-window] [--no-sparse] [--no-variants] [--no-kv-outer]
 
 The reported throughput counts algorithmic FLOPs only: 4 * d * (visible query-key
 pairs) * B * H, i.e. the two matrix products over the causal triangle.
@@ -218,6 +218,66 @@ def sparse_record(fa, workloads, torch, steps, warmup):
                          "algorithmic_flops_per_launch": flops}}
 
 
+def variants_record(fa, workloads, torch, steps, warmup):
+    """The bench head (B=1, H=16, N=8192, causal, bf16) in the other forms the
+    library takes, each timed like the forward: a [B, N, H, d] view (strided
+    call), d = 96, d_v = 64 with d = 128, and the backward of the block-sparse
+    and sliding-window workloads (10 d FLOPs per visible pair)."""
+    dev = torch.device("cuda:0")
+    out = {}
+    w = workloads.WORKLOADS[WORKLOAD]
+
+    def rec(name, step, flops, s=steps, wm=warmup):
+        ms, _ = time_graph(step, s, wm, torch)
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name] = {"ms_per_step": round(ms, 5), "TFLOP/s": round(tf, 2),
+                     "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    def dev_bf16(a):
+        return torch.from_numpy(a).to(dev).to(torch.bfloat16)
+
+    # strided: q, k, v as [B, H, N, d] views of [B, N, H, d] memory
+    x = workloads.make_inputs(w)
+    qb, kb, vb = (dev_bf16(x[n].transpose(0, 2, 1, 3).copy()).transpose(1, 2) for n in "qkv")
+    ob = torch.empty_like(qb)
+    rec("fwd_bshd_d128", lambda: fa.attn_fwd(qb, kb, vb, causal=True, out=ob), w.fwd_flops())
+    # d = 96
+    x96 = workloads.random_inputs(1, 16, 8192, 96, "bf16", seed=11)
+    q96, k96, v96 = (dev_bf16(x96[n]).contiguous() for n in "qkv")
+    o96 = torch.empty_like(q96)
+    rec("fwd_d96", lambda: fa.attn_fwd(q96, k96, v96, causal=True, out=o96),
+        4 * 96 * (8192 * 8193 // 2) * 16)
+    # d_v = 64 with d = 128: 2 d + 2 d_v FLOPs per visible pair
+    xv = workloads.random_inputs(1, 16, 8192, 64, "bf16", seed=12)
+    q, k = (dev_bf16(x[n]).contiguous() for n in "qk")
+    v64 = dev_bf16(xv["v"]).contiguous()
+    o64 = torch.empty((1, 16, 8192, 64), dtype=torch.bfloat16, device=dev)
+    rec("fwd_d128_dv64", lambda: fa.attn_fwd(q, k, v64, causal=True, out=o64),
+        2 * (128 + 64) * (8192 * 8193 // 2) * 16)
+    # backward of the block-sparse and the sliding-window workloads
+    for name, wl in (("bwd_block_sparse", "long_sparse_bf16"), ("bwd_window", "long_window_bf16")):
+        ww = workloads.WORKLOADS[wl]
+        xw = workloads.make_inputs(ww)
+        qq, kk, vv = (dev_bf16(xw[n]).contiguous() for n in "qkv")
+        do = torch.randn_like(qq)
+        kw = {}
+        if ww.sparse is not None:
+            mask = workloads.block_sparse_mask(ww.N, ww.H, *ww.sparse)
+            kw["block_mask"] = torch.from_numpy(mask).to(dev)
+            pairs = workloads.sparse_pairs(mask, ww.N, ww.causal)
+        else:
+            kw["window"] = ww.window
+            pairs = ww.pairs() * ww.H
+        oo, ll = fa.attn_fwd(qq, kk, vv, causal=ww.causal, **kw)
+        g = [torch.empty_like(qq) for _ in range(3)]
+        ws = torch.empty(fa.bwd_workspace_bytes(ww.B, ww.H, ww.N, ww.d, fa.BF16), dtype=torch.uint8,
+                         device=dev)
+        rec(name, lambda: fa.attn_bwd(qq, kk, vv, oo, ll, do, causal=ww.causal, dq=g[0], dk=g[1],
+                                      dv=g[2], workspace=ws, **kw),
+            10 * ww.d * pairs * ww.B, s=20, wm=100)
+    return out
+
+
 def kv_outer_record(fa, workloads, torch, steps, warmup):
     """The bench workload in the key/value-outer loop order (attn_fwd_kv_outer),
     timed over a few calls: each is tens of milliseconds."""
@@ -263,6 +323,8 @@ def main():
     ap.add_argument("--window-warmup", type=int, default=1500)
     ap.add_argument("--no-sparse", action="store_true",
                     help="skip the block-sparse forward measurement")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the strided / d = 96 / d_v = 64 / sparse and window backward timings")
     ap.add_argument("--no-kv-outer", action="store_true",
                     help="skip the key/value-outer loop-order measurement")
     ap.add_argument("--kv-steps", type=int, default=3)
@@ -354,6 +416,8 @@ def main():
     if not args.no_sparse:
         record["attn_fwd_block_sparse"] = sparse_record(fa, workloads, torch, args.window_steps,
                                                         args.window_warmup)
+    if not args.no_variants:
+        record["variants"] = variants_record(fa, workloads, torch, 50, 300)
     if not args.no_kv_outer:
         record["attn_fwd_kv_outer"] = kv_outer_record(fa, workloads, torch, args.kv_steps,
                                                       args.kv_warmup)
