@@ -221,6 +221,25 @@ int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse
                 int mask, float scale, int dtype, void* stream);
 
 /*
+ * attn_bwd_dv -- backward pass of attn_fwd_dv.
+ *
+ * As attn_bwd, except that v, o, dout and dv are dense [B][H][N][d_v] arrays
+ * while q, k, dq and dk are [B][H][N][d].  In the gradients of attn_bwd,
+ * dP = dout v^T and dv = P^T dout contract or produce d_v columns, while the
+ * recomputed S = q k^T, dq = scale dS k and dk = scale dS^T q stay over d
+ * (V is N x d_v in "Flash Attention: IO-Aware Exact Attention", section "Why
+ * intermediate matrices cost memory traffic").  Supported
+ * (d, d_v): (128, 64), (64, 128), and d_v == d (the attn_bwd kernels);
+ * FA_ERR_UNSUPPORTED for other pairs and for FA_F32, FA_ERR_SHAPE for
+ * d_v < 1.  The workspace is as for attn_bwd (attn_bwd_workspace_bytes).
+ */
+int attn_bwd_dv(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv,
+                int64_t B, int64_t H, int64_t N, int64_t d, int64_t d_v,
+                int mask, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/*
  * attn_fwd_block_sparse -- forward pass with a block-sparse mask.
  *
  * As attn_fwd, except that key j is visible to query i only if the mask

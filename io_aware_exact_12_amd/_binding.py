@@ -57,6 +57,9 @@ def lib():
         L.attn_fwd_dv.restype = ctypes.c_int
         L.attn_fwd_dv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
                                   ctypes.c_float, ctypes.c_int, vp]
+        L.attn_bwd_dv.restype = ctypes.c_int
+        L.attn_bwd_dv.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                             ctypes.c_int, vp, ctypes.c_size_t, vp]
         L.attn_fwd_block_sparse.restype = ctypes.c_int
         L.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i64, i64,
                                             ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
@@ -136,6 +139,12 @@ def attn_bwd_strided_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, in_st, g
 
 def attn_fwd_dv_raw(q, k, v, o, lse, B, H, N, d, dv, mask, scale, dtype, stream):
     return lib().attn_fwd_dv(q, k, v, o, lse, B, H, N, d, dv, mask, scale, dtype, stream)
+
+
+def attn_bwd_dv_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, d_v, mask, scale, dtype, ws,
+                    ws_bytes, stream):
+    return lib().attn_bwd_dv(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, d_v, mask, scale, dtype,
+                             ws, ws_bytes, stream)
 
 
 def attn_fwd_block_sparse_raw(q, k, v, o, lse, B, H, N, d, block_mask, mask_batches, mask_heads,
@@ -320,13 +329,18 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
 
     All tensors are contiguous device tensors; q, k, v, o, dout share one
     [B, H, N, d] shape and dtype (float16 or bfloat16), lse is float32 [B, H, N].
+    v, o and dout may instead be [B, H, N, dv] (contiguous, no window or block
+    mask), which calls ``attn_bwd_dv``.
     ``workspace`` (a uint8 device tensor) is allocated when not given.
     """
     import torch
     shape = q.shape
-    for t in (k, v, o, dout):
-        if t.shape != shape or t.dtype != q.dtype:
-            raise ValueError("q, k, v, o, dout must share one shape and dtype")
+    d_v = v.shape[-1] if v.dim() == 4 else None
+    vshape = shape[:3] + (d_v,)
+    for t, want in ((k, shape), (v, vshape), (o, vshape), (dout, vshape)):
+        if t.shape != want or t.dtype != q.dtype:
+            raise ValueError("q, k must share one [B, H, N, d] shape, v, o, dout one [B, H, N, dv], "
+                             "all one dtype")
     for t in (q, k, v, o, dout):
         if not t.is_cuda or t.stride(-1) != 1:
             raise ValueError("inputs must be device tensors with a contiguous last axis")
@@ -347,6 +361,18 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
+    if d_v != d:
+        if window is not None or block_mask is not None:
+            raise ValueError("dv != d takes no window or block mask")
+        if not all(t.is_contiguous() for t in (q, k, v, o, dout, dq, dk, dv)):
+            raise ValueError("dv != d takes contiguous tensors")
+        st = attn_bwd_dv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                             d_v, MASK_CAUSAL if causal else MASK_NONE, float(scale), code,
+                             workspace.data_ptr(), ws_bytes, stream.cuda_stream)
+        if st != 0:
+            raise FaError(st, "attn_bwd_dv")
+        return dq, dk, dv
     if block_mask is not None:
         _check_block_mask(block_mask, B, H, N)
         if window is not None or not all(t.is_contiguous() for t in (q, k, v, o, dout, dq, dk, dv)):

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 // Block-sparse: mask blocks of 64 x 64; a query block of the forward lists at
 // most this many key tiles (its LDS list).
 constexpr int64_t kMaxSparseTiles = 2048;
@@ -124,7 +124,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
              int64_t d, int mask, int64_t window, float scale, int dtype, void* workspace,
              size_t workspace_bytes, void* stream, const int64_t* in_st = nullptr,
              const int64_t* out_st = nullptr, const uint8_t* block_mask = nullptr,
-             int64_t mask_b = 0, int64_t mask_h = 0) {
+             int64_t mask_b = 0, int64_t mask_h = 0, int64_t dvw = 0) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL) return FA_ERR_MASK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr ||
@@ -151,6 +151,14 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
     a.block_mask = block_mask;
     a.mask_sh = mask_h == 1 ? 0 : nb * nb;
     a.mask_sb = mask_b == 1 ? 0 : mask_h * nb * nb;
+  }
+  a.dvw = d;
+  a.lv = a.in;
+  a.outv = a.out;
+  if (dvw != 0 && dvw != d) {  // v, o, dout and dv rows of dvw elements, dense
+    if (!((d == 128 && dvw == 64) || (d == 64 && dvw == 128))) return FA_ERR_UNSUPPORTED;
+    a.dvw = dvw;
+    a.lv = a.outv = fa::dense_layout(H, N, dvw);
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
@@ -249,6 +257,17 @@ int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse
   if (N > 0 && N * dv * (dtype == FA_F32 ? 4 : 2) > INT32_MAX - 1024) return FA_ERR_SHAPE;
   return fwd_impl(q, k, v, o, lse, B, H, N, d, mask, N, scale, dtype, stream, nullptr, nullptr,
                   nullptr, nullptr, 0, 0, dv);
+}
+
+int attn_bwd_dv(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                int64_t d, int64_t d_v, int mask, float scale, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (d_v < 1) return FA_ERR_SHAPE;
+  if (d_v != 64 && d_v != 96 && d_v != 128) return FA_ERR_UNSUPPORTED;
+  if (N > 0 && N * d_v * (dtype == FA_F32 ? 4 : 2) > INT32_MAX - 1024) return FA_ERR_SHAPE;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, N, scale, dtype, workspace,
+                  workspace_bytes, stream, nullptr, nullptr, nullptr, 0, 0, d_v);
 }
 
 int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,

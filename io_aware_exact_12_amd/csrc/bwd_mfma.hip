@@ -174,9 +174,10 @@ __device__ __forceinline__ void load_resident(typename Elt<IsBf16>::vec8 (&f)[D 
 // Store one lane's column of a transposed accumulator (rows = d) as row `row`
 // of a view with row stride sn elements, multiplied by `mul` and rounded to
 // the element type.
-template <bool IsBf16, int D>
+template <bool IsBf16, int D, int NA>
 __device__ __forceinline__ void store_row(uint16_t* base, int row, int64_t sn, int g,
-                                          const f32x16 (&acc)[D / 32], float mul) {
+                                          const f32x16 (&acc)[NA], float mul) {
+  static_assert(NA >= D / 32, "one accumulator per 32 columns");
   using E = Elt<IsBf16>;
   typedef __attribute__((ext_vector_type(4))) typename E::scalar h4_t;
   uint16_t* orow = base + (int64_t)row * sn;
@@ -205,30 +206,34 @@ __device__ __forceinline__ void store_row(uint16_t* base, int row, int64_t sn, i
 // them; a half of a masked tile that lies before all of the wave's keys still
 // runs and contributes zeros.  A negative scale flips the sign of the resident
 // K (exact), so S carries the sign and dK = scale dS^T Q uses Q as stored.
-template <int D> struct DkdvLds {
+template <int D, int DV = D> struct DkdvLds {
   static constexpr int kQ = 0;
-  static constexpr int kDO = STile<D>::kBytes;
-  static constexpr int kLse = 2 * STile<D>::kBytes;  // -LSE * log2(e) of the 64 queries
+  static constexpr int kDO = STile<D>::kBytes;                     // dO rows of d_v
+  static constexpr int kLse = kDO + STile<DV>::kBytes;  // -LSE * log2(e) of the 64 queries
   static constexpr int kD = kLse + 4 * kT;
   static constexpr int kStage = kD + 4 * kT;
   static constexpr int kBytes = 2 * kStage;
 };
 
-template <bool IsBf16, int D, bool Causal, int Mode>
+template <bool IsBf16, int D, bool Causal, int Mode, int DV = D>
 struct DkdvBlock {
   static constexpr bool kWin = Causal && Mode == kModeWindow;  // sliding window narrower than N
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
-  using T = STile<D>;
-  using Ld = DkdvLds<D>;
-  static constexpr int kKs = D / 16, kDB = D / 32;
+  using T = STile<D>;    // Q tiles
+  using TO = STile<DV>;  // dO tiles (d_v wide)
+  using Ld = DkdvLds<D, DV>;
+  static constexpr int kKs = D / 16, kDB = D / 32;      // over d: S = Q K^T, dK^T
+  static constexpr int kKsO = DV / 16, kDBO = DV / 32;  // over d_v: dP = dO V^T, dV^T
+  static constexpr int kDBA = kDB > kDBO ? kDB : kDBO;
+  static constexpr int kMin = kKs < kKsO ? kKs : kKsO;
 
   int lane, g, N, win, my_k;
   float c;
-  vec8 kf[kKs], vf[kKs];
-  f32x16 acc[kDB];        // dV^T in pass V, dK^T in pass K
-  int roff[kKs];          // row operand of k step kk: LDS row l32, chunk 2 kk + g
-  int toff[2][kDB];       // transpose reads (elements 0..3 / 4..7) of d block db, k step 0
+  vec8 kf[kKs], vf[kKsO];
+  f32x16 acc[kDBA];       // dV^T in pass V, dK^T in pass K
+  int roff[kKs], roffO[kKsO];    // row operand of k step kk: LDS row l32, chunk 2 kk + g
+  int toff[2][kDB], toffO[2][kDBO];  // transpose reads (elements 0..3 / 4..7) of d block db
 
   __device__ __forceinline__ void init(int lane_, int N_, int win_, int kw0, float c_) {
     lane = lane_;
@@ -239,6 +244,10 @@ struct DkdvBlock {
     my_k = kw0 + (lane & 31);
 #pragma unroll
     for (int kk = 0; kk < kKs; ++kk) roff[kk] = T::at(lane & 31, 2 * kk + g);
+    if constexpr (DV != D) {
+#pragma unroll
+      for (int kk = 0; kk < kKsO; ++kk) roffO[kk] = TO::at(lane & 31, 2 * kk + g);
+    }
     const int grp = lane >> 4, s16 = lane & 15;
     const int r0 = 4 * g + (s16 >> 2);
 #pragma unroll
@@ -247,10 +256,18 @@ struct DkdvBlock {
       toff[0][db] = T::at(r0, col >> 4) + (col & 15);
       toff[1][db] = T::at(r0 + 8, col >> 4) + (col & 15);
     }
+    if constexpr (DV != D) {
+#pragma unroll
+      for (int db = 0; db < kDBO; ++db) {
+        const int col = 2 * (16 * (grp & 1) + 4 * (s16 & 3)) + 64 * db;
+        toffO[0][db] = TO::at(r0, col >> 4) + (col & 15);
+        toffO[1][db] = TO::at(r0 + 8, col >> 4) + (col & 15);
+      }
+    }
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
-    for (int i = 0; i < kDB; ++i) acc[i] = f32x16{};
+    for (int i = 0; i < kDBA; ++i) acc[i] = f32x16{};
   }
 
   // Logical tile rows 16 t + 32 h keep their swizzle, so a half and a k step
@@ -264,6 +281,22 @@ struct DkdvBlock {
     const auto hi = E::read_tr((const lds_void*)(p + toff[1][db]));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
+  // the same two reads on a dO tile (d_v wide)
+  __device__ __forceinline__ vec8 row_opO(const uint8_t* tile, int h, int kk) const {
+    if constexpr (DV == D) return row_op(tile, h, kk);
+    return *reinterpret_cast<const vec8*>(tile + roffO[kk] + 32 * h * TO::kRowBytes);
+  }
+  __device__ __forceinline__ vec8 tr_opO(const uint8_t* tile, int h, int t, int db) const {
+    if constexpr (DV == D) return tr_op(tile, h, t, db);
+    const uint8_t* p = tile + (32 * h + 16 * t) * TO::kRowBytes;
+    const auto lo = E::read_tr((const lds_void*)(p + toffO[0][db]));
+    const auto hi = E::read_tr((const lds_void*)(p + toffO[1][db]));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // MFMA i of the S / dP chains: while both remain they alternate (S even, dP
+  // odd); the longer chain then finishes alone
+  static constexpr bool is_dp(int i) { return i < 2 * kMin ? (i & 1) != 0 : kKsO > kKs; }
+  static constexpr int kstep(int i) { return i < 2 * kMin ? i >> 1 : kMin + (i - 2 * kMin); }
   // per-query floats of registers r, r+1 (consecutive queries) of half h
   __device__ __forceinline__ f32x2 pair_vals(const uint8_t* sb, int off, int h, int r) const {
     return *reinterpret_cast<const f32x2*>(reinterpret_cast<const float*>(sb + off) + 32 * h + 8 * g +
@@ -301,12 +334,12 @@ struct DkdvBlock {
       pw[e >> 2][e & 3] = E::pack2(prob<kMasked>(s, nl[0], qs0, 2 * e), prob<kMasked>(s, nl[1], qs0, 2 * e + 1));
     }
     __builtin_amdgcn_sched_barrier(0);
-    vec8 b[2] = {tr_op(o, h, 0, 0), tr_op(o, h, 0, 1 % kDB)};
+    vec8 b[2] = {tr_opO(o, h, 0, 0), tr_opO(o, h, 0, 1 % kDBO)};
 #pragma unroll
-    for (int i = 0; i < 2 * kDB; ++i) {
-      const int tt = i / kDB, db = i % kDB;
+    for (int i = 0; i < 2 * kDBO; ++i) {
+      const int tt = i / kDBO, db = i % kDBO;
       acc[db] = E::mfma(b[i & 1], __builtin_bit_cast(vec8, pw[tt]), acc[db]);
-      if (i + 2 < 2 * kDB) b[i & 1] = tr_op(o, h, (i + 2) / kDB, (i + 2) % kDB);
+      if (i + 2 < 2 * kDBO) b[i & 1] = tr_opO(o, h, (i + 2) / kDBO, (i + 2) % kDBO);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -316,15 +349,16 @@ struct DkdvBlock {
     const uint8_t* q = sb + Ld::kQ;
     const uint8_t* o = sb + Ld::kDO;
     f32x16 s = f32x16{}, dp = f32x16{};
-    vec8 a[2] = {row_op(q, h, 0), row_op(o, h, 0)};
+    constexpr int kN = kKs + kKsO;
+    auto op = [&](int i) { return is_dp(i) ? row_opO(o, h, kstep(i)) : row_op(q, h, kstep(i)); };
+    vec8 a[2] = {op(0), op(1)};
 #pragma unroll
-    for (int i = 0; i < 2 * kKs; ++i) {
-      const int kk = i >> 1;
-      if (i & 1)
-        dp = E::mfma(a[1], vf[kk], dp);
+    for (int i = 0; i < kN; ++i) {
+      if (is_dp(i))
+        dp = E::mfma(a[i & 1], vf[kstep(i)], dp);
       else
-        s = E::mfma(a[0], kf[kk], s);
-      if (i + 2 < 2 * kKs) a[i & 1] = (i & 1) ? row_op(o, h, kk + 1) : row_op(q, h, kk + 1);
+        s = E::mfma(a[i & 1], kf[kstep(i)], s);
+      if (i + 2 < kN) a[i & 1] = op(i + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
     u32x4 sw[2];
@@ -348,16 +382,18 @@ struct DkdvBlock {
   }
 };
 
-template <bool IsBf16, int D, bool Causal, int Mode>
+template <bool IsBf16, int D, bool Causal, int Mode, int DV>
 __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NLse, const float* __restrict__ Dsum,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int win, int H, int BH, float c,
-    float dk_mul, uint32_t k_sign, Layout in, Layout out, const uint8_t* __restrict__ bmask,
-    int64_t m_sb, int64_t m_sh) {
+    float dk_mul, uint32_t k_sign, Layout in, Layout out, Layout lv, Layout outv,
+    const uint8_t* __restrict__ bmask, int64_t m_sb, int64_t m_sh) {
   using T = STile<D>;
-  using Ld = DkdvLds<D>;
+  using TO = STile<DV>;
+  using Ld = DkdvLds<D, DV>;
   constexpr bool kSparse = Mode == kModeSparse;
+  if constexpr (DV == D) lv = in, outv = out;  // one layout: the d_v addressing folds away
   static_assert(kT == kSparseBlock && kRes % kSparseBlock == 0, "mask blocks are tiles");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes + (kSparse ? kSparseBytes : 0)];
 
@@ -366,13 +402,14 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
   const int bh = blockIdx.x % BH, kblk = blockIdx.x / BH;  // heaviest (earliest keys) first
   const int b = bh / H, h = bh - b * H;
   const int64_t head = b * in.sb + h * in.sh, head_out = b * out.sb + h * out.sh;
+  const int64_t head_v = b * lv.sb + h * lv.sh, head_dv = b * outv.sb + h * outv.sh;
   const int k0 = kblk * kRes, kw0 = k0 + 32 * wave;
 
   constexpr bool kWin = Causal && Mode == kModeWindow;
-  DkdvBlock<IsBf16, D, Causal, Mode> blk;
+  DkdvBlock<IsBf16, D, Causal, Mode, DV> blk;
   blk.init(lane, N, win, kw0, c);
   load_resident<IsBf16, D>(blk.kf, K + head, N, blk.my_k, in.sn, blk.g, k_sign);
-  load_resident<IsBf16, D>(blk.vf, V + head, N, blk.my_k, in.sn, blk.g, 0u);
+  load_resident<IsBf16, DV>(blk.vf, V + head_v, N, blk.my_k, lv.sn, blk.g, 0u);
 
   // query tiles that can see these keys: from the diagonal to the end of the
   // last key's sliding window
@@ -408,11 +445,12 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
     else return true;
   };
   const uint16_t* q_h = Q + head;
-  const uint16_t* do_h = dO + head;
+  const uint16_t* do_h = dO + head_v;
   const float* nl_h = NLse + (int64_t)bh * N;
   const float* d_h = Dsum + (int64_t)bh * N;
-  uint32_t src[T::kPerWave];
+  uint32_t src[T::kPerWave], srcO[TO::kPerWave];
   T::sources(wave, lane, (uint32_t)(2 * in.sn), src);
+  TO::sources(wave, lane, (uint32_t)(2 * lv.sn), srcO);
   const uint32_t lds0 = lds_u32(smem);
 
   // the copies of query tile it into stage st (-LSE2 by wave 0, D by wave 1)
@@ -420,7 +458,7 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
     const int qt0 = it * kT;
     const uint32_t base = lds0 + (uint32_t)(st * Ld::kStage);
     copy_tile<D>(base + Ld::kQ, q_h, N, qt0, in.sn, wave, src);
-    copy_tile<D>(base + Ld::kDO, do_h, N, qt0, in.sn, wave, src);
+    copy_tile<DV>(base + Ld::kDO, do_h, N, qt0, lv.sn, wave, srcO);
     const int left = N - qt0;
     if (wave < 2) {
       const i32x4 rs = make_rsrc(wave == 0 ? nl_h + qt0 : d_h + qt0, left > 0 ? (uint32_t)left * 4u : 0u);
@@ -461,7 +499,7 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
     __syncthreads();
   }
   const bool store = kw0 < N && blk.my_k < N;
-  if (store) store_row<IsBf16, D>(dV + head_out, blk.my_k, out.sn, blk.g, blk.acc, 1.f);
+  if (store) store_row<IsBf16, DV>(dV + head_dv, blk.my_k, outv.sn, blk.g, blk.acc, 1.f);
   // ---- pass K; the first tile is already in stage n_it & 1
   blk.zero();
   for (int i = 0; i < n_it; ++i) {
@@ -491,25 +529,27 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
 //   P^T = exp2(c S^T - LSE2)                           (LSE2: lane scalar)
 //   pass 1:  D += sum over the keys of P^T dP^T
 //   pass 2:  dS^T = P^T (dP^T - D),  dQ^T += K^T dS^T  (A = K^T by transpose reads)
-template <int D> struct DqLds {
+template <int D, int DV = D> struct DqLds {
   static constexpr int kK = 0;
-  static constexpr int kV = STile<D>::kBytes;
-  static constexpr int kStage = 2 * STile<D>::kBytes;
+  static constexpr int kV = STile<D>::kBytes;                 // V rows of d_v
+  static constexpr int kStage = kV + STile<DV>::kBytes;
   static constexpr int kBytes = 2 * kStage;
 };
 
-template <bool IsBf16, int D, bool Causal, int Mode>
+template <bool IsBf16, int D, bool Causal, int Mode, int DV>
 __global__ __launch_bounds__(kThr, 2) void bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dsum,
     float* __restrict__ NLse, uint16_t* __restrict__ dQ, int N, int win, int H, int BH, int n_qblocks,
-    float c, float dq_mul, uint32_t q_sign, Layout in, Layout out, const uint8_t* __restrict__ bmask,
-    int64_t m_sb, int64_t m_sh) {
+    float c, float dq_mul, uint32_t q_sign, Layout in, Layout out, Layout lv,
+    const uint8_t* __restrict__ bmask, int64_t m_sb, int64_t m_sh) {
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using T = STile<D>;
-  using Ld = DqLds<D>;
-  constexpr int kKs = D / 16, kDB = D / 32;
+  using TO = STile<DV>;
+  using Ld = DqLds<D, DV>;
+  constexpr int kKs = D / 16, kDB = D / 32, kKsO = DV / 16;
+  if constexpr (DV == D) lv = in;  // one layout: the d_v addressing folds away
   constexpr bool kSparse = Mode == kModeSparse;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes + (kSparse ? kSparseBytes : 0)];
 
@@ -519,12 +559,12 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
   int qb = blockIdx.x / BH;
   if (Causal) qb = n_qblocks - 1 - qb;  // heaviest first
   const int b = bh / H, h = bh - b * H;
-  const int64_t head = b * in.sb + h * in.sh;
+  const int64_t head = b * in.sb + h * in.sh, head_v = b * lv.sb + h * lv.sh;
   const int q0 = qb * kRes, qw0 = q0 + 32 * wave, my_q = qw0 + l32;
 
-  vec8 qf[kKs], of[kKs];
+  vec8 qf[kKs], of[kKsO];
   load_resident<IsBf16, D>(qf, Q + head, N, my_q, in.sn, g, q_sign);
-  load_resident<IsBf16, D>(of, dO + head, N, my_q, in.sn, g, 0u);
+  load_resident<IsBf16, DV>(of, dO + head_v, N, my_q, lv.sn, g, 0u);
   const bool q_ok = my_q < N;
   const float lse2 = q_ok ? LSE[(int64_t)bh * N + my_q] * 1.4426950408889634f : INFINITY;
 
@@ -561,15 +601,16 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
   };
   const bool wave_live = qw0 < N;
   const uint16_t* k_h = K + head;
-  const uint16_t* v_h = V + head;
-  uint32_t src[T::kPerWave];
+  const uint16_t* v_h = V + head_v;
+  uint32_t src[T::kPerWave], srcO[TO::kPerWave];
   T::sources(wave, lane, (uint32_t)(2 * in.sn), src);
+  TO::sources(wave, lane, (uint32_t)(2 * lv.sn), srcO);
   const uint32_t lds0 = lds_u32(smem);
 
   auto issue = [&](int it, int st) {
     const uint32_t base = lds0 + (uint32_t)(st * Ld::kStage);
     copy_tile<D>(base + Ld::kK, k_h, N, it * kT, in.sn, wave, src);
-    copy_tile<D>(base + Ld::kV, v_h, N, it * kT, in.sn, wave, src);
+    copy_tile<DV>(base + Ld::kV, v_h, N, it * kT, lv.sn, wave, srcO);
   };
 
   // S^T and dP^T of key half kh of the tile in stage st, and P^T with the
@@ -581,9 +622,9 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
     dp = f32x16{};
     const int r = 32 * kh + l32;
 #pragma unroll
-    for (int kk = 0; kk < kKs; ++kk) {
-      s = E::mfma(row_frag<IsBf16, D>(k_lds, r, g, kk), qf[kk], s);
-      dp = E::mfma(row_frag<IsBf16, D>(v_lds, r, g, kk), of[kk], dp);
+    for (int kk = 0; kk < (kKs > kKsO ? kKs : kKsO); ++kk) {
+      if (kk < kKs) s = E::mfma(row_frag<IsBf16, D>(k_lds, r, g, kk), qf[kk], s);
+      if (kk < kKsO) dp = E::mfma(row_frag<IsBf16, DV>(v_lds, r, g, kk), of[kk], dp);
     }
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -658,7 +699,7 @@ __global__ __launch_bounds__(kThr, 2) void bwd_dq(
   store_row<IsBf16, D>(dQ + (b * out.sb + h * out.sh), my_q, out.sn, g, dq, dq_mul);
 }
 
-template <bool IsBf16, int D, bool Causal, int Mode>
+template <bool IsBf16, int D, bool Causal, int Mode, int DV = D>
 hipError_t launch(const BwdArgs& a, hipStream_t st) {
   const int N = (int)a.N;
   const int BH = (int)(a.B * a.H);
@@ -675,16 +716,16 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
   float* dsum = static_cast<float*>(a.workspace);
   float* nlse = dsum + a.B * a.H * a.N;
   // dQ (and D into the workspace) first; dK, dV read D afterwards on the same stream
-  hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal, Mode>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st, q,
+  hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal, Mode, DV>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st, q,
                      k, v, dout, a.lse, dsum, nlse, static_cast<uint16_t*>(a.dq), N, win, (int)a.H, BH,
-                     nblk, c, a.scale, q_sign, a.in, a.out, a.block_mask, a.mask_sb, a.mask_sh);
+                     nblk, c, a.scale, q_sign, a.in, a.out, a.lv, a.block_mask, a.mask_sb, a.mask_sh);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dK = scale dS^T Q; a negative scale flips the resident K instead of Q
-  hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal, Mode>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
+  hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal, Mode, DV>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
                      q, k, v, dout, nlse, dsum, static_cast<uint16_t*>(a.dk),
                      static_cast<uint16_t*>(a.dv), N, win, (int)a.H, BH, c, a.scale, q_sign, a.in, a.out,
-                     a.block_mask, a.mask_sb, a.mask_sh);
+                     a.lv, a.outv, a.block_mask, a.mask_sb, a.mask_sh);
   return hipGetLastError();
 }
 
@@ -701,6 +742,11 @@ hipError_t dispatch_d(const BwdArgs& a, hipStream_t s) {
 
 template <bool IsBf16>
 hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
+  // d_v != d (plain masks only): q, k, dq, dk rows of d, v, o, dout, dv rows of d_v
+  if (a.dvw == 64 && a.d == 128)
+    return a.causal ? launch<IsBf16, 128, true, kModePlain, 64>(a, s) : launch<IsBf16, 128, false, kModePlain, 64>(a, s);
+  if (a.dvw == 128 && a.d == 64)
+    return a.causal ? launch<IsBf16, 64, true, kModePlain, 128>(a, s) : launch<IsBf16, 64, false, kModePlain, 128>(a, s);
   if (a.d == 128) return dispatch_d<IsBf16, 128>(a, s);
   return a.d == 96 ? dispatch_d<IsBf16, 96>(a, s) : dispatch_d<IsBf16, 64>(a, s);
 }

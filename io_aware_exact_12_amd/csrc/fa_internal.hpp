@@ -61,6 +61,9 @@ struct BwdArgs {
   Layout out;      // dq, dk, dv
   const uint8_t* block_mask;  // as for FwdArgs
   int64_t mask_sb, mask_sh;
+  int64_t dvw;     // width of v, o, dout, dv rows (d_v; d except in the d_v != d call)
+  Layout lv;       // v, o, dout
+  Layout outv;     // dv
 };
 
 // Launchers return the hipError_t of the launch (hipSuccess when enqueued).

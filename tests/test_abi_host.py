@@ -30,12 +30,13 @@ def test_library_exports_every_declared_symbol():
     assert {"attn_fwd", "attn_bwd", "attn_fwd_window", "attn_bwd_window", "attn_bwd_workspace_bytes",
             "attn_fwd_kv_outer", "attn_fwd_kv_outer_workspace_bytes", "attn_fwd_strided",
             "attn_bwd_strided", "attn_fwd_block_sparse", "attn_bwd_block_sparse", "attn_fwd_dv",
+            "attn_bwd_dv",
             "fa_status_str",
             "fa_abi_version"} <= set(declared)
     lib = ctypes.CDLL(fa._binding.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
-    assert fa.lib().fa_abi_version() == 7
+    assert fa.lib().fa_abi_version() == 8
 
 
 def test_status_strings():
@@ -337,3 +338,20 @@ def test_dv_validation():
         assert fdv(d, dv, q=P[0] + 2) == FA_ERR_ALIGN, (d, dv)  # accepted: reaches the pointer checks
     assert fdv(128, 64, q=None) == FA_ERR_NULL
     assert fdv(64, 128, N=(1 << 23)) == FA_ERR_SHAPE           # v rows of a head span 2 GiB
+
+
+def test_bwd_dv_validation():
+    def bdv(d, dv, q=P[0], **kw):
+        a = dict(B=1, H=1, N=16, mask=0, scale=0.125, dtype=fa.BF16, ws=1 << 20)
+        a.update(kw)
+        return fa.attn_bwd_dv_raw(q, P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], a["B"], a["H"],
+                                  a["N"], d, dv, a["mask"], a["scale"], a["dtype"], P[1], a["ws"], None)
+    assert bdv(128, 0) == FA_ERR_SHAPE
+    for d, dv in ((128, 96), (96, 64), (64, 96), (128, 32), (64, 256)):
+        assert bdv(d, dv) == FA_ERR_UNSUPPORTED, (d, dv)
+    assert bdv(128, 64, dtype=fa.F32) == FA_ERR_UNSUPPORTED
+    assert bdv(128, 64, ws=8) == FA_ERR_WORKSPACE
+    for d, dv in ((128, 64), (64, 128), (128, 128), (96, 96)):
+        assert bdv(d, dv, q=P[0] + 2) == FA_ERR_ALIGN, (d, dv)  # accepted: reaches the pointer checks
+    assert bdv(128, 64, q=None) == FA_ERR_NULL
+    assert bdv(64, 128, N=(1 << 23), ws=1 << 40) == FA_ERR_SHAPE  # v rows of a head span 2 GiB

@@ -561,6 +561,22 @@ def test_backward_against_torch_autograd(causal):
         np.testing.assert_allclose(a, b.numpy(), rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("d,dv", [(8, 4), (4, 12)])
+def test_backward_dv_differs_from_d_against_torch_autograd(d, dv):
+    """Gradients with V (and dO) of width d_v != d against float64 autograd."""
+    q, k = _rand(2, 29, d, seed=181), _rand(2, 29, d, seed=182)
+    v, do = _rand(2, 29, dv, seed=183), _rand(2, 29, dv, seed=184)
+    for causal in (False, True):
+        dq, dk, dvg, o, _ = oracle.dense_bwd(q, k, v, do, causal=causal)
+        assert dq.shape == q.shape and dk.shape == k.shape and dvg.shape == v.shape
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+        to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal)
+        to.backward(torch.from_numpy(do))
+        np.testing.assert_allclose(o, to.detach().numpy(), rtol=1e-12, atol=1e-13)
+        for a, b in ((dq, tq.grad), (dk, tk.grad), (dvg, tv.grad)):
+            np.testing.assert_allclose(a, b.numpy(), rtol=1e-10, atol=1e-12)
+
+
 def test_backward_invariants():
     q, k, v, do = (_rand(2, 17, 6, seed=s) for s in (48, 49, 50, 51))
     for causal in (False, True):

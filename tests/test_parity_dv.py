@@ -1,10 +1,11 @@
-"""GPU parity of the forward with values of another width (attn_fwd_dv).
+"""GPU parity with values of another width (attn_fwd_dv, attn_bwd_dv).
 
-q and k are [B, H, N, d], v and o [B, H, N, dv] with (d, dv) in
-{(128, 64), (64, 128)}.  The HIP result is compared element by element with
-the float64 oracle (``oracle.dense_fwd``, which takes v of any width) on the
-same dtype-rounded inputs: O within 2e-2 + 1e-2 |ref| (fp16/bf16) or 1e-5
-(fp32), the fp32 LSE within 1e-4 + 1e-5 |ref|.
+q and k are [B, H, N, d], v, o and dout [B, H, N, dv] with (d, dv) in
+{(128, 64), (64, 128)}.  The HIP results are compared element by element with
+the float64 oracle (``oracle.dense_fwd`` and ``oracle.dense_bwd``, which take v
+of any width) on the same dtype-rounded inputs: O, dQ, dK, dV within
+2e-2 + 1e-2 |ref| (fp16/bf16) or 1e-5 (fp32), the fp32 LSE within
+1e-4 + 1e-5 |ref|.
 """
 import sys
 
@@ -80,3 +81,41 @@ def test_dv_long_head_sampled_rows(fa):
     ro, rl = oracle.dense_fwd(xq["q"], xq["k"], xv["v"], causal=True, rows=rows)
     compare("O", o.float().cpu().numpy()[:, :, rows], ro, "bf16")
     compare("LSE", lse.cpu().numpy()[:, :, rows], rl, "lse")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d,dv", [(128, 64), (64, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dv_backward_sweep(fa, dtype, d, dv, causal):
+    for i, n in enumerate([1, 31, 65, 257, 300, 777]):
+        seed = 9850 + n + d + dv + int(causal)
+        bh = (1, 2) if i % 2 else (2, 1)
+        log(f"case dv bwd dtype={dtype} d={d} dv={dv} causal={causal} B,H={bh} N={n} seed={seed}")
+        xq = workloads.random_inputs(bh[0], bh[1], n, d, dtype, seed)
+        xv = workloads.random_inputs(bh[0], bh[1], n, dv, dtype, seed + 1, with_do=True)
+        dev = lambda x: torch.from_numpy(x).to("cuda").to(TORCH_DT[dtype]).contiguous()
+        q, k, v, do = dev(xq["q"]), dev(xq["k"]), dev(xv["v"]), dev(xv["do"])
+        o, lse = fa.attn_fwd(q, k, v, causal=causal)
+        dq, dk, dvg = fa.attn_bwd(q, k, v, o, lse, do, causal=causal)
+        assert dq.shape == q.shape and dk.shape == k.shape and dvg.shape == v.shape
+        torch.cuda.synchronize()
+        rq, rk, rv, _, _ = oracle.dense_bwd(xq["q"], xq["k"], xv["v"], xv["do"], causal=causal)
+        for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dvg, rv)):
+            compare(name, g.float().cpu().numpy(), r, dtype)
+
+
+def test_dv_backward_long_head(fa):
+    """A longer head (B=1, H=2, N=2113, causal, bf16) for both pairs."""
+    n = 2113
+    for d, dv in ((128, 64), (64, 128)):
+        xq = workloads.random_inputs(1, 2, n, d, "bf16", 9993 + d)
+        xv = workloads.random_inputs(1, 2, n, dv, "bf16", 9994 + dv, with_do=True)
+        dev = lambda x: torch.from_numpy(x).to("cuda").to(torch.bfloat16).contiguous()
+        q, k, v, do = dev(xq["q"]), dev(xq["k"]), dev(xv["v"]), dev(xv["do"])
+        log(f"case dv bwd long head d={d} dv={dv}")
+        o, lse = fa.attn_fwd(q, k, v, causal=True)
+        dq, dk, dvg = fa.attn_bwd(q, k, v, o, lse, do, causal=True)
+        torch.cuda.synchronize()
+        rq, rk, rv, _, _ = oracle.dense_bwd(xq["q"], xq["k"], xv["v"], xv["do"], causal=True)
+        for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dvg, rv)):
+            compare(name, g.float().cpu().numpy(), r, "bf16")
