@@ -221,8 +221,9 @@ def sparse_record(fa, workloads, torch, steps, warmup):
 def variants_record(fa, workloads, torch, steps, warmup):
     """The bench head (B=1, H=16, N=8192, causal, bf16) in the other forms the
     library takes, each timed like the forward: a [B, N, H, d] view (strided
-    call), d = 96, d_v = 64 with d = 128, and the backward of the block-sparse
-    and sliding-window workloads (10 d FLOPs per visible pair)."""
+    call), d = 96, d = 256, d_v = 64 with d = 128 (forward and backward), and the
+    backward of the block-sparse and sliding-window workloads (10 d FLOPs per
+    visible pair)."""
     dev = torch.device("cuda:0")
     out = {}
     w = workloads.WORKLOADS[WORKLOAD]
@@ -247,6 +248,13 @@ def variants_record(fa, workloads, torch, steps, warmup):
     o96 = torch.empty_like(q96)
     rec("fwd_d96", lambda: fa.attn_fwd(q96, k96, v96, causal=True, out=o96),
         4 * 96 * (8192 * 8193 // 2) * 16)
+    # d = 256 (its own kernel)
+    x256 = workloads.random_inputs(1, 16, 8192, 256, "bf16", seed=13)
+    q256, k256, v256 = (dev_bf16(x256[n]).contiguous() for n in "qkv")
+    del x256
+    o256 = torch.empty_like(q256)
+    rec("fwd_d256", lambda: fa.attn_fwd(q256, k256, v256, causal=True, out=o256),
+        4 * 256 * (8192 * 8193 // 2) * 16)
     # d_v = 64 with d = 128: 2 d + 2 d_v FLOPs per visible pair
     xv = workloads.random_inputs(1, 16, 8192, 64, "bf16", seed=12)
     q, k = (dev_bf16(x[n]).contiguous() for n in "qk")
@@ -254,6 +262,15 @@ def variants_record(fa, workloads, torch, steps, warmup):
     o64 = torch.empty((1, 16, 8192, 64), dtype=torch.bfloat16, device=dev)
     rec("fwd_d128_dv64", lambda: fa.attn_fwd(q, k, v64, causal=True, out=o64),
         2 * (128 + 64) * (8192 * 8193 // 2) * 16)
+    # its backward: S, dQ, dK over d, dP, dV over d_v (6 d + 4 d_v FLOPs per visible pair)
+    lse64 = torch.empty((1, 16, 8192), dtype=torch.float32, device=dev)
+    fa.attn_fwd(q, k, v64, causal=True, out=o64, lse=lse64)
+    do64 = torch.randn_like(o64)
+    g64 = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v64)]
+    ws64 = torch.empty(fa.bwd_workspace_bytes(1, 16, 8192, 128, fa.BF16), dtype=torch.uint8, device=dev)
+    rec("bwd_d128_dv64", lambda: fa.attn_bwd(q, k, v64, o64, lse64, do64, causal=True, dq=g64[0],
+                                             dk=g64[1], dv=g64[2], workspace=ws64),
+        (6 * 128 + 4 * 64) * (8192 * 8193 // 2) * 16, s=20, wm=100)
     # backward of the block-sparse and the sliding-window workloads
     for name, wl in (("bwd_block_sparse", "long_sparse_bf16"), ("bwd_window", "long_window_bf16")):
         ww = workloads.WORKLOADS[wl]

@@ -57,7 +57,7 @@ enum fa_status {
   FA_ERR_DTYPE = 3,       /* dtype is not one of enum fa_dtype                  */
   FA_ERR_MASK = 4,        /* mask is not one of enum fa_mask                    */
   FA_ERR_SCALE = 5,       /* scale is NaN or infinite                           */
-  FA_ERR_UNSUPPORTED = 6, /* head dimension d is not 64, 96 or 128 (or fp32 backward) */
+  FA_ERR_UNSUPPORTED = 6, /* head dimension or variant not built (see each call) */
   FA_ERR_WORKSPACE = 7,   /* backward workspace missing or too small            */
   FA_ERR_HIP = 8,         /* the HIP runtime rejected a launch                  */
   FA_ERR_ALIGN = 9,       /* a tensor pointer is not 16-byte aligned            */
@@ -79,7 +79,13 @@ enum fa_status {
  *            separate quantities").  May be NULL, in which case it is not
  *            written.
  *   B, H, N  batch, heads, sequence length (queries and keys), each >= 1.
- *   d        head dimension of q, k and v: 64, 96 or 128.
+ *   d        head dimension of q, k and v: 64, 96, 128 or 256.  d = 256
+ *            takes FA_F16 or FA_BF16 (FA_ERR_UNSUPPORTED for FA_F32) and
+ *            runs a kernel of its own: one workgroup per CU that keeps the
+ *            256-wide accumulators of 128 queries in registers.  The calls
+ *            below that add a window narrower than N, a block mask, d_v != d,
+ *            the backward or the key/value-outer order return
+ *            FA_ERR_UNSUPPORTED for d = 256.
  *   mask     enum fa_mask.
  *   scale    finite multiplier of the raw dot products (any sign; usually
  *            1/sqrt(d)).
@@ -136,7 +142,8 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
  *   workspace         device memory of at least attn_bwd_workspace_bytes()
  *                     bytes, 16-byte aligned, owned by the caller; its
  *                     contents are scratch on return.
- *   mask, scale, B, H, N, d, stream: as for attn_fwd.
+ *   mask, scale, B, H, N, d, stream: as for attn_fwd (d = 256 returns
+ *                     FA_ERR_UNSUPPORTED, and attn_bwd_workspace_bytes 0).
  *   dtype             FA_F16 or FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED).
  *
  * Deterministic: no atomics are used.  FA_ERR_WORKSPACE if workspace is NULL

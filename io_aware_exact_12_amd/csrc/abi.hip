@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 // Block-sparse: mask blocks of 64 x 64; a query block of the forward lists at
 // most this many key tiles (its LDS list).
 constexpr int64_t kMaxSparseTiles = 2048;
@@ -29,7 +29,7 @@ int check_common(int64_t B, int64_t H, int64_t N, int64_t d, int mask, float sca
   const int64_t bh = B * H;
   if (bh > INT64_MAX / N || bh * N > INT64_MAX / 128 / 4) return FA_ERR_SHAPE;
   if (((N + 63) / 64) * bh > kMaxGrid) return FA_ERR_SHAPE;
-  if (d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 96 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   // one head of a dense [N][d] array must span less than 2 GiB (one buffer resource)
   if (N * d * (dtype == FA_F32 ? 4 : 2) > INT32_MAX - 1024) return FA_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
@@ -105,12 +105,18 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.mask_sb = mask_b == 1 ? 0 : mask_h * nb * nb;
   }
   a.lv = a.dv == d ? a.in : fa::dense_layout(H, N, a.dv);
+  // d = 256: bf16 / fp16, plain masks, d_v = d
+  if (d == 256 && (dtype == FA_F32 || a.window < N || block_mask != nullptr)) return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
     return FA_ERR_ALIGN;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (d == 256) {
+    e = dtype == FA_BF16 ? fa::launch_fwd_wide_bf16(a, s) : fa::launch_fwd_wide_f16(a, s);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
   switch (dtype) {
     case FA_BF16: e = fa::launch_fwd_bf16(a, s); break;
     case FA_F16: e = fa::launch_fwd_f16(a, s); break;
@@ -132,7 +138,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
     return FA_ERR_NULL;
   const int st = check_common(B, H, N, d, mask, scale, dtype);
   if (st != FA_OK) return st;
-  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32 || d == 256) return FA_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < fa::bwd_workspace_bytes(B, H, N))
     return FA_ERR_WORKSPACE;
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask == FA_MASK_CAUSAL, scale,
@@ -177,7 +183,7 @@ int kv_outer_impl(const void* q, const void* k, const void* v, void* o, float* l
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_NULL;
   const int st = check_common(B, H, N, d, mask, scale, dtype);
   if (st != FA_OK) return st;
-  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32 || d == 256) return FA_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < fa::kv_outer_workspace_bytes(B, H, N, d))
     return FA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace) ||
@@ -210,7 +216,7 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
-  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK) return 0;
+  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK || d == 256) return 0;
   return fa::bwd_workspace_bytes(B, H, N);
 }
 
@@ -253,7 +259,7 @@ int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse
                 int64_t H, int64_t N, int64_t d, int64_t dv, int mask, float scale, int dtype,
                 void* stream) {
   if (dv < 1) return FA_ERR_SHAPE;
-  if (dv != 64 && dv != 96 && dv != 128) return FA_ERR_UNSUPPORTED;
+  if (dv != 64 && dv != 96 && dv != 128 && dv != 256) return FA_ERR_UNSUPPORTED;
   if (N > 0 && N * dv * (dtype == FA_F32 ? 4 : 2) > INT32_MAX - 1024) return FA_ERR_SHAPE;
   return fwd_impl(q, k, v, o, lse, B, H, N, d, mask, N, scale, dtype, stream, nullptr, nullptr,
                   nullptr, nullptr, 0, 0, dv);
@@ -264,7 +270,7 @@ int attn_bwd_dv(const void* q, const void* k, const void* v, const void* o, cons
                 int64_t d, int64_t d_v, int mask, float scale, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream) {
   if (d_v < 1) return FA_ERR_SHAPE;
-  if (d_v != 64 && d_v != 96 && d_v != 128) return FA_ERR_UNSUPPORTED;
+  if (d_v != 64 && d_v != 96 && d_v != 128 && d_v != 256) return FA_ERR_UNSUPPORTED;
   if (N > 0 && N * d_v * (dtype == FA_F32 ? 4 : 2) > INT32_MAX - 1024) return FA_ERR_SHAPE;
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, N, scale, dtype, workspace,
                   workspace_bytes, stream, nullptr, nullptr, nullptr, 0, 0, d_v);
@@ -290,7 +296,8 @@ int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const voi
 }
 
 size_t attn_fwd_kv_outer_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
-  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK || dtype == FA_F32) return 0;
+  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK || dtype == FA_F32 || d == 256)
+    return 0;
   return fa::kv_outer_workspace_bytes(B, H, N, d);
 }
 

@@ -70,6 +70,9 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+// d = 256 forward (plain masks, d_v = d): one 4-wave workgroup per CU
+hipError_t launch_fwd_wide_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_wide_f16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_f16(const BwdArgs& a, hipStream_t s);
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N);

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(fa._binding.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
-    assert fa.lib().fa_abi_version() == 8
+    assert fa.lib().fa_abi_version() == 9
 
 
 def test_status_strings():
@@ -56,7 +56,7 @@ def test_bad_shapes(kw):
     assert fwd(**kw) == FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("d", [1, 32, 80, 127, 256])
+@pytest.mark.parametrize("d", [1, 32, 80, 127, 192, 257, 512])
 def test_unsupported_head_dim(d):
     assert fwd(d=d) == FA_ERR_UNSUPPORTED
 
@@ -355,3 +355,23 @@ def test_bwd_dv_validation():
         assert bdv(d, dv, q=P[0] + 2) == FA_ERR_ALIGN, (d, dv)  # accepted: reaches the pointer checks
     assert bdv(128, 64, q=None) == FA_ERR_NULL
     assert bdv(64, 128, N=(1 << 23), ws=1 << 40) == FA_ERR_SHAPE  # v rows of a head span 2 GiB
+
+
+def test_wide_head_validation():
+    """d = 256: the plain forward (bf16 / fp16) reaches the pointer checks; fp32
+    and every variant it does not take return FA_ERR_UNSUPPORTED."""
+    assert fwd(d=256, q=P[0] + 2) == FA_ERR_ALIGN
+    assert fwd(d=256, dtype=fa.F16, mask=1, q=P[0] + 2) == FA_ERR_ALIGN
+    assert fwd(d=256, dtype=fa.F32) == FA_ERR_UNSUPPORTED
+    assert fwd(d=256, N=(1 << 22)) == FA_ERR_SHAPE      # one head spans 2 GiB
+    assert fwd_w(4, d=256, N=64) == FA_ERR_UNSUPPORTED
+    assert fwd_w(64, d=256, N=64, q=P[0] + 2) == FA_ERR_ALIGN   # a window >= N is plain causal
+    assert fwd_bs(d=256) == FA_ERR_UNSUPPORTED
+    assert fa.attn_fwd_dv_raw(P[0], P[1], P[2], P[3], P[4], 1, 1, 16, 256, 128, 0, 0.1, fa.BF16,
+                              None) == FA_ERR_UNSUPPORTED
+    assert fa.attn_fwd_dv_raw(P[0] + 2, P[1], P[2], P[3], P[4], 1, 1, 16, 256, 256, 0, 0.1, fa.BF16,
+                              None) == FA_ERR_ALIGN
+    assert bwd(d=256) == FA_ERR_UNSUPPORTED
+    assert fa.bwd_workspace_bytes(1, 1, 16, 256, fa.BF16) == 0
+    assert kvo(d=256) == FA_ERR_UNSUPPORTED
+    assert fa.kv_outer_workspace_bytes(1, 1, 16, 256, fa.BF16) == 0
