@@ -83,9 +83,9 @@ enum fa_status {
  *            takes FA_F16 or FA_BF16 (FA_ERR_UNSUPPORTED for FA_F32) and
  *            runs a kernel of its own: one workgroup per CU that keeps the
  *            256-wide accumulators of 128 queries in registers.  The calls
- *            below that add a window narrower than N, a block mask, d_v != d,
- *            the backward or the key/value-outer order return
- *            FA_ERR_UNSUPPORTED for d = 256.
+ *            below that add a window narrower than N, a block mask, d_v != d
+ *            or the key/value-outer order return FA_ERR_UNSUPPORTED for
+ *            d = 256; attn_bwd and attn_bwd_strided take it.
  *   mask     enum fa_mask.
  *   scale    finite multiplier of the raw dot products (any sign; usually
  *            1/sqrt(d)).
@@ -142,8 +142,8 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
  *   workspace         device memory of at least attn_bwd_workspace_bytes()
  *                     bytes, 16-byte aligned, owned by the caller; its
  *                     contents are scratch on return.
- *   mask, scale, B, H, N, d, stream: as for attn_fwd (d = 256 returns
- *                     FA_ERR_UNSUPPORTED, and attn_bwd_workspace_bytes 0).
+ *   mask, scale, B, H, N, d, stream: as for attn_fwd (d = 256 runs the
+ *                     same two kernels at one workgroup per CU).
  *   dtype             FA_F16 or FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED).
  *
  * Deterministic: no atomics are used.  FA_ERR_WORKSPACE if workspace is NULL

@@ -138,7 +138,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
     return FA_ERR_NULL;
   const int st = check_common(B, H, N, d, mask, scale, dtype);
   if (st != FA_OK) return st;
-  if (dtype == FA_F32 || d == 256) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < fa::bwd_workspace_bytes(B, H, N))
     return FA_ERR_WORKSPACE;
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask == FA_MASK_CAUSAL, scale,
@@ -161,6 +161,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   a.dvw = d;
   a.lv = a.in;
   a.outv = a.out;
+  // d = 256: plain masks, d_v = d
+  if (d == 256 && (a.window < N || block_mask != nullptr || (dvw != 0 && dvw != d)))
+    return FA_ERR_UNSUPPORTED;
   if (dvw != 0 && dvw != d) {  // v, o, dout and dv rows of dvw elements, dense
     if (!((d == 128 && dvw == 64) || (d == 64 && dvw == 128))) return FA_ERR_UNSUPPORTED;
     a.dvw = dvw;
@@ -216,7 +219,7 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
-  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK || d == 256) return 0;
+  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK) return 0;
   return fa::bwd_workspace_bytes(B, H, N);
 }
 

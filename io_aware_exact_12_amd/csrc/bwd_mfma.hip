@@ -235,8 +235,12 @@ struct DkdvBlock {
   }
 };
 
+// Workgroups per CU: two below d = 256; at d = 256 one, so that each wave
+// may hold 512 registers (its resident operands alone take 128).
+template <int D> constexpr int kBwdOcc = D > 128 ? 1 : 2;
+
 template <bool IsBf16, int D, bool Causal, int Mode, int DV>
-__global__ __launch_bounds__(kThr, 2) void bwd_dkdv(
+__global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NLse, const float* __restrict__ Dsum,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int win, int H, int BH, float c,
@@ -390,7 +394,7 @@ template <int D, int DV = D> struct DqLds {
 };
 
 template <bool IsBf16, int D, bool Causal, int Mode, int DV>
-__global__ __launch_bounds__(kThr, 2) void bwd_dq(
+__global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dsum,
     float* __restrict__ NLse, uint16_t* __restrict__ dQ, int N, int win, int H, int BH, int n_qblocks,
@@ -600,6 +604,8 @@ hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
     return a.causal ? launch<IsBf16, 128, true, kModePlain, 64>(a, s) : launch<IsBf16, 128, false, kModePlain, 64>(a, s);
   if (a.dvw == 128 && a.d == 64)
     return a.causal ? launch<IsBf16, 64, true, kModePlain, 128>(a, s) : launch<IsBf16, 64, false, kModePlain, 128>(a, s);
+  if (a.d == 256)  // plain masks only
+    return a.causal ? launch<IsBf16, 256, true, kModePlain>(a, s) : launch<IsBf16, 256, false, kModePlain>(a, s);
   if (a.d == 128) return dispatch_d<IsBf16, 128>(a, s);
   return a.d == 96 ? dispatch_d<IsBf16, 96>(a, s) : dispatch_d<IsBf16, 64>(a, s);
 }

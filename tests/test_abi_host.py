@@ -358,8 +358,8 @@ def test_bwd_dv_validation():
 
 
 def test_wide_head_validation():
-    """d = 256: the plain forward (bf16 / fp16) reaches the pointer checks; fp32
-    and every variant it does not take return FA_ERR_UNSUPPORTED."""
+    """d = 256: the plain forward and backward (bf16 / fp16) reach the pointer
+    checks; fp32 and every variant they do not take return FA_ERR_UNSUPPORTED."""
     assert fwd(d=256, q=P[0] + 2) == FA_ERR_ALIGN
     assert fwd(d=256, dtype=fa.F16, mask=1, q=P[0] + 2) == FA_ERR_ALIGN
     assert fwd(d=256, dtype=fa.F32) == FA_ERR_UNSUPPORTED
@@ -371,7 +371,12 @@ def test_wide_head_validation():
                               None) == FA_ERR_UNSUPPORTED
     assert fa.attn_fwd_dv_raw(P[0] + 2, P[1], P[2], P[3], P[4], 1, 1, 16, 256, 256, 0, 0.1, fa.BF16,
                               None) == FA_ERR_ALIGN
-    assert bwd(d=256) == FA_ERR_UNSUPPORTED
-    assert fa.bwd_workspace_bytes(1, 1, 16, 256, fa.BF16) == 0
+    assert bwd(d=256, q=P[0] + 2) == FA_ERR_ALIGN
+    assert bwd(d=256, dtype=fa.F32) == FA_ERR_UNSUPPORTED
+    assert bwd_w(4, d=256, N=64) == FA_ERR_UNSUPPORTED
+    assert fa.attn_bwd_block_sparse_raw(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], 1, 1, 64,
+                                        256, P[7], 1, 1, 0, 0.1, fa.BF16, P[1], 1 << 20,
+                                        None) == FA_ERR_UNSUPPORTED
+    assert fa.bwd_workspace_bytes(1, 1, 16, 256, fa.BF16) == 8 * 16
     assert kvo(d=256) == FA_ERR_UNSUPPORTED
     assert fa.kv_outer_workspace_bytes(1, 1, 16, 256, fa.BF16) == 0

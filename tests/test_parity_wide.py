@@ -1,7 +1,7 @@
-"""GPU parity of the wide-head forward (d = 256, attn_fwd and attn_fwd_strided).
+"""GPU parity at head dim 256 (attn_fwd, attn_bwd and their strided calls).
 
 The HIP result is compared element by element with the float64 oracle
-(``oracle.dense_fwd``) on the same dtype-rounded inputs: O within
+(``oracle.dense_fwd``, ``oracle.dense_bwd``) on the same dtype-rounded inputs: O, dQ, dK, dV within
 2e-2 + 1e-2 |ref|, the fp32 LSE within 1e-4 + 1e-5 |ref|.  Lengths cover one
 row, ragged tails of the 64-key tiles and the 128-query blocks, several
 blocks, negative and zero scales, sharp rows whose maximum moves late, and a
@@ -110,3 +110,45 @@ def test_wide_long_head_sampled_rows(fa):
                                      np.random.default_rng(12301).integers(0, n, 24)]))
     log("case wide long head")
     run(fa, x, "bf16", True, rows=rows)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_backward_sweep(fa, dtype, causal):
+    """dQ, dK, dV at d = 256 against ``oracle.dense_bwd`` (same tolerance)."""
+    for i, n in enumerate([1, 31, 65, 129, 300, 777]):
+        seed = 12400 + 7 * n + int(causal)
+        bh = (1, 2) if i % 2 else (2, 1)
+        log(f"case wide bwd dtype={dtype} causal={causal} B,H={bh} N={n} seed={seed}")
+        x = workloads.random_inputs(bh[0], bh[1], n, D, dtype, seed, with_do=True)
+        q, k, v, do = (dev(x[m], dtype) for m in ("q", "k", "v", "do"))
+        o, lse = fa.attn_fwd(q, k, v, causal=causal)
+        dq, dk, dv = fa.attn_bwd(q, k, v, o, lse, do, causal=causal)
+        torch.cuda.synchronize()
+        rq, rk, rv, _, _ = oracle.dense_bwd(x["q"], x["k"], x["v"], x["do"], causal=causal)
+        for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            compare(name, g.float().cpu().numpy(), r, "o")
+
+
+def test_wide_backward_scales_and_bshd(fa):
+    """Negative and zero scale, and [B, N, H, d] views (the strided call)."""
+    x = workloads.random_inputs(1, 2, 333, D, "bf16", 12500, with_do=True)
+    q, k, v, do = (dev(x[m], "bf16") for m in ("q", "k", "v", "do"))
+    for scale in (-0.2, 0.0):
+        log(f"case wide bwd scale={scale}")
+        o, lse = fa.attn_fwd(q, k, v, causal=True, scale=scale)
+        dq, dk, dv = fa.attn_bwd(q, k, v, o, lse, do, causal=True, scale=scale)
+        torch.cuda.synchronize()
+        rq, rk, rv, _, _ = oracle.dense_bwd(x["q"], x["k"], x["v"], x["do"], causal=True, scale=scale)
+        for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            compare(name, g.float().cpu().numpy(), r, "o")
+    b, h, n = 2, 2, 300
+    x = workloads.random_inputs(b, h, n, D, "bf16", 12501, with_do=True)
+    q, k, v, do = (dev(x[m].transpose(0, 2, 1, 3), "bf16").transpose(1, 2) for m in ("q", "k", "v", "do"))
+    log("case wide bwd bshd")
+    o, lse = fa.attn_fwd(q, k, v, causal=True)
+    dq, dk, dv = fa.attn_bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    rq, rk, rv, _, _ = oracle.dense_bwd(x["q"], x["k"], x["v"], x["do"], causal=True)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        compare(name, g.float().cpu().numpy(), r, "o")
