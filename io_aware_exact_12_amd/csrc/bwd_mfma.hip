@@ -80,13 +80,17 @@ struct DkdvBlock {
   static constexpr int kKsO = DV / 16, kDBO = DV / 32;  // over d_v: dP = dO V^T, dV^T
   static constexpr int kDBA = kDB > kDBO ? kDB : kDBO;
   static constexpr int kMin = kKs < kKsO ? kKs : kKsO;
+  // Rows of 32 chunks (d = 256): the swizzle (< 16) never moves a chunk
+  // between the two 256-byte halves of a row, so the offsets of the second
+  // half are those of the first plus 256 and only the first half's are kept.
+  static constexpr int kRo = kKs > 8 ? 8 : kKs, kTo = kDB > 4 ? 4 : kDB;
 
   int lane, g, N, win, my_k;
   float c;
   vec8 kf[kKs], vf[kKsO];
   f32x16 acc[kDBA];       // dV^T in pass V, dK^T in pass K
-  int roff[kKs], roffO[kKsO];    // row operand of k step kk: LDS row l32, chunk 2 kk + g
-  int toff[2][kDB], toffO[2][kDBO];  // transpose reads (elements 0..3 / 4..7) of d block db
+  int roff[kRo], roffO[kKsO];    // row operand of k step kk: LDS row l32, chunk 2 kk + g
+  int toff[2][kTo], toffO[2][kDBO];  // transpose reads (elements 0..3 / 4..7) of d block db
 
   __device__ __forceinline__ void init(int lane_, int N_, int win_, int kw0, float c_) {
     lane = lane_;
@@ -96,7 +100,7 @@ struct DkdvBlock {
     g = lane >> 5;
     my_k = kw0 + (lane & 31);
 #pragma unroll
-    for (int kk = 0; kk < kKs; ++kk) roff[kk] = T::at(lane & 31, 2 * kk + g);
+    for (int kk = 0; kk < kRo; ++kk) roff[kk] = T::at(lane & 31, 2 * kk + g);
     if constexpr (DV != D) {
 #pragma unroll
       for (int kk = 0; kk < kKsO; ++kk) roffO[kk] = TO::at(lane & 31, 2 * kk + g);
@@ -104,7 +108,7 @@ struct DkdvBlock {
     const int grp = lane >> 4, s16 = lane & 15;
     const int r0 = 4 * g + (s16 >> 2);
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) {
+    for (int db = 0; db < kTo; ++db) {
       const int col = 2 * (16 * (grp & 1) + 4 * (s16 & 3)) + 64 * db;  // byte column
       toff[0][db] = T::at(r0, col >> 4) + (col & 15);
       toff[1][db] = T::at(r0 + 8, col >> 4) + (col & 15);
@@ -126,12 +130,12 @@ struct DkdvBlock {
   // Logical tile rows 16 t + 32 h keep their swizzle, so a half and a k step
   // only add whole-row offsets to the per-lane offsets above.
   __device__ __forceinline__ vec8 row_op(const uint8_t* tile, int h, int kk) const {
-    return *reinterpret_cast<const vec8*>(tile + roff[kk] + 32 * h * T::kRowBytes);
+    return *reinterpret_cast<const vec8*>(tile + roff[kk % kRo] + 256 * (kk / kRo) + 32 * h * T::kRowBytes);
   }
   __device__ __forceinline__ vec8 tr_op(const uint8_t* tile, int h, int t, int db) const {
-    const uint8_t* p = tile + (32 * h + 16 * t) * T::kRowBytes;
-    const auto lo = E::read_tr((const lds_void*)(p + toff[0][db]));
-    const auto hi = E::read_tr((const lds_void*)(p + toff[1][db]));
+    const uint8_t* p = tile + (32 * h + 16 * t) * T::kRowBytes + 256 * (db / kTo);
+    const auto lo = E::read_tr((const lds_void*)(p + toff[0][db % kTo]));
+    const auto hi = E::read_tr((const lds_void*)(p + toff[1][db % kTo]));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
   // the same two reads on a dO tile (d_v wide)
@@ -266,7 +270,10 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dkdv(
   DkdvBlock<IsBf16, D, Causal, Mode, DV> blk;
   blk.init(lane, N, win, kw0, c);
   load_resident<IsBf16, D>(blk.kf, K + head, N, blk.my_k, in.sn, blk.g, k_sign);
-  load_resident<IsBf16, DV>(blk.vf, V + head_v, N, blk.my_k, lv.sn, blk.g, 0u);
+  // V^T is used only in pass K; at d = 256 it is loaded there, which keeps
+  // its 64 registers free during pass V
+  constexpr bool kLateV = D > 128;
+  if constexpr (!kLateV) load_resident<IsBf16, DV>(blk.vf, V + head_v, N, blk.my_k, lv.sn, blk.g, 0u);
 
   // query tiles that can see these keys: from the diagonal to the end of the
   // last key's sliding window
@@ -357,6 +364,7 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dkdv(
   }
   const bool store = kw0 < N && blk.my_k < N;
   if (store) store_row<IsBf16, DV>(dV + head_dv, blk.my_k, outv.sn, blk.g, blk.acc, 1.f);
+  if constexpr (kLateV) load_resident<IsBf16, DV>(blk.vf, V + head_v, N, blk.my_k, lv.sn, blk.g, 0u);
   // ---- pass K; the first tile is already in stage n_it & 1
   blk.zero();
   for (int i = 0; i < n_it; ++i) {
