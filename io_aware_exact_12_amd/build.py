@@ -35,15 +35,17 @@ COMMON_FLAGS = [
 ]
 
 
-# Per-source flags.  The backward kernels at d = 256 run one wave per SIMD,
-# where the compiler would otherwise pick the AGPR form of the MFMAs and then
-# shuttle the accumulators between the two register files and scratch (2.4x
-# slower); with the VGPR form they stay in VGPRs and only overflow into
-# AGPRs.  Every kernel of the file that runs two waves per SIMD compiles to
-# the same instructions either way.  (The d = 256 forward measured 5 % faster
-# with the AGPR form and keeps it.)
+# Per-source flags.  The d = 256 kernels run one wave per SIMD, where the
+# compiler would otherwise pick the AGPR form of the MFMAs and then shuttle
+# accumulators between the two register files around the MFMAs or at every
+# loop iteration (and, in the backward, through scratch: 2.4x slower); with
+# the VGPR form they stay in VGPRs and only overflow into AGPRs.  Every
+# kernel of these files that runs two waves per SIMD compiles to the same
+# instructions either way.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 SOURCE_FLAGS = {
-    "bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "bwd_mfma.hip": _VGPR_FORM,
+    "fwd_wide.hip": _VGPR_FORM,
 }
 
 

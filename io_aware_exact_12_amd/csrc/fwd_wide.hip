@@ -9,18 +9,21 @@
 //
 // At d = 256 a 32-query wave needs 128 accumulator registers for O^T and 64
 // for its resident Q^T operands, so the kernel runs one 4-wave workgroup per
-// CU (one wave per SIMD, up to 512 registers a wave) and two K/V stages of
-// 64-key tiles (2 x 64 KB of LDS).  Per wave: 32 resident queries in the lane
-// column of 32x32x16 MFMAs; for each 32-key half of a tile
-//   S^T = K Q^T           (A = K rows from LDS, B = Q^T resident)
-//   P^T = exp2(c S^T - c m)  against a lazily raised reference m
-//   O^T += V^T P^T        (A = V^T by LDS transpose reads, B = P^T from registers)
-// The reference only moves when a block's maximum exceeds it by more than
-// kLazy (in log2 units): probabilities stay below 2^kLazy and the rescale of
-// the 128 accumulators is rare.  The result does not depend on the
-// reference, which only cancels between numerator and denominator.
+// CU: one wave per SIMD, up to 512 registers a wave.  With no second wave on
+// the SIMD, the wave overlaps its own MFMAs and softmax work: key blocks of 32
+// rows stream through a 4-stage LDS ring (K and V tiles of 16 KB each, in the
+// permuted, swizzled format of the streamed-tile helpers), and block u runs
+//   [its row maximum and reference check]  while PV(u-1) drains,
+//   [S(u+1) = K Q^T, 16 MFMAs] with the exp2, packing and row sums of P(u)
+//                                 placed between them,
+//   [O^T += V^T P^T of block u, 16 MFMAs].
+// The reference maximum only moves when a block's maximum exceeds it by more
+// than kLazy (log2 units): probabilities stay below 2^kLazy and the rescale of
+// the 128 accumulators is rare.  The result does not depend on the reference,
+// which cancels between numerator and denominator.
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <type_traits>
 
 #include "fa_internal.hpp"
 #include "mfma_common.hpp"
@@ -34,13 +37,29 @@ using namespace tiles;
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;
+constexpr int kB = 32;       // keys per block (one streamed tile)
+constexpr int kStages = 4;
 
-template <int D> struct WideLds {
-  static constexpr int kK = 0;
-  static constexpr int kV = STile<D>::kBytes;
-  static constexpr int kStage = 2 * STile<D>::kBytes;
-  static constexpr int kBytes = 2 * kStage;
+// A 32-row streamed tile: the first half of STile<D>'s format.
+template <int D> struct BlockTile {
+  using T = STile<D>;
+  static constexpr int kBytes = kB * T::kRowBytes;
+  static constexpr int kPerWave = kBytes / 1024 / kW;  // wave-wide 1 KB copies per wave
+  static_assert(kPerWave * kW * 1024 == kBytes, "tile copies split evenly over the waves");
+  static __device__ __forceinline__ void sources(int wave, int lane, uint32_t row_bytes,
+                                                 uint32_t (&src)[kPerWave]) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int byte = (wave + kW * i) * 1024 + 16 * lane;
+      const int r = byte / T::kRowBytes, phys = (byte % T::kRowBytes) / 16;
+      src[i] = (uint32_t)tile_row(r) * row_bytes + (uint32_t)(16 * (phys ^ T::swz(r)));
+    }
+  }
 };
+
+// MFMA slot of step st (0 scale, 1 exp2, 2 pack and partial sum) of score
+// pair e among the 16 score MFMAs of a block.
+constexpr int slot_of(int e, int st) { return e + (st == 0 ? 0 : st == 1 ? 2 : 5); }
 
 template <bool IsBf16, int D, bool Causal>
 __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
@@ -50,10 +69,12 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using T = STile<D>;
-  using Ld = WideLds<D>;
+  using BT = BlockTile<D>;
   constexpr int kKs = D / 16, kDB = D / 32;
-  static_assert(Ld::kBytes <= 160 * 1024, "two K/V stages fit the LDS");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes];
+  constexpr int kStage = 2 * BT::kBytes;  // K tile, then V tile
+  static_assert(kStages * kStage <= 160 * 1024, "the ring fits the LDS");
+  static_assert(kKs == 16, "the probability schedule spreads 8 score pairs over 16 MFMAs");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
 
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -66,84 +87,139 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
   vec8 qf[kKs];
   load_resident<IsBf16, D>(qf, Q + (b * lq.sb + h * lq.sh), N, my_q, lq.sn, g, q_sign);
 
+  // blocks of the workgroup, and the last one this wave computes
   const int last_row = min(N, q0 + kRes) - 1;
-  const int n_tiles = Causal ? last_row / kT + 1 : (N + kT - 1) / kT;
+  const int n_blk = Causal ? last_row / kB + 1 : (N + kB - 1) / kB;
   const bool wave_live = qw0 < N;
+  const int u_last = Causal ? min(qw0 + 31, N - 1) / kB : n_blk - 1;
   const int64_t head = b * in.sb + h * in.sh;
   const uint16_t* k_h = K + head;
   const uint16_t* v_h = V + head;
-  uint32_t src[T::kPerWave];
-  T::sources(wave, lane, (uint32_t)(2 * in.sn), src);
+  uint32_t src[BT::kPerWave];
+  BT::sources(wave, lane, (uint32_t)(2 * in.sn), src);
   const uint32_t lds0 = lds_u32(smem);
-  auto issue = [&](int it, int st) {
-    const uint32_t base = lds0 + (uint32_t)(st * Ld::kStage);
-    copy_tile<D>(base + Ld::kK, k_h, N, it * kT, in.sn, wave, src);
-    copy_tile<D>(base + Ld::kV, v_h, N, it * kT, in.sn, wave, src);
+  // copies of block u's K and V rows into its stage: 2 kPerWave per wave
+  auto issue = [&](int u) {
+    const int row0 = u * kB, left = N - row0;
+    const uint32_t bytes = left > 0 ? (uint32_t)(left - 1) * (uint32_t)(2 * in.sn) + (uint32_t)T::kDataBytes : 0u;
+    const i32x4 rk = make_rsrc(k_h + (int64_t)row0 * in.sn, bytes);
+    const i32x4 rv = make_rsrc(v_h + (int64_t)row0 * in.sn, bytes);
+    const uint32_t base = lds0 + (uint32_t)((u & (kStages - 1)) * kStage);
+#pragma unroll
+    for (int i = 0; i < BT::kPerWave; ++i) dma16(rk, base + (uint32_t)((wave + kW * i) * 1024), src[i]);
+#pragma unroll
+    for (int i = 0; i < BT::kPerWave; ++i)
+      dma16(rv, base + (uint32_t)(BT::kBytes + (wave + kW * i) * 1024), src[i]);
   };
+  auto k_tile = [&](int u) { return smem + (u & (kStages - 1)) * kStage; };
+  auto v_tile = [&](int u) { return smem + (u & (kStages - 1)) * kStage + BT::kBytes; };
 
   f32x16 acc[kDB];
 #pragma unroll
   for (int i = 0; i < kDB; ++i) acc[i] = f32x16{};
   float m = -INFINITY;  // reference: raw (sign-adjusted) score of this lane's query
   float l = 0.f;        // this lane half's share of the row sum, relative to m
+  f32x16 s_cur = f32x16{}, s_next = f32x16{};
 
-  issue(0, 0);
-  wait_copies();
+  for (int u = 0; u < kStages - 1 && u < n_blk; ++u) issue(u);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  for (int it = 0; it < n_tiles; ++it) {
-    const int st = it & 1;
-    if (it + 1 < n_tiles) issue(it + 1, st ^ 1);
-    const uint8_t* k_lds = smem + st * Ld::kStage + Ld::kK;
-    const uint8_t* v_lds = smem + st * Ld::kStage + Ld::kV;
-    if (wave_live) {
+  if (wave_live) {
+    const uint8_t* kt = k_tile(0);
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const int ks0 = it * kT + 32 * kh;
-        if ((Causal && ks0 > qw0 + 31) || ks0 >= N) continue;
-        // register rr of lane half g holds key ks0 + 16 (rr >> 3) + 8 g + (rr & 7)
-        f32x16 s = f32x16{};
-        const int r = 32 * kh + l32;
+    for (int kk = 0; kk < kKs; ++kk) s_cur = E::mfma(row_frag<IsBf16, D>(kt, l32, g, kk), qf[kk], s_cur);
+  }
+
+  for (int u = 0; u < n_blk; ++u) {
+    const bool more = u + kStages - 1 < n_blk;
+    if (more) issue(u + kStages - 1);  // into the stage block u-1 left
+    if (wave_live && u <= u_last) {
+      const int ks0 = u * kB;
+      // register rr of lane half g holds key ks0 + 16 (rr >> 3) + 8 g + (rr & 7)
+      if ((Causal && ks0 + kB - 1 > qw0) || ks0 + kB > N) {
 #pragma unroll
-        for (int kk = 0; kk < kKs; ++kk) s = E::mfma(row_frag<IsBf16, D>(k_lds, r, g, kk), qf[kk], s);
-        if ((Causal && ks0 + 31 > qw0) || ks0 + 32 > N) {
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int kj = ks0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
-            if (kj >= N || (Causal && kj > my_q)) s[rr] = -INFINITY;
-          }
+        for (int rr = 0; rr < 16; ++rr) {
+          const int kj = ks0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
+          if (kj >= N || (Causal && kj > my_q)) s_cur[rr] = -INFINITY;
         }
-        float mx = s[0];
-#pragma unroll
-        for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, s[rr]);
-        mx = xhalf_max(mx);
-        // (-inf) - (-inf) is NaN and compares false: a row that has seen no key
-        // yet keeps its reference until a block shows it one
-        if (__builtin_amdgcn_ballot_w64((mx - m) * c > kLazy) != 0) {
-          const float m_new = fmaxf(m, mx);
-          const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
-          l *= alpha;
-#pragma unroll
-          for (int db = 0; db < kDB; ++db) acc[db] *= alpha;
-          m = m_new;
-        }
-        const float neg_mc = m == -INFINITY ? 0.f : -m * c;
-        u32x4 pw[2];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e], c, neg_mc));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e + 1], c, neg_mc));
-          pw[e >> 2][e & 3] = E::pack2(p0, p1);
-          l += p0 + p1;
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int db = 0; db < kDB; ++db)
-            acc[db] = E::mfma(tr_frag<IsBf16, D>(v_lds, lane, 2 * kh + t, db),
-                              __builtin_bit_cast(vec8, pw[t]), acc[db]);
       }
+      float mx = s_cur[0];
+#pragma unroll
+      for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, s_cur[rr]);
+      mx = xhalf_max(mx);
+      // (-inf) - (-inf) is NaN and compares false: a row that has seen no key
+      // yet keeps its reference until a block shows it one
+      if (__builtin_amdgcn_ballot_w64((mx - m) * c > kLazy) != 0) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) acc[db] *= alpha;
+        m = m_new;
+      }
+      const float neg_mc = m == -INFINITY ? 0.f : -m * c;
+
+      // S(u+1) with P(u) between its MFMAs; a wave's last block forms no S
+      // (two copies of the loop, so that no branch sits between the MFMAs)
+      u32x4 pw[2];
+      float sum[2] = {0.f, 0.f};
+      auto phase_a = [&](auto next) {
+        constexpr bool kNext = decltype(next)::value;
+        const uint8_t* kt = k_tile(u + 1);
+        float pr[16];
+        vec8 ka[2];
+        if constexpr (kNext) {
+          ka[0] = row_frag<IsBf16, D>(kt, l32, g, 0);
+          ka[1] = row_frag<IsBf16, D>(kt, l32, g, 1);
+        }
+#pragma unroll
+        for (int t = 0; t < kKs; ++t) {
+          if constexpr (kNext) {
+            s_next = E::mfma(ka[t & 1], qf[t], t == 0 ? f32x16{} : s_next);
+            if (t + 2 < kKs) ka[t & 1] = row_frag<IsBf16, D>(kt, l32, g, t + 2);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (t == slot_of(e, 0)) {
+              pr[2 * e] = __builtin_fmaf(s_cur[2 * e], c, neg_mc);
+              pr[2 * e + 1] = __builtin_fmaf(s_cur[2 * e + 1], c, neg_mc);
+            }
+            if (t == slot_of(e, 1)) {
+              pr[2 * e] = __builtin_amdgcn_exp2f(pr[2 * e]);
+              pr[2 * e + 1] = __builtin_amdgcn_exp2f(pr[2 * e + 1]);
+            }
+            if (t == slot_of(e, 2)) {
+              pw[e >> 2][e & 3] = E::pack2(pr[2 * e], pr[2 * e + 1]);
+              sum[e & 1] += pr[2 * e] + pr[2 * e + 1];
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      if (u + 1 <= u_last)
+        phase_a(std::true_type{});
+      else
+        phase_a(std::false_type{});
+      l += sum[0] + sum[1];
+
+      // O^T += V^T P^T of block u; operand reads two MFMAs ahead
+      const uint8_t* vt = v_tile(u);
+      vec8 va[2] = {tr_frag<IsBf16, D>(vt, lane, 0, 0), tr_frag<IsBf16, D>(vt, lane, 0, 1)};
+#pragma unroll
+      for (int i = 0; i < 2 * kDB; ++i) {
+        const int tt = i / kDB, db = i % kDB;
+        acc[db] = E::mfma(va[i & 1], __builtin_bit_cast(vec8, pw[tt]), acc[db]);
+        if (i + 2 < 2 * kDB) va[i & 1] = tr_frag<IsBf16, D>(vt, lane, (i + 2) / kDB, (i + 2) % kDB);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s_cur = s_next;
     }
-    wait_copies();
+    // block u+2's tiles must be in LDS for S(u+2) in the next block; the
+    // copies just issued (block u+3) may stay in flight
+    if (more)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * BT::kPerWave));  // vmcnt(2 kPerWave)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
   if (!wave_live) return;
