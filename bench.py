@@ -295,7 +295,8 @@ def variants_record(fa, workloads, torch, steps, warmup):
             pairs = ww.pairs() * ww.H
         oo, ll = fa.attn_fwd(qq, kk, vv, causal=ww.causal, **kw)
         g = [torch.empty_like(qq) for _ in range(3)]
-        ws = torch.empty(fa.bwd_workspace_bytes(ww.B, ww.H, ww.N, ww.d, fa.BF16), dtype=torch.uint8,
+        wsq = fa.bwd_block_sparse_workspace_bytes if ww.sparse is not None else fa.bwd_workspace_bytes
+        ws = torch.empty(wsq(ww.B, ww.H, ww.N, ww.d, fa.BF16), dtype=torch.uint8,
                          device=dev)
         rec(name, lambda: fa.attn_bwd(qq, kk, vv, oo, ll, do, causal=ww.causal, dq=g[0], dk=g[1],
                                       dv=g[2], workspace=ws, **kw),

@@ -277,7 +277,17 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, 
  * mask_heads and mask).  Tiles hidden from every block of a workgroup are
  * skipped; rows that saw no key get dq = 0, keys no query saw get
  * dk = dv = 0.
+ *
+ * The workspace must hold attn_bwd_block_sparse_workspace_bytes() bytes
+ * (FA_ERR_WORKSPACE otherwise): besides attn_bwd's per-query terms, a counter
+ * per 128 keys and fp32 partial dK and dV of up to four chunks per key.  A
+ * key block that many query tiles see (a global block) has its tiles split
+ * over up to four workgroups of at least 32 tiles each; the last of them to
+ * finish adds the partials in chunk order, so the result is still the same
+ * bits on every call.  Calls that share a workspace must not overlap.
  */
+size_t attn_bwd_block_sparse_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
+
 int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
                           int64_t B, int64_t H, int64_t N, int64_t d,

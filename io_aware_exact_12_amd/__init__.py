@@ -10,5 +10,5 @@ from ._binding import (BF16, F16, F32, MASK_CAUSAL, MASK_NONE, FaError,  # noqa:
                        attn_fwd_strided_raw, attn_bwd_strided_raw, attn_fwd_block_sparse_raw,
                        attn_fwd_dv_raw, attn_bwd_dv_raw,
                        attn_bwd_block_sparse_raw,
-                       bwd_workspace_bytes, declared_symbols, kv_outer_workspace_bytes, lib,
+                       bwd_workspace_bytes, bwd_block_sparse_workspace_bytes, declared_symbols, kv_outer_workspace_bytes, lib,
                        status_str)

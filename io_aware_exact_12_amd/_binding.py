@@ -74,6 +74,8 @@ def lib():
         L.attn_fwd_kv_outer_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        L.attn_bwd_block_sparse_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_bwd_block_sparse_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.fa_status_str.restype = ctypes.c_char_p
         L.fa_status_str.argtypes = [ctypes.c_int]
         L.fa_abi_version.restype = ctypes.c_int
@@ -119,6 +121,10 @@ def attn_bwd_window_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, window, s
 
 def bwd_workspace_bytes(B, H, N, d, dtype_code):
     return lib().attn_bwd_workspace_bytes(B, H, N, d, dtype_code)
+
+
+def bwd_block_sparse_workspace_bytes(B, H, N, d, dtype_code):
+    return lib().attn_bwd_block_sparse_workspace_bytes(B, H, N, d, dtype_code)
 
 
 def _strides(st):
@@ -356,7 +362,8 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = bwd_workspace_bytes(B, H, N, d, code)
+    need = (bwd_block_sparse_workspace_bytes if block_mask is not None else bwd_workspace_bytes)(
+        B, H, N, d, code)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if stream is None:

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 9;
+constexpr int kAbiVersion = 10;
 // Block-sparse: mask blocks of 64 x 64; a query block of the forward lists at
 // most this many key tiles (its LDS list).
 constexpr int64_t kMaxSparseTiles = 2048;
@@ -139,8 +139,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   const int st = check_common(B, H, N, d, mask, scale, dtype);
   if (st != FA_OK) return st;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
-  if (workspace == nullptr || workspace_bytes < fa::bwd_workspace_bytes(B, H, N))
-    return FA_ERR_WORKSPACE;
+  const size_t need = block_mask != nullptr ? fa::bwd_sparse_workspace_bytes(B, H, N, d)
+                                            : fa::bwd_workspace_bytes(B, H, N);
+  if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask == FA_MASK_CAUSAL, scale,
                 workspace, window < N ? window : N, fa::dense_layout(H, N, d),
                 fa::dense_layout(H, N, d)};
@@ -286,6 +287,11 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, 
   if (block_mask == nullptr) return FA_ERR_NULL;
   return fwd_impl(q, k, v, o, lse, B, H, N, d, mask, N, scale, dtype, stream, nullptr, nullptr,
                   nullptr, block_mask, mask_batches, mask_heads);
+}
+
+size_t attn_bwd_block_sparse_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK || d == 256) return 0;
+  return fa::bwd_sparse_workspace_bytes(B, H, N, d);
 }
 
 int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,

@@ -239,6 +239,61 @@ struct DkdvBlock {
   }
 };
 
+// Block-sparse dK/dV: a key block that many query tiles see (a global block
+// of the mask) would leave one workgroup walking all of them.  Its list is
+// cut into up to kSplit chunks of at least kChunk tiles, each run by its own
+// workgroup, which writes fp32 partial dK^T and dV^T to the workspace; the
+// last of them to finish (a per-key-block counter, zeroed by the dQ kernel)
+// adds the partials in chunk order, so the result stays deterministic.
+constexpr int kSplit = 4, kChunk = 32;
+struct SplitArgs {
+  int* cnt;        // [B*H][key blocks of kRes], zeroed by bwd_dq each call
+  float* part_dv;  // [kSplit][B*H][N][d_v]
+  float* part_dk;  // [kSplit][B*H][N][d]
+};
+// Byte offsets of those arrays in the block-sparse workspace, after the
+// fp32 D and -LSE log2(e) of every query.
+struct SparseWs {
+  size_t cnt, part_dv, part_dk, bytes;
+  SparseWs(int64_t bh, int64_t n, int64_t d, int64_t dv) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    cnt = up((size_t)(8 * bh * n));
+    part_dv = up(cnt + (size_t)(4 * bh * ((n + kRes - 1) / kRes)));
+    part_dk = part_dv + (size_t)(4 * kSplit * bh * n * dv);
+    bytes = part_dk + (size_t)(4 * kSplit * bh * n * d);
+  }
+};
+
+// One lane's column of a transposed fp32 accumulator as row `row` of a dense
+// [.][D] fp32 array, and the sum of such rows over the first n slots.
+template <int D, int NA>
+__device__ __forceinline__ void store_row_f32(float* base, int row, int g, const f32x16 (&acc)[NA]) {
+  float* orow = base + (int64_t)row * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+      *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * gq + 4 * g) =
+          f32x4{acc[db][4 * gq], acc[db][4 * gq + 1], acc[db][4 * gq + 2], acc[db][4 * gq + 3]};
+}
+template <int D, int NA>
+__device__ __forceinline__ void sum_rows_f32(const float* base, int64_t slot, int n, int row, int g,
+                                             f32x16 (&acc)[NA]) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  for (int z = 0; z < n; ++z) {
+    const float* orow = base + z * slot + (int64_t)row * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(orow + db * 32 + 8 * gq + 4 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[db][4 * gq + j] += v[j];
+      }
+  }
+}
+
 // Workgroups per CU: two below d = 256; at d = 256 one, so that each wave
 // may hold 512 registers (its resident operands alone take 128).
 template <int D> constexpr int kBwdOcc = D > 128 ? 1 : 2;
@@ -249,7 +304,7 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dkdv(
     const uint16_t* __restrict__ dO, const float* __restrict__ NLse, const float* __restrict__ Dsum,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int win, int H, int BH, float c,
     float dk_mul, uint32_t k_sign, Layout in, Layout out, Layout lv, Layout outv,
-    const uint8_t* __restrict__ bmask, int64_t m_sb, int64_t m_sh) {
+    const uint8_t* __restrict__ bmask, int64_t m_sb, int64_t m_sh, SplitArgs split) {
   using T = STile<D>;
   using TO = STile<DV>;
   using Ld = DkdvLds<D, DV>;
@@ -260,7 +315,10 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dkdv(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int bh = blockIdx.x % BH, kblk = blockIdx.x / BH;  // heaviest (earliest keys) first
+  const int bh = blockIdx.x % BH;
+  // heaviest (earliest keys) first; block-sparse: the chunks of a key block together
+  const int kblk = kSparse ? blockIdx.x / BH / kSplit : blockIdx.x / BH;
+  const int z = kSparse ? blockIdx.x / BH % kSplit : 0;
   const int b = bh / H, h = bh - b * H;
   const int64_t head = b * in.sb + h * in.sh, head_out = b * out.sb + h * out.sh;
   const int64_t head_v = b * lv.sb + h * lv.sh, head_dv = b * outv.sb + h * outv.sh;
@@ -339,15 +397,26 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dkdv(
            kw0 + 32 > N;
   };
 
-  issue(tile_of(0), 0);
+  // list positions [i0, i1) of this workgroup (block-sparse chunks)
+  int i0 = 0, i1 = n_it, n_chunks = 1;
+  if constexpr (kSparse) {
+    n_chunks = min(kSplit, max(1, n_it / kChunk));
+    if (z >= n_chunks) return;  // workgroup-uniform
+    const int per = (n_it + n_chunks - 1) / n_chunks;
+    i0 = z * per;
+    i1 = min(n_it, i0 + per);
+  }
+  const int n_mine = i1 - i0;
+
+  issue(tile_of(i0), 0);
   wait_copies();
   __syncthreads();
   // ---- pass V
   blk.zero();
-  for (int i = 0; i < n_it; ++i) {
-    const int it = tile_of(i), st = i & 1;
+  for (int i = i0; i < i1; ++i) {
+    const int it = tile_of(i), st = (i - i0) & 1;
     // the next tile, or (after the last one) the first tile again for pass K
-    issue(tile_of(i + 1 < n_it ? i + 1 : 0), st ^ 1);
+    issue(tile_of(i + 1 < i1 ? i + 1 : i0), st ^ 1);
     if (live(it) && wave_sees(i)) {
       const uint8_t* sb = smem + st * Ld::kStage;
       const bool m = masked(it);
@@ -363,13 +432,18 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dkdv(
     __syncthreads();
   }
   const bool store = kw0 < N && blk.my_k < N;
-  if (store) store_row<IsBf16, DV>(dV + head_dv, blk.my_k, outv.sn, blk.g, blk.acc, 1.f);
+  const int64_t slot_v = (int64_t)BH * N * DV, slot_k = (int64_t)BH * N * D;
+  if (kSparse && n_chunks > 1) {
+    if (store) store_row_f32<DV>(split.part_dv + z * slot_v + (int64_t)bh * N * DV, blk.my_k, blk.g, blk.acc);
+  } else if (store) {
+    store_row<IsBf16, DV>(dV + head_dv, blk.my_k, outv.sn, blk.g, blk.acc, 1.f);
+  }
   if constexpr (kLateV) load_resident<IsBf16, DV>(blk.vf, V + head_v, N, blk.my_k, lv.sn, blk.g, 0u);
-  // ---- pass K; the first tile is already in stage n_it & 1
+  // ---- pass K; the first tile is already in stage n_mine & 1
   blk.zero();
-  for (int i = 0; i < n_it; ++i) {
-    const int it = tile_of(i), st = (i + n_it) & 1;
-    if (i + 1 < n_it) issue(tile_of(i + 1), st ^ 1);
+  for (int i = i0; i < i1; ++i) {
+    const int it = tile_of(i), st = (i - i0 + n_mine) & 1;
+    if (i + 1 < i1) issue(tile_of(i + 1), st ^ 1);
     if (live(it) && wave_sees(i)) {
       const uint8_t* sb = smem + st * Ld::kStage;
       const bool m = masked(it);
@@ -383,6 +457,23 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dkdv(
     }
     wait_copies();
     __syncthreads();
+  }
+  if (kSparse && n_chunks > 1) {
+    if (store) store_row_f32<D>(split.part_dk + z * slot_k + (int64_t)bh * N * D, blk.my_k, blk.g, blk.acc);
+    // the last chunk to finish adds the partials in chunk order
+    __threadfence();
+    __syncthreads();
+    int* flag = reinterpret_cast<int*>(smem);  // the stages are free: no copy is in flight
+    if (threadIdx.x == 0) flag[0] = atomicAdd(split.cnt + (int64_t)bh * ((N + kRes - 1) / kRes) + kblk, 1);
+    __syncthreads();
+    if (flag[0] != n_chunks - 1) return;
+    __threadfence();
+    if (!store) return;
+    sum_rows_f32<DV>(split.part_dv + (int64_t)bh * N * DV, slot_v, n_chunks, blk.my_k, blk.g, blk.acc);
+    store_row<IsBf16, DV>(dV + head_dv, blk.my_k, outv.sn, blk.g, blk.acc, 1.f);
+    sum_rows_f32<D>(split.part_dk + (int64_t)bh * N * D, slot_k, n_chunks, blk.my_k, blk.g, blk.acc);
+    store_row<IsBf16, D>(dK + head_out, blk.my_k, out.sn, blk.g, blk.acc, dk_mul);
+    return;
   }
   if (store) store_row<IsBf16, D>(dK + head_out, blk.my_k, out.sn, blk.g, blk.acc, dk_mul);
 }
@@ -407,7 +498,7 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dq(
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dsum,
     float* __restrict__ NLse, uint16_t* __restrict__ dQ, int N, int win, int H, int BH, int n_qblocks,
     float c, float dq_mul, uint32_t q_sign, Layout in, Layout out, Layout lv,
-    const uint8_t* __restrict__ bmask, int64_t m_sb, int64_t m_sh) {
+    const uint8_t* __restrict__ bmask, int64_t m_sb, int64_t m_sh, SplitArgs split) {
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using T = STile<D>;
@@ -425,6 +516,11 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dq(
   if (Causal) qb = n_qblocks - 1 - qb;  // heaviest first
   const int b = bh / H, h = bh - b * H;
   const int64_t head = b * in.sb + h * in.sh, head_v = b * lv.sb + h * lv.sh;
+  if constexpr (kSparse) {
+    // the dK/dV kernel's per-key-block chunk counters of this head start at zero
+    if (qb == 0)
+      for (int i = threadIdx.x; i < n_qblocks; i += kThr) split.cnt[(int64_t)bh * n_qblocks + i] = 0;
+  }
   const int q0 = qb * kRes, qw0 = q0 + 32 * wave, my_q = qw0 + l32;
 
   vec8 qf[kKs], of[kKsO];
@@ -577,20 +673,29 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
   const auto* k = static_cast<const uint16_t*>(a.k);
   const auto* v = static_cast<const uint16_t*>(a.v);
   const auto* dout = static_cast<const uint16_t*>(a.dout);
-  // workspace: D, then -LSE * log2(e), one fp32 per query each
+  // workspace: D, then -LSE * log2(e), one fp32 per query each; block-sparse
+  // also the chunk counters and partial sums
   float* dsum = static_cast<float*>(a.workspace);
   float* nlse = dsum + a.B * a.H * a.N;
+  SplitArgs split{nullptr, nullptr, nullptr};
+  if constexpr (Mode == kModeSparse) {
+    const SparseWs w(a.B * a.H, a.N, D, DV);
+    char* base = static_cast<char*>(a.workspace);
+    split = SplitArgs{reinterpret_cast<int*>(base + w.cnt), reinterpret_cast<float*>(base + w.part_dv),
+                      reinterpret_cast<float*>(base + w.part_dk)};
+  }
+  const int kgrid = Mode == kModeSparse ? nblk * BH * kSplit : nblk * BH;
   // dQ (and D into the workspace) first; dK, dV read D afterwards on the same stream
   hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal, Mode, DV>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st, q,
                      k, v, dout, a.lse, dsum, nlse, static_cast<uint16_t*>(a.dq), N, win, (int)a.H, BH,
-                     nblk, c, a.scale, q_sign, a.in, a.out, a.lv, a.block_mask, a.mask_sb, a.mask_sh);
+                     nblk, c, a.scale, q_sign, a.in, a.out, a.lv, a.block_mask, a.mask_sb, a.mask_sh, split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dK = scale dS^T Q; a negative scale flips the resident K instead of Q
-  hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal, Mode, DV>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
+  hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal, Mode, DV>), dim3((unsigned)kgrid), dim3(kThr), 0, st,
                      q, k, v, dout, nlse, dsum, static_cast<uint16_t*>(a.dk),
                      static_cast<uint16_t*>(a.dv), N, win, (int)a.H, BH, c, a.scale, q_sign, a.in, a.out,
-                     a.lv, a.outv, a.block_mask, a.mask_sb, a.mask_sh);
+                     a.lv, a.outv, a.block_mask, a.mask_sb, a.mask_sh, split);
   return hipGetLastError();
 }
 
@@ -621,6 +726,9 @@ hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
 }  // namespace
 
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) { return (size_t)(B * H * N) * 8; }
+size_t bwd_sparse_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  return SparseWs(B * H, N, d, d).bytes;
+}
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) { return dispatch<true>(a, s); }
 hipError_t launch_bwd_f16(const BwdArgs& a, hipStream_t s) { return dispatch<false>(a, s); }
 

@@ -76,6 +76,9 @@ hipError_t launch_fwd_wide_f16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_f16(const BwdArgs& a, hipStream_t s);
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N);
+// Block-sparse backward: also chunk counters and fp32 partial dK, dV of up to
+// four chunks of every key's query-tile list.
+size_t bwd_sparse_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 // Key/value-outer forward (the comparison loop order): fp32 row state
 // (O, m, l) of B*H*N rows in ws.
 hipError_t launch_fwd_kv_outer_bf16(const FwdArgs& a, void* ws, hipStream_t s);

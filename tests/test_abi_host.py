@@ -30,13 +30,13 @@ def test_library_exports_every_declared_symbol():
     assert {"attn_fwd", "attn_bwd", "attn_fwd_window", "attn_bwd_window", "attn_bwd_workspace_bytes",
             "attn_fwd_kv_outer", "attn_fwd_kv_outer_workspace_bytes", "attn_fwd_strided",
             "attn_bwd_strided", "attn_fwd_block_sparse", "attn_bwd_block_sparse", "attn_fwd_dv",
-            "attn_bwd_dv",
+            "attn_bwd_dv", "attn_bwd_block_sparse_workspace_bytes",
             "fa_status_str",
             "fa_abi_version"} <= set(declared)
     lib = ctypes.CDLL(fa._binding.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
-    assert fa.lib().fa_abi_version() == 9
+    assert fa.lib().fa_abi_version() == 10
 
 
 def test_status_strings():
@@ -311,7 +311,7 @@ def test_block_sparse_validation():
 
 def test_block_sparse_backward_validation():
     def bb(mask_ptr=P[7], mb=1, mh=1, **kw):
-        a = dict(q=P[0], B=2, H=3, N=200, d=64, mask=0, scale=0.125, dtype=fa.BF16, ws=1 << 20)
+        a = dict(q=P[0], B=2, H=3, N=200, d=64, mask=0, scale=0.125, dtype=fa.BF16, ws=1 << 24)
         a.update(kw)
         return fa.attn_bwd_block_sparse_raw(a["q"], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0],
                                             a["B"], a["H"], a["N"], a["d"], mask_ptr, mb, mh, a["mask"],
@@ -380,3 +380,24 @@ def test_wide_head_validation():
     assert fa.bwd_workspace_bytes(1, 1, 16, 256, fa.BF16) == 8 * 16
     assert kvo(d=256) == FA_ERR_UNSUPPORTED
     assert fa.kv_outer_workspace_bytes(1, 1, 16, 256, fa.BF16) == 0
+
+
+def test_block_sparse_backward_workspace():
+    """The block-sparse backward needs, past attn_bwd's 8 bytes per query, a
+    counter per 128 keys and fp32 partial dK and dV of four chunks per key,
+    each array on a 256-byte boundary."""
+    up = lambda x: (x + 255) // 256 * 256
+    for B, H, N, d in ((1, 16, 8192, 128), (2, 3, 200, 64), (1, 1, 1, 96)):
+        bh = B * H
+        cnt = up(8 * bh * N)
+        part = up(cnt + 4 * bh * (-(-N // 128)))
+        want = part + 4 * 4 * bh * N * 2 * d
+        assert fa.bwd_block_sparse_workspace_bytes(B, H, N, d, fa.BF16) == want
+    assert fa.bwd_block_sparse_workspace_bytes(1, 1, 16, 80, fa.BF16) == 0
+    assert fa.bwd_block_sparse_workspace_bytes(1, 1, 16, 256, fa.BF16) == 0
+    need = fa.bwd_block_sparse_workspace_bytes(2, 3, 200, 64, fa.BF16)
+    def bb(ws):
+        return fa.attn_bwd_block_sparse_raw(P[0] + 2, P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], 2, 3,
+                                            200, 64, P[7], 1, 1, 0, 0.125, fa.BF16, P[1], ws, None)
+    assert bb(need - 1) == FA_ERR_WORKSPACE
+    assert bb(need) == FA_ERR_ALIGN        # big enough: reaches the pointer checks

@@ -144,3 +144,27 @@ def test_block_sparse_backward_sweep(fa, dtype, d, causal):
             f"mask {mb}x{mh} density={dens} seed={seed}")
         x = workloads.random_inputs(b, h, n, d, dtype, seed, with_do=True)
         bwd_case(fa, x, dtype, causal, random_mask(mb, mh, n, dens, seed + 1, empty_row=(i == 2)))
+
+
+def test_block_sparse_backward_split_key_blocks(fa):
+    """Key blocks whose query-tile lists are long enough to be split over
+    several dK/dV workgroups (global blocks of the mask recipe; an all-ones
+    mask, where every key block splits), against the oracle, and the split
+    result bitwise equal on a second call (the partials are added in chunk
+    order)."""
+    cases = [(4096, 2, False, workloads.block_sparse_mask(4096, 2, 1, 2, 3, seed=9950)),  # 2 chunks
+             (6144, 1, True, workloads.block_sparse_mask(6144, 1, 1, 2, 3, seed=9951)),   # 3 chunks
+             (4096, 1, False, np.ones((1, 1, 64, 64), np.uint8))]                       # all split
+    for n, h, causal, mask in cases:
+        log(f"case block-sparse bwd split N={n} H={h} causal={causal} density={mask.mean():.3f}")
+        x = workloads.random_inputs(1, h, n, 128, "bf16", 9960 + n + h, with_do=True)
+        bwd_case(fa, x, "bf16", causal, mask)
+    n, h, causal, mask = cases[0]
+    x = workloads.random_inputs(1, h, n, 128, "bf16", 9960 + n + h, with_do=True)
+    q, k, v, do = (torch.from_numpy(x[m]).to("cuda").to(torch.bfloat16).contiguous() for m in ("q", "k", "v", "do"))
+    bm = torch.from_numpy(np.ascontiguousarray(mask)).to("cuda")
+    o, lse = fa.attn_fwd(q, k, v, block_mask=bm)
+    g1 = fa.attn_bwd(q, k, v, o, lse, do, block_mask=bm)
+    g2 = fa.attn_bwd(q, k, v, o, lse, do, block_mask=bm)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
