@@ -72,10 +72,12 @@ def cpu_baseline(w, x, budget_s=12.0):
     import numpy as np
 
     import oracle
+    blas = "unknown"
     try:
         import threadpoolctl
-        threads = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) \
-            if threadpoolctl.threadpool_info() else 1
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        threads = max(int(i.get("num_threads", 1)) for i in info) if info else 1
+        blas = ", ".join(sorted({str(i.get("internal_api")) for i in info})) or blas
     except Exception:  # threadpoolctl missing or no BLAS pool found
         threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
@@ -90,7 +92,8 @@ def cpu_baseline(w, x, budget_s=12.0):
     flops = 4.0 * w.d * pairs * heads
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"dense float64 oracle on {heads} of {w.B * w.H} heads (all {w.N} rows each, "
-                      f"full N x N scores computed, causal-visible FLOPs counted), {dt:.1f} s"}
+                      f"full N x N scores computed, causal-visible FLOPs counted), {dt:.1f} s",
+            "seconds": round(dt, 3), "blas": blas, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
 def time_graph(step, steps, warmup, torch):
@@ -449,6 +452,7 @@ def main():
                                                       args.kv_warmup)
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(w, x)
+        record["cpu_baseline"]["gpu_over_cpu"] = round(record["value"] / record["cpu_baseline"]["value"], 1)
     print(json.dumps(record), flush=True)
 
 
