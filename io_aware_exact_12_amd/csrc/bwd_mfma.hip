@@ -574,9 +574,10 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dq(
     copy_tile<DV>(base + Ld::kV, v_h, N, it * kT, lv.sn, wave, srcO);
   };
 
-  // S^T and dP^T of key half kh of the tile in stage st, and P^T with the
-  // masks applied; register e of lane half g holds key ks0 + 16 (e >> 3) + 8 g + (e & 7).
-  auto scores = [&](int st, int kh, int ks0, f32x16& p, f32x16& dp) {
+  // S^T and dP^T of key half kh of the tile in stage st, and P^T, with the
+  // masks applied when `masked` holds; register e of lane half g holds key
+  // ks0 + 16 (e >> 3) + 8 g + (e & 7).
+  auto scores = [&](auto masked, int st, int kh, int ks0, f32x16& p, f32x16& dp) {
     const uint8_t* k_lds = smem + st * Ld::kStage + Ld::kK;
     const uint8_t* v_lds = smem + st * Ld::kStage + Ld::kV;
     f32x16 s = f32x16{};
@@ -591,8 +592,24 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dq(
     for (int rr = 0; rr < 16; ++rr) {
       const int kj = ks0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
       const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c, -lse2));
-      p[rr] = (kj >= N || (Causal && kj > my_q) || (kWin && kj <= my_q - win)) ? 0.f : pr;
+      if constexpr (decltype(masked)::value)
+        p[rr] = (kj >= N || (Causal && kj > my_q) || (kWin && kj <= my_q - win)) ? 0.f : pr;
+      else
+        p[rr] = pr;
     }
+  };
+  // Whether key half ks0 .. ks0 + 31 hides some key from some query of this
+  // wave (causal diagonal, left edge of the window, end of the sequence); the
+  // other halves skip the per-element masks.  Rows past N need none: their
+  // LSE is +inf, so their probabilities are 0.
+  auto needs_mask = [&](int ks0) {
+    return (Causal && ks0 + 31 > qw0) || (kWin && ks0 <= qw0 + 31 - win) || ks0 + 32 > N;
+  };
+  auto scores_at = [&](int st, int kh, int ks0, f32x16& p, f32x16& dp) {
+    if (needs_mask(ks0))
+      scores(BoolTag<true>{}, st, kh, ks0, p, dp);
+    else
+      scores(BoolTag<false>{}, st, kh, ks0, p, dp);
   };
 
   // ---- pass 1: D = sum_j P_ij dP_ij
@@ -611,7 +628,7 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dq(
         const int ks0 = kt0 + 32 * kh;
         if ((Causal && ks0 > qw0 + 31) || (kWin && ks0 + 31 <= qw0 - win) || ks0 >= N) continue;
         f32x16 p, dp;
-        scores(st, kh, ks0, p, dp);
+        scores_at(st, kh, ks0, p, dp);
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) dpart = __builtin_fmaf(p[rr], dp[rr], dpart);
       }
@@ -639,7 +656,7 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dq(
         const int ks0 = kt0 + 32 * kh;
         if ((Causal && ks0 > qw0 + 31) || (kWin && ks0 + 31 <= qw0 - win) || ks0 >= N) continue;
         f32x16 p, dp;
-        scores(st, kh, ks0, p, dp);
+        scores_at(st, kh, ks0, p, dp);
         u32x4 sw[2];
 #pragma unroll
         for (int e = 0; e < 16; e += 2)
