@@ -71,7 +71,7 @@ constexpr float kSumCap = 256.0f;
 constexpr float kNoRef = 1e30f;
 // Masks a block of scores may need: none, the causal diagonal and the
 // sequence end, or those and the left edge of a sliding window.
-constexpr int kMaskNone = 0, kMaskEdge = 1, kMaskWindow = 2, kMaskSparse = 3;
+constexpr int kMaskNone = 0, kMaskEdge = 1, kMaskWindow = 2;
 // Block-sparse: a workgroup's list of key tiles (index | query-block bits <<
 // 16, see compact_tiles) lives in LDS after the rings.
 
@@ -145,6 +145,7 @@ struct FwdBlock {
   // of this wave's 64-row query block in a list entry
   const uint32_t* tiles;
   int n_pos, qbit;
+  bool live;  // block-sparse: the wave computed the previous list position
   float c;
   uint32_t src_k[kFullK], src_v[kFullV], src_x;  // per-lane source offsets of the copies
   // The extra copy writes LDS byte x_off + (K stage offset & x_kmask) +
@@ -264,10 +265,10 @@ struct FwdBlock {
     m_ref = -INFINITY;
     neg_mc = kNoRef;
     l_part = 0.f;
-    if (kWin) {
-      // A wave whose window starts after the workgroup's first step begins
-      // with a normal block: zeros make its PV MFMAs add 0 and send it down
-      // the reference-update path.
+    if (kWin || kSparse) {
+      // A wave whose window starts after the workgroup's first step (or a
+      // block-sparse run) begins with a normal block: zeros make its PV MFMAs
+      // add 0, and kNoRef sends it down the reference-update path.
       s_cur = f32x16{};
       p_prev[0] = p_prev[1] = u32x4{};
 #pragma unroll
@@ -327,16 +328,12 @@ struct FwdBlock {
 
   // Hide keys of block u that this lane's query may not see: the causal
   // diagonal and the sequence end; with kMaskWindow also keys left of the
-  // query's sliding window; with kMaskSparse the whole block when the mask
-  // hides its tile from this wave's query block.
+  // query's sliding window.
   template <int kMask>
   __device__ __forceinline__ void apply_mask(int u, f32x16& st) const {
     // register r of lane half g holds key kpos(u) + 16 (r >> 3) + 8 g + (r & 7)
     const int k0 = kpos(u);
-    int lim = (Causal ? min(my_q, N - 1) : N - 1) - k0 - 8 * g;
-    if (kMask == kMaskSparse && (u >> 1) < n_pos &&
-        ((tiles[u >> 1] >> qbit) & 1u) == 0)
-      lim = -1;  // the whole block is hidden from this wave
+    const int lim = (Causal ? min(my_q, N - 1) : N - 1) - k0 - 8 * g;
     const int lo = my_q - win + 1 - k0 - 8 * g;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -534,16 +531,10 @@ struct FwdBlock {
   // wave to overlap its MFMAs and VALU work.  So a wave's priority falls as it
   // gets through the step (3 at the start, 2, 1, 0 at each half block): the
   // wave that is behind issues first and the pair stays level.
-  //
-  // Block-sparse: j is the position in the workgroup's tile list; stages
-  // follow positions, and the copies fetch the listed tiles.
   template <int kMask, bool kFirstStep = false>
   __device__ __forceinline__ void step(int j) {
     __builtin_amdgcn_s_setprio(3);
-    if (kSparse)
-      load_tiles(tile_at(j + 3), (j + 3) & 3, tile_at(j + 2), (j + 2) & 3);
-    else
-      load_tiles(j + 3, (j + 3) & 3, j + 2, (j + 2) & 3);
+    load_tiles(j + 3, (j + 3) & 3, j + 2, (j + 2) & 3);
     if (kFirstStep) {
       if (u_lo == 2 * j && u_lo < n_sub) block<kMask, true, 0>(2 * j);
       if (u_lo == 2 * j + 1 && u_lo < n_sub)
@@ -555,6 +546,38 @@ struct FwdBlock {
       if (u >= u_lo && u < n_sub) block<kMask, false, 0>(u);
       if (u + 1 >= u_lo && u + 1 < n_sub) block<kMask, false, 1>(u + 1);
     }
+    __builtin_amdgcn_s_setprio(0);
+    wait_older_copies();
+    __syncthreads();
+  }
+
+  // Whether this wave's 64-row query block sees the tile at list position p
+  // (wave-uniform).
+  __device__ __forceinline__ bool sees(int p) const {
+    return p < n_pos && q0 < N &&
+           ((__builtin_amdgcn_readfirstlane((int)tiles[p]) >> qbit) & 1) != 0;
+  }
+
+  // Block-sparse tile step j (list position j).  A wave computes the two
+  // blocks of the tile only if its query block sees it, so each wave walks
+  // runs of visible positions and sits out the rest.  A run's first block
+  // forms its own scores from the resident K tile (the prefetched ones belong
+  // to a hidden block); its PV MFMAs are those the previous run's last block
+  // left pending (zeros before the first run), so nothing is drained between
+  // runs.  A row without a reference yet (kNoRef) takes the block's
+  // reference-update path.  A visible tile needs no block mask, only the
+  // causal and sequence-end masks.  The copies and the barrier are the
+  // workgroup's, as in step().
+  __device__ __forceinline__ void sparse_step(int j) {
+    __builtin_amdgcn_s_setprio(3);
+    load_tiles(tile_at(j + 3), (j + 3) & 3, tile_at(j + 2), (j + 2) & 3);
+    const bool vis = sees(j);
+    if (vis) {
+      if (!live) s_cur = scores<kMaskNone>(2 * j);
+      block<kMaskEdge, false, 0>(2 * j);
+      block<kMaskEdge, false, 1>(2 * j + 1);
+    }
+    live = vis;
     __builtin_amdgcn_s_setprio(0);
     wait_older_copies();
     __syncthreads();
@@ -586,17 +609,15 @@ struct FwdBlock {
     if constexpr (kSparse) {
       build_tile_list(list, mask, q0_blk);
       tiles = list;
-      n_sub = q0 >= N ? 0 : 2 * n_pos;  // every wave walks the whole list
       // prologue as below, by list position
       load_tiles(tile_at(0), 0, tile_at(0), 0);
       load_tiles(tile_at(1), 1, tile_at(1), 1);
       load_tiles(tile_at(2), 2, n_tiles, 3);
       wait_older_copies();
       __syncthreads();
-      if (n_sub > 0) s_cur = scores<kMaskNone>(0);
-      if (n_pos > 0) step<kMaskSparse, true>(0);
-      for (int j = 1; j < n_pos; ++j) step<kMaskSparse>(j);
-      if (n_sub > 0) drain();
+      live = false;
+      for (int j = 0; j < n_pos; ++j) sparse_step(j);
+      drain();  // the last run's last block (adds 0 if the wave saw nothing)
       return;
     }
     const int j_lo = kWin ? max(0, q0_blk - win + 1) / kBN : 0;

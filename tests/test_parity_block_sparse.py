@@ -86,6 +86,26 @@ def test_block_sparse_sweep(fa, dtype, d, causal):
         run_case(fa, x, dtype, causal, random_mask(mb, mh, n, dens, seed + 1, empty_row=(i == 3)))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_alternating_runs_sharp_rows(fa, causal):
+    """Each query block sees runs of two key tiles separated by two hidden ones,
+    shifted from block to block, so the four query blocks of a workgroup walk
+    different runs of one tile list and every run after the first restarts
+    from a reference set earlier.  Sharp fp16 rows (scores of std 9, rising
+    along the keys) move the reference at many of those restarts."""
+    n, d = 1500, 128
+    x = workloads.random_inputs(1, 2, n, d, "fp16", seed=9800 + int(causal), qk_std=3.0,
+                                v_dist="uniform")
+    ramp = np.linspace(0, 2, n, dtype=np.float32)[None, None, :, None]
+    x["k"] = workloads.round_to_dtype(x["k"] + ramp, "fp16")
+    nb = -(-n // 64)
+    qb, kb = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    mask = (((kb // 2 + qb) % 2 == 0) | (kb == qb)).astype(np.uint8)[None, None]
+    log(f"case block-sparse alternating runs fp16 sharp causal={causal} N={n} "
+        f"density={float(mask.mean()):.2f}")
+    run_case(fa, x, "fp16", causal, mask)
+
+
 def test_block_sparse_all_ones_equals_plain_kernel(fa):
     """With every block visible the sparse path computes what attn_fwd does."""
     for causal in (False, True):
