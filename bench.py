@@ -18,7 +18,9 @@ sliding window of 1024 keys (4 * d * windowed pairs * B * H FLOPs), and under
 "attn_fwd_kv_outer" the bench workload run in the original key/value-outer loop
 order (the comparison of the two orders' memory traffic; same FLOP count),
 and under "attn_fwd_block_sparse" the head under a band + global + random
-64x64 block mask (4 * d * visible pairs FLOPs).
+64x64 block mask (4 * d * visible pairs FLOPs).  "variants" times the head in
+the library's other forms, and "configs" the forward on each of the five
+parity workloads at full size.
 """
 from __future__ import annotations
 
@@ -307,6 +309,38 @@ def variants_record(fa, workloads, torch, steps, warmup):
     return out
 
 
+def configs_record(fa, workloads, torch, steps, warmup):
+    """The forward on each of the five parity workloads, at full size, timed
+    like the bench head: tiny fp32 (B=1, H=1, N=256, d=64, unmasked), the
+    GPT-2-small shape (B=8, H=12, T=1024, d=64, causal, bf16), the bench head,
+    the ragged sharp fp16 case (B=2, H=8, N=4097, d=128, unmasked) and the
+    forward of the fwd+bwd case (B=4, H=16, T=4096, d=128, causal, bf16).
+    fp32 inputs run on the fp64-VALU path; their share of the bf16 MFMA peak
+    is not meaningful and is left out."""
+    dev = torch.device("cuda:0")
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+    out = {}
+    for name in ("tiny_fp32_full", "gpt2s_causal_bf16", "long_causal_bf16", "ragged_sharp_fp16",
+                 "fwd_bwd_causal_bf16"):
+        w = workloads.WORKLOADS[name]
+        x = workloads.make_inputs(w)
+        q, k, v = (torch.from_numpy(x[n]).to(dev).to(tdt[w.dtype]).contiguous() for n in "qkv")
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def step():
+            fa.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                        stream=torch.cuda.current_stream(dev))
+
+        ms, _ = time_graph(step, steps, warmup, torch)
+        tf = w.fwd_flops() / (ms * 1e-3) / 1e12
+        out[name] = {"dtype": w.dtype, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                     "mask": "causal" if w.causal else "none", "ms_per_step": round(ms, 5),
+                     "TFLOP/s": round(tf, 2),
+                     "frac_of_mfma_peak": None if w.dtype == "fp32" else round(tf / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
 def kv_outer_record(fa, workloads, torch, steps, warmup):
     """The bench workload in the key/value-outer loop order (attn_fwd_kv_outer),
     timed over a few calls: each is tens of milliseconds."""
@@ -353,7 +387,8 @@ def main():
     ap.add_argument("--no-sparse", action="store_true",
                     help="skip the block-sparse forward measurement")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the strided / d = 96 / d_v = 64 / sparse and window backward timings")
+                    help="skip the strided / d = 96 / d_v = 64 / sparse and window backward timings "
+                         "and the per-workload forward timings")
     ap.add_argument("--no-kv-outer", action="store_true",
                     help="skip the key/value-outer loop-order measurement")
     ap.add_argument("--kv-steps", type=int, default=3)
@@ -447,6 +482,7 @@ def main():
                                                         args.window_warmup)
     if not args.no_variants:
         record["variants"] = variants_record(fa, workloads, torch, 50, 300)
+        record["configs"] = configs_record(fa, workloads, torch, 50, 300)
     if not args.no_kv_outer:
         record["attn_fwd_kv_outer"] = kv_outer_record(fa, workloads, torch, args.kv_steps,
                                                       args.kv_warmup)
