@@ -21,25 +21,35 @@
 namespace fa {
 namespace {
 
-constexpr int kRows = 64;   // query rows per workgroup (one wave, one row per lane)
+constexpr int kRows = 64;   // query rows per workgroup (one row per lane of each wave)
 constexpr int kKeys = 16;   // keys per LDS tile
+constexpr int kSplit = 4;   // waves per workgroup; wave w takes key tiles w, w + kSplit, ..
 
+// The rows' key range is split over kSplit waves, each with its own LDS tiles
+// and its own running (max, denominator, numerator) state; the states are
+// merged at the end with the same alpha rescaling, in wave order, so the
+// result is deterministic.
 template <int D, int DV, bool Causal>
-__global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict__ Q,
-                                                         const float* __restrict__ K,
-                                                         const float* __restrict__ V,
-                                                         float* __restrict__ O,
-                                                         float* __restrict__ LSE, int N,
-                                                         int win, int H, int n_qblocks, float scale,
-                                                         Layout lq, Layout in, Layout lv, Layout out,
-                                                         const uint8_t* __restrict__ bmask,
-                                                         int64_t m_sb, int64_t m_sh) {
+__global__ __launch_bounds__(kRows * kSplit) void fwd_f32_kernel(const float* __restrict__ Q,
+                                                                 const float* __restrict__ K,
+                                                                 const float* __restrict__ V,
+                                                                 float* __restrict__ O,
+                                                                 float* __restrict__ LSE, int N,
+                                                                 int win, int H, int n_qblocks, float scale,
+                                                                 Layout lq, Layout in, Layout lv, Layout out,
+                                                                 const uint8_t* __restrict__ bmask,
+                                                                 int64_t m_sb, int64_t m_sh) {
   constexpr int kQStride = D + 1;  // odd stride: lanes reading their own row hit distinct banks
+  constexpr int kAStride = DV + 1;
+  static_assert(kRows * kAStride <= kSplit * kKeys * (D + DV), "the merge buffer fits in the tiles");
   __shared__ float qs[kRows * kQStride];
-  __shared__ __attribute__((aligned(16))) float ks[kKeys * D];
-  __shared__ __attribute__((aligned(16))) float vs[kKeys * DV];
+  __shared__ __attribute__((aligned(16))) float tiles[kSplit * kKeys * (D + DV)];
+  __shared__ double part_m[kSplit][kRows], part_l[kSplit][kRows];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kRows - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kRows);
+  float* ks = tiles + wave * kKeys * (D + DV);
+  float* vs = ks + kKeys * D;
   const int bh = blockIdx.x / n_qblocks;
   const int q0 = (blockIdx.x % n_qblocks) * kRows;
   const int b = bh / H, h = bh - b * H;
@@ -49,10 +59,11 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   const float* Kh = K + head_off;
   const float* Vh = V + (b * lv.sb + h * lv.sh);
 
-  for (int idx = lane; idx < kRows * D; idx += kRows) {
+  for (int idx = threadIdx.x; idx < kRows * D; idx += kRows * kSplit) {
     const int r = idx / D, col = idx % D;
     qs[r * kQStride + col] = (q0 + r < N) ? Qh[(int64_t)(q0 + r) * lq.sn + col] : 0.f;
   }
+  __syncthreads();
 
   const int my_q = q0 + lane;
   // block-sparse mask row of this query (64 x 64 blocks), if any
@@ -71,8 +82,11 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   double m_run = -INFINITY, l_run = 0.0;
   const double dscale = (double)scale;
 
-  for (int key0 = key_lo; key0 < n_keys; key0 += kKeys) {
-    __syncthreads();  // previous tile fully consumed (and Q staged on the first pass)
+  // Each wave reads only the tiles it wrote itself, and a wave's LDS accesses
+  // complete in order, so the waves need no barrier inside the loop.
+  for (int key0 = key_lo + wave * kKeys; key0 < n_keys; key0 += kSplit * kKeys) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     for (int idx = lane; idx < kKeys * D / 4; idx += kRows) {
       const int r = (idx * 4) / D, col = (idx * 4) % D;
       const bool ok = key0 + r < N;
@@ -87,7 +101,8 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
                            : float4{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<float4*>(vs + r * DV + col) = vv;
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 
     double t[kKeys];
 #pragma unroll
@@ -127,13 +142,42 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
     }
   }
 
-  if (my_q < N) {
-    float* orow = O + (b * out.sb + h * out.sh) + (int64_t)my_q * out.sn;
+  // Merge: m = max over the waves, alpha_w = exp(m_w - m) rounded to fp32 and
+  // used for both the denominator and the numerator; the numerators are
+  // added into LDS in wave order.
+  part_m[wave][lane] = m_run;
+  part_l[wave][lane] = l_run;
+  __syncthreads();
+  double m_all = -INFINITY;
 #pragma unroll
-    // a row that saw no key (block-sparse) stores O = 0 and LSE = -inf
-    for (int col = 0; col < DV; ++col) orow[col] = l_run > 0.0 ? (float)((double)acc[col] / l_run) : 0.f;
-    if (LSE != nullptr) LSE[(int64_t)bh * N + my_q] = (float)(m_run + log(l_run));
+  for (int w = 0; w < kSplit; ++w) m_all = fmax(m_all, part_m[w][lane]);
+  double l_all = 0.0;
+  float alpha_me = 0.f;
+#pragma unroll
+  for (int w = 0; w < kSplit; ++w) {
+    const double mw = part_m[w][lane];
+    const float aw = (mw == -INFINITY) ? 0.f : (float)exp(mw - m_all);
+    l_all += (double)aw * part_l[w][lane];
+    if (w == wave) alpha_me = aw;
   }
+  float* sum = tiles;  // [kRows][kAStride]; every wave is past its last tile read
+  for (int w = 0; w < kSplit; ++w) {
+    if (w == wave) {
+#pragma unroll
+      for (int col = 0; col < DV; ++col) {
+        const float mine = alpha_me * acc[col];
+        sum[lane * kAStride + col] = w == 0 ? mine : sum[lane * kAStride + col] + mine;
+      }
+    }
+    __syncthreads();
+  }
+  if (wave != 0 || my_q >= N) return;
+  float* orow = O + (b * out.sb + h * out.sh) + (int64_t)my_q * out.sn;
+  // a row that saw no key (block-sparse) stores O = 0 and LSE = -inf
+#pragma unroll
+  for (int col = 0; col < DV; ++col)
+    orow[col] = l_all > 0.0 ? (float)((double)sum[lane * kAStride + col] / l_all) : 0.f;
+  if (LSE != nullptr) LSE[(int64_t)bh * N + my_q] = (float)(m_all + log(l_all));
 }
 
 template <int D, bool Causal, int DV = D>
@@ -141,7 +185,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int N = (int)a.N;
   const int n_qblocks = (N + kRows - 1) / kRows;
   const dim3 grid((unsigned)(n_qblocks * a.B * a.H));
-  hipLaunchKernelGGL((fwd_f32_kernel<D, DV, Causal>), grid, dim3(kRows), 0, stream,
+  hipLaunchKernelGGL((fwd_f32_kernel<D, DV, Causal>), grid, dim3(kRows * kSplit), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, N,
                      (int)(a.window < a.N ? a.window : a.N), (int)a.H, n_qblocks, a.scale, a.lq, a.in, a.lv, a.out,

@@ -173,6 +173,23 @@ def test_sharp_rows_rescaling(fa):
         compare("LSE", lse, rl, LSE_TOL["fp16"])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_sharp_rows_fp32(fa, d):
+    """fp32 inputs with scores of std 9 and an increasing trend, held to 1e-5:
+    the fp32 path splits each row's keys over four waves, whose running maxima
+    differ widely before they are merged."""
+    n = 777
+    log(f"case sharp rows fp32 d={d} N={n}")
+    x = workloads.random_inputs(1, 2, n, d, "fp32", seed=70 + d, qk_std=3.0, v_dist="uniform")
+    ramp = np.linspace(0, 2, n, dtype=np.float32)[None, None, :, None]
+    x["k"] = (x["k"] + ramp).astype(np.float32)
+    for causal in (False, True):
+        o, lse = run_fwd(fa, x, "fp32", causal)
+        ro, rl = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=causal)
+        compare("O", o, ro, "fp32")
+        compare("LSE", lse, rl, LSE_TOL["fp32"])
+
+
 # ------------------------------------------------------------------ properties
 
 def test_deterministic(fa):
