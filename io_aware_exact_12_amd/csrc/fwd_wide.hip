@@ -61,11 +61,17 @@ template <int D> struct BlockTile {
 // pair e among the 16 score MFMAs of a block.
 constexpr int slot_of(int e, int st) { return e + (st == 0 ? 0 : st == 1 ? 2 : 5); }
 
-template <bool IsBf16, int D, bool Causal>
+// kWin (causal only): a sliding window of `win` keys, key j visible to query
+// i iff i - win < j <= i.  Blocks left of every query's window are skipped
+// (the workgroup starts at the first block any of its queries sees, a wave at
+// the first its own queries see), and the left-edge mask is applied in the
+// blocks that cross a window's start.
+template <bool IsBf16, int D, bool Causal, bool kWin>
 __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int H, int BH, int n_qblocks, float c,
-    uint32_t q_sign, Layout lq, Layout in, Layout out) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int win, int H, int BH, int n_qblocks,
+    float c, uint32_t q_sign, Layout lq, Layout in, Layout out) {
+  static_assert(!kWin || Causal, "the sliding window is causal");
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using T = STile<D>;
@@ -92,6 +98,9 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
   const int n_blk = Causal ? last_row / kB + 1 : (N + kB - 1) / kB;
   const bool wave_live = qw0 < N;
   const int u_last = Causal ? min(qw0 + 31, N - 1) / kB : n_blk - 1;
+  // first block of the workgroup and of this wave (sliding window; 0 without)
+  const int u_first = kWin ? max(0, q0 - win + 1) / kB : 0;
+  const int u_lo = kWin ? max(0, qw0 - win + 1) / kB : 0;
   const int64_t head = b * in.sb + h * in.sh;
   const uint16_t* k_h = K + head;
   const uint16_t* v_h = V + head;
@@ -121,26 +130,34 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
   float l = 0.f;        // this lane half's share of the row sum, relative to m
   f32x16 s_cur = f32x16{}, s_next = f32x16{};
 
-  for (int u = 0; u < kStages - 1 && u < n_blk; ++u) issue(u);
+  for (int u = u_first; u < u_first + kStages - 1 && u < n_blk; ++u) issue(u);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  if (wave_live) {
-    const uint8_t* kt = k_tile(0);
+  // scores of the first block of every wave that starts in the workgroup's
+  // first block (all of them without a window); K tile u_first is resident
+  auto first_scores = [&](int u) {
+    const uint8_t* kt = k_tile(u);
+    f32x16 st = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < kKs; ++kk) s_cur = E::mfma(row_frag<IsBf16, D>(kt, l32, g, kk), qf[kk], s_cur);
-  }
+    for (int kk = 0; kk < kKs; ++kk) st = E::mfma(row_frag<IsBf16, D>(kt, l32, g, kk), qf[kk], st);
+    return st;
+  };
+  if (wave_live && u_lo == u_first) s_cur = first_scores(u_first);
 
-  for (int u = 0; u < n_blk; ++u) {
+  for (int u = u_first; u < n_blk; ++u) {
     const bool more = u + kStages - 1 < n_blk;
     if (more) issue(u + kStages - 1);  // into the stage block u-1 left
-    if (wave_live && u <= u_last) {
+    // a wave whose window starts after the workgroup's first block forms the
+    // scores of its first block from the resident tile
+    if (kWin && wave_live && u == u_lo && u_lo > u_first) s_cur = first_scores(u);
+    if (wave_live && u >= u_lo && u <= u_last) {
       const int ks0 = u * kB;
       // register rr of lane half g holds key ks0 + 16 (rr >> 3) + 8 g + (rr & 7)
-      if ((Causal && ks0 + kB - 1 > qw0) || ks0 + kB > N) {
+      if ((Causal && ks0 + kB - 1 > qw0) || ks0 + kB > N || (kWin && ks0 <= qw0 + 31 - win)) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int kj = ks0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
-          if (kj >= N || (Causal && kj > my_q)) s_cur[rr] = -INFINITY;
+          if (kj >= N || (Causal && kj > my_q) || (kWin && kj <= my_q - win)) s_cur[rr] = -INFINITY;
         }
       }
       float mx = s_cur[0];
@@ -230,7 +247,7 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
     LSE[(int64_t)bh * N + my_q] = ((m == -INFINITY ? 0.f : m * c) + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
-template <bool IsBf16, int D, bool Causal>
+template <bool IsBf16, int D, bool Causal, bool kWin = false>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int N = (int)a.N;
   const int BH = (int)(a.B * a.H);
@@ -239,16 +256,20 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   // exp2 argument rounds to 0, so visible keys weigh exactly 1)
   const float c = a.scale != 0.f ? __builtin_fabsf(a.scale) * 1.4426950408889634f : 1e-30f;
   const uint32_t q_sign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_wide_kernel<IsBf16, D, Causal>), dim3((unsigned)(n_qblocks * BH)), dim3(kThr),
-                     0, stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, N, (int)a.H,
-                     BH, n_qblocks, c, q_sign, a.lq, a.in, a.out);
+  const int win = (int)(a.window < a.N ? a.window : a.N);
+  hipLaunchKernelGGL((fwd_wide_kernel<IsBf16, D, Causal, kWin>), dim3((unsigned)(n_qblocks * BH)),
+                     dim3(kThr), 0, stream, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                     static_cast<uint16_t*>(a.o), a.lse, N, win, (int)a.H, BH, n_qblocks, c, q_sign, a.lq,
+                     a.in, a.out);
   return hipGetLastError();
 }
 
 template <bool IsBf16>
 hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
-  return a.causal ? launch<IsBf16, 256, true>(a, s) : launch<IsBf16, 256, false>(a, s);
+  if (!a.causal) return launch<IsBf16, 256, false>(a, s);
+  if (a.window < a.N) return launch<IsBf16, 256, true, true>(a, s);
+  return launch<IsBf16, 256, true>(a, s);
 }
 
 }  // namespace

@@ -149,9 +149,9 @@ def fwd_w(window, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=16, d=64
 
 
 def bwd_w(window, ws_bytes=1 << 20, **kw):
-    a = dict(B=1, H=1, N=16, d=64, scale=0.125, dtype=fa.BF16)
+    a = dict(B=1, H=1, N=16, d=64, scale=0.125, dtype=fa.BF16, q=P[0])
     a.update(kw)
-    return fa.attn_bwd_window_raw(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], a["B"],
+    return fa.attn_bwd_window_raw(a["q"], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], a["B"],
                                   a["H"], a["N"], a["d"], window, a["scale"], a["dtype"], P[1],
                                   ws_bytes, None)
 
@@ -358,13 +358,14 @@ def test_bwd_dv_validation():
 
 
 def test_wide_head_validation():
-    """d = 256: the plain forward and backward (bf16 / fp16) reach the pointer
-    checks; fp32 and every variant they do not take return FA_ERR_UNSUPPORTED."""
+    """d = 256: the plain and sliding-window forward and backward (bf16 / fp16)
+    reach the pointer checks; fp32 and every variant they do not take return
+    FA_ERR_UNSUPPORTED."""
     assert fwd(d=256, q=P[0] + 2) == FA_ERR_ALIGN
     assert fwd(d=256, dtype=fa.F16, mask=1, q=P[0] + 2) == FA_ERR_ALIGN
     assert fwd(d=256, dtype=fa.F32) == FA_ERR_UNSUPPORTED
     assert fwd(d=256, N=(1 << 22)) == FA_ERR_SHAPE      # one head spans 2 GiB
-    assert fwd_w(4, d=256, N=64) == FA_ERR_UNSUPPORTED
+    assert fwd_w(4, d=256, N=64, q=P[0] + 2) == FA_ERR_ALIGN
     assert fwd_w(64, d=256, N=64, q=P[0] + 2) == FA_ERR_ALIGN   # a window >= N is plain causal
     assert fwd_bs(d=256) == FA_ERR_UNSUPPORTED
     assert fa.attn_fwd_dv_raw(P[0], P[1], P[2], P[3], P[4], 1, 1, 16, 256, 128, 0, 0.1, fa.BF16,
@@ -373,7 +374,7 @@ def test_wide_head_validation():
                               None) == FA_ERR_ALIGN
     assert bwd(d=256, q=P[0] + 2) == FA_ERR_ALIGN
     assert bwd(d=256, dtype=fa.F32) == FA_ERR_UNSUPPORTED
-    assert bwd_w(4, d=256, N=64) == FA_ERR_UNSUPPORTED
+    assert bwd_w(4, d=256, N=64, q=P[0] + 2) == FA_ERR_ALIGN
     assert fa.attn_bwd_block_sparse_raw(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], 1, 1, 64,
                                         256, P[7], 1, 1, 0, 0.1, fa.BF16, P[1], 1 << 20,
                                         None) == FA_ERR_UNSUPPORTED

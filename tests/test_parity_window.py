@@ -75,6 +75,24 @@ def test_window_fwd_sweep(fa, dtype, d):
         fwd_case(fa, workloads.random_inputs(bh[0], bh[1], n, d, dtype, seed), dtype, w)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_window_fwd_sweep_d256(fa, dtype):
+    """Head dim 256 (its own kernel: 32-key blocks, one wave per SIMD): waves
+    whose window starts after the workgroup's first block form their first
+    scores from the resident tile; one sharp fp16/bf16 case (scores of std 9)
+    moves the lazy reference at those starts."""
+    cases = [(1, 1), (31, 1), (64, 17), (257, 32), (257, 33), (600, 64), (600, 65), (1000, 100),
+             (777, 300), (300, 5000)]
+    for i, (n, w) in enumerate(cases):
+        seed = 7050 + 13 * n + w
+        bh = (1, 2) if i % 2 else (2, 1)
+        log(f"case window fwd dtype={dtype} d=256 B,H={bh} N={n} W={w} seed={seed}")
+        fwd_case(fa, workloads.random_inputs(bh[0], bh[1], n, 256, dtype, seed), dtype, w)
+    log(f"case window fwd dtype={dtype} d=256 sharp N=700 W=150")
+    fwd_case(fa, workloads.random_inputs(1, 2, 700, 256, dtype, 7099, qk_std=3.0, v_dist="uniform"),
+             dtype, 150)
+
+
 def test_window_fwd_long_sampled_rows(fa):
     n, w = 4099, 1000
     log(f"case window fwd long N={n} W={w}")
@@ -131,7 +149,7 @@ def bwd_case(fa, x, dtype, w):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 def test_window_bwd_sweep(fa, dtype, d):
     for i, (n, w) in enumerate([(1, 1), (65, 1), (65, 33), (300, 64), (300, 100), (777, 129),
                                 (777, 300), (500, 500)]):
