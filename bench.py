@@ -226,7 +226,8 @@ def sparse_record(fa, workloads, torch, steps, warmup):
 def variants_record(fa, workloads, torch, steps, warmup):
     """The bench head (B=1, H=16, N=8192, causal, bf16) in the other forms the
     library takes, each timed like the forward: a [B, N, H, d] view (strided
-    call), d = 96, d = 256 and d_v = 64 with d = 128 (forward and backward), and the
+    call), d = 96, d = 256 (also with a window of 1024 keys) and d_v = 64 with
+    d = 128 (forward and backward), and the
     backward of the block-sparse and sliding-window workloads (10 d FLOPs per
     visible pair)."""
     dev = torch.device("cuda:0")
@@ -268,6 +269,16 @@ def variants_record(fa, workloads, torch, steps, warmup):
     rec("bwd_d256", lambda: fa.attn_bwd(q256, k256, v256, o256, lse256, do256, causal=True, dq=g256[0],
                                         dk=g256[1], dv=g256[2], workspace=ws256),
         10 * 256 * (8192 * 8193 // 2) * 16, s=10, wm=30)
+    # d = 256 with the sliding window of 1024 keys: W (W + 1) / 2 + (N - W) W pairs per head
+    wpairs = (1024 * 1025 // 2 + (8192 - 1024) * 1024) * 16
+    rec("fwd_d256_window", lambda: fa.attn_fwd(q256, k256, v256, causal=True, window=1024, out=o256),
+        4 * 256 * wpairs)
+    lse256w = torch.empty_like(lse256)
+    fa.attn_fwd(q256, k256, v256, causal=True, window=1024, out=o256, lse=lse256w)
+    rec("bwd_d256_window", lambda: fa.attn_bwd(q256, k256, v256, o256, lse256w, do256, causal=True,
+                                               window=1024, dq=g256[0], dk=g256[1], dv=g256[2],
+                                               workspace=ws256),
+        10 * 256 * wpairs, s=10, wm=30)
     # d_v = 64 with d = 128: 2 d + 2 d_v FLOPs per visible pair
     xv = workloads.random_inputs(1, 16, 8192, 64, "bf16", seed=12)
     q, k = (dev_bf16(x[n]).contiguous() for n in "qk")
