@@ -411,8 +411,8 @@ def main():
                          "the reference kernel for scaling HBM byte counters, and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(attention shards over (batch, head) with no exchange; see the design notes)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(attention shards over (batch, head) with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -9,8 +9,8 @@ exactly representable in the named storage dtype, so that a torch tensor made
 from it in that dtype carries the very same numbers the oracle sees (upcast to
 float64 there).
 
-Shapes and value distributions follow the five workloads the method is judged
-on: a tiny fp32 unmasked head, a GPT-2-small-shaped causal layer, the long
+Shapes and value distributions follow the five workloads the method is checked
+and measured on: a tiny fp32 unmasked head, a GPT-2-small-shaped causal layer, the long
 context causal head, a ragged-length fp16 case with sharp softmax rows, and the
 causal forward+backward case.  A sixth, the long context head under a causal
 sliding window of 1024 keys, measures the window path; a seventh, the same
