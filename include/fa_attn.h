@@ -83,9 +83,9 @@ enum fa_status {
  *            takes FA_F16 or FA_BF16 (FA_ERR_UNSUPPORTED for FA_F32) and
  *            runs a kernel of its own: one workgroup per CU that keeps the
  *            256-wide accumulators of 128 queries in registers.  The calls
- *            below that add a block mask, d_v != d or the key/value-outer
- *            order return FA_ERR_UNSUPPORTED for d = 256; attn_bwd,
- *            attn_bwd_strided and the sliding-window calls take it.
+ *            below that add d_v != d or the key/value-outer order return
+ *            FA_ERR_UNSUPPORTED for d = 256; attn_bwd, attn_bwd_strided, the
+ *            sliding-window and the block-sparse calls take it.
  *   mask     enum fa_mask.
  *   scale    finite multiplier of the raw dot products (any sign; usually
  *            1/sqrt(d)).

@@ -205,8 +205,7 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=N
     """Exact attention forward on the GPU: returns ``(o, lse)`` (lse None if not requested).
 
     q, k, v: contiguous device tensors [B, H, N, d] of one dtype (float32,
-    float16 or bfloat16), d in {64, 96, 128, 256} (256: float16 or bfloat16,
-    no block mask).  ``scale`` defaults to 1/sqrt(d).
+    float16 or bfloat16), d in {64, 96, 128, 256} (256: float16 or bfloat16).  ``scale`` defaults to 1/sqrt(d).
     ``window`` (causal only) calls ``attn_fwd_window``: query i sees keys
     i - window < j <= i.  ``block_mask`` (uint8 device tensor
     [1 or B, 1 or H, ceil(N/64), ceil(N/64)]) calls ``attn_fwd_block_sparse``.

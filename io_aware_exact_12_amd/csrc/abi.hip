@@ -105,8 +105,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.mask_sb = mask_b == 1 ? 0 : mask_h * nb * nb;
   }
   a.lv = a.dv == d ? a.in : fa::dense_layout(H, N, a.dv);
-  // d = 256: bf16 / fp16, plain masks or the sliding window, d_v = d
-  if (d == 256 && (dtype == FA_F32 || block_mask != nullptr)) return FA_ERR_UNSUPPORTED;
+  // d = 256: bf16 / fp16, d_v = d
+  if (d == 256 && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
     return FA_ERR_ALIGN;
@@ -162,8 +162,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   a.dvw = d;
   a.lv = a.in;
   a.outv = a.out;
-  // d = 256: plain masks or the sliding window, d_v = d
-  if (d == 256 && (block_mask != nullptr || (dvw != 0 && dvw != d))) return FA_ERR_UNSUPPORTED;
+  // d = 256: d_v = d
+  if (d == 256 && dvw != 0 && dvw != d) return FA_ERR_UNSUPPORTED;
   if (dvw != 0 && dvw != d) {  // v, o, dout and dv rows of dvw elements, dense
     if (!((d == 128 && dvw == 64) || (d == 64 && dvw == 128))) return FA_ERR_UNSUPPORTED;
     a.dvw = dvw;
@@ -289,7 +289,7 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, 
 }
 
 size_t attn_bwd_block_sparse_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
-  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK || d == 256) return 0;
+  if (check_common(B, H, N, d, FA_MASK_NONE, 1.0f, dtype) != FA_OK) return 0;
   return fa::bwd_sparse_workspace_bytes(B, H, N, d);
 }
 

@@ -734,7 +734,9 @@ hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
     return a.causal ? launch<IsBf16, 128, true, kModePlain, 64>(a, s) : launch<IsBf16, 128, false, kModePlain, 64>(a, s);
   if (a.dvw == 128 && a.d == 64)
     return a.causal ? launch<IsBf16, 64, true, kModePlain, 128>(a, s) : launch<IsBf16, 64, false, kModePlain, 128>(a, s);
-  if (a.d == 256) {  // plain masks and the sliding window
+  if (a.d == 256) {  // plain masks, the sliding window and block masks
+    if (a.block_mask != nullptr)
+      return a.causal ? launch<IsBf16, 256, true, kModeSparse>(a, s) : launch<IsBf16, 256, false, kModeSparse>(a, s);
     if (!a.causal) return launch<IsBf16, 256, false, kModePlain>(a, s);
     if (a.window < a.N) return launch<IsBf16, 256, true, kModeWindow>(a, s);
     return launch<IsBf16, 256, true, kModePlain>(a, s);

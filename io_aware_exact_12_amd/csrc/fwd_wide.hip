@@ -66,21 +66,29 @@ constexpr int slot_of(int e, int st) { return e + (st == 0 ? 0 : st == 1 ? 2 : 5
 // (the workgroup starts at the first block any of its queries sees, a wave at
 // the first its own queries see), and the left-edge mask is applied in the
 // blocks that cross a window's start.
-template <bool IsBf16, int D, bool Causal, bool kWin>
+// kSparse: a block mask of 64 x 64 blocks (and-ed with causal when that is
+// on).  The workgroup lists the 64-key tiles that one of its two 64-row query
+// blocks sees and walks their 32-key halves as its blocks; a wave masks the
+// blocks of tiles its own query block does not see, and a row that sees no
+// key stores O = 0 and LSE = -inf.
+template <bool IsBf16, int D, bool Causal, bool kWin, bool kSparse>
 __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int win, int H, int BH, int n_qblocks,
-    float c, uint32_t q_sign, Layout lq, Layout in, Layout out) {
+    float c, uint32_t q_sign, Layout lq, Layout in, Layout out, const uint8_t* __restrict__ bmask,
+    int64_t m_sb, int64_t m_sh) {
   static_assert(!kWin || Causal, "the sliding window is causal");
+  static_assert(!(kWin && kSparse), "one of the two masks");
+  static_assert(2 * kB == kSparseBlock && kRes % kSparseBlock == 0, "mask tiles are two blocks");
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using T = STile<D>;
   using BT = BlockTile<D>;
   constexpr int kKs = D / 16, kDB = D / 32;
   constexpr int kStage = 2 * BT::kBytes;  // K tile, then V tile
-  static_assert(kStages * kStage <= 160 * 1024, "the ring fits the LDS");
+  static_assert(kStages * kStage + kSparseBytes <= 160 * 1024, "the ring and the tile list fit the LDS");
   static_assert(kKs == 16, "the probability schedule spreads 8 score pairs over 16 MFMAs");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage + (kSparse ? kSparseBytes : 0)];
 
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -95,9 +103,40 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
 
   // blocks of the workgroup, and the last one this wave computes
   const int last_row = min(N, q0 + kRes) - 1;
-  const int n_blk = Causal ? last_row / kB + 1 : (N + kB - 1) / kB;
+  int n_blk = Causal ? last_row / kB + 1 : (N + kB - 1) / kB;
   const bool wave_live = qw0 < N;
-  const int u_last = Causal ? min(qw0 + 31, N - 1) / kB : n_blk - 1;
+  // block-sparse: the listed tiles (index | query-block bits << 16) in LDS
+  uint32_t* const list = reinterpret_cast<uint32_t*>(smem + kStages * kStage);
+  const int n_tiles_all = (N + kSparseBlock - 1) / kSparseBlock;
+  int n_pos = 0;
+  if constexpr (kSparse) {
+    const int qb0 = q0 / kSparseBlock;
+    const int n_tiles = Causal ? last_row / kSparseBlock + 1 : n_tiles_all;
+    const uint8_t* mk = bmask + (bh / H) * m_sb + (bh % H) * m_sh;
+    n_pos = compact_tiles<kW>(list, n_tiles, [&](int jt) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int i = 0; i < kRes / kSparseBlock; ++i) {
+        const int qbk = qb0 + i;
+        if (qbk < n_tiles_all && (!Causal || jt <= qbk) && mk[(int64_t)qbk * n_tiles_all + jt] != 0)
+          bits |= 1u << i;
+      }
+      return bits;
+    });
+    n_blk = 2 * n_pos;
+  }
+  // first key of block u (block-sparse: half u & 1 of the tile at list
+  // position u / 2; past the list, a tile past the end, which reads as zeros)
+  auto ks_of = [&](int u) {
+    if constexpr (kSparse) {
+      const int p = u >> 1;
+      const int t = p < n_pos ? __builtin_amdgcn_readfirstlane((int)(list[p] & 0xFFFFu)) : n_tiles_all;
+      return kSparseBlock * t + kB * (u & 1);
+    } else {
+      return u * kB;
+    }
+  };
+  const int u_last = (Causal && !kSparse) ? min(qw0 + 31, N - 1) / kB : n_blk - 1;
   // first block of the workgroup and of this wave (sliding window; 0 without)
   const int u_first = kWin ? max(0, q0 - win + 1) / kB : 0;
   const int u_lo = kWin ? max(0, qw0 - win + 1) / kB : 0;
@@ -109,7 +148,7 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
   const uint32_t lds0 = lds_u32(smem);
   // copies of block u's K and V rows into its stage: 2 kPerWave per wave
   auto issue = [&](int u) {
-    const int row0 = u * kB, left = N - row0;
+    const int row0 = ks_of(u), left = N - row0;
     const uint32_t bytes = left > 0 ? (uint32_t)(left - 1) * (uint32_t)(2 * in.sn) + (uint32_t)T::kDataBytes : 0u;
     const i32x4 rk = make_rsrc(k_h + (int64_t)row0 * in.sn, bytes);
     const i32x4 rv = make_rsrc(v_h + (int64_t)row0 * in.sn, bytes);
@@ -151,9 +190,12 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
     // scores of its first block from the resident tile
     if (kWin && wave_live && u == u_lo && u_lo > u_first) s_cur = first_scores(u);
     if (wave_live && u >= u_lo && u <= u_last) {
-      const int ks0 = u * kB;
+      const int ks0 = ks_of(u);
       // register rr of lane half g holds key ks0 + 16 (rr >> 3) + 8 g + (rr & 7)
-      if ((Causal && ks0 + kB - 1 > qw0) || ks0 + kB > N || (kWin && ks0 <= qw0 + 31 - win)) {
+      if (kSparse && ((list[u >> 1] >> (16 + wave / 2)) & 1u) == 0) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) s_cur[rr] = -INFINITY;  // tile hidden from this query block
+      } else if ((Causal && ks0 + kB - 1 > qw0) || ks0 + kB > N || (kWin && ks0 <= qw0 + 31 - win)) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int kj = ks0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
@@ -242,12 +284,13 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
   if (!wave_live) return;
   const float l_tot = xhalf_sum(l);
   if (my_q >= N) return;
-  store_row<IsBf16, D>(O + (b * out.sb + h * out.sh), my_q, out.sn, g, acc, 1.0f / l_tot);
+  const float inv = (!kSparse || l_tot > 0.f) ? 1.0f / l_tot : 0.f;  // a row with no key: O = 0
+  store_row<IsBf16, D>(O + (b * out.sb + h * out.sh), my_q, out.sn, g, acc, inv);
   if (LSE != nullptr && g == 0)
     LSE[(int64_t)bh * N + my_q] = ((m == -INFINITY ? 0.f : m * c) + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
-template <bool IsBf16, int D, bool Causal, bool kWin = false>
+template <bool IsBf16, int D, bool Causal, bool kWin = false, bool kSparse = false>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int N = (int)a.N;
   const int BH = (int)(a.B * a.H);
@@ -257,16 +300,18 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const float c = a.scale != 0.f ? __builtin_fabsf(a.scale) * 1.4426950408889634f : 1e-30f;
   const uint32_t q_sign = a.scale < 0.f ? 0x80008000u : 0u;
   const int win = (int)(a.window < a.N ? a.window : a.N);
-  hipLaunchKernelGGL((fwd_wide_kernel<IsBf16, D, Causal, kWin>), dim3((unsigned)(n_qblocks * BH)),
+  hipLaunchKernelGGL((fwd_wide_kernel<IsBf16, D, Causal, kWin, kSparse>), dim3((unsigned)(n_qblocks * BH)),
                      dim3(kThr), 0, stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<uint16_t*>(a.o), a.lse, N, win, (int)a.H, BH, n_qblocks, c, q_sign, a.lq,
-                     a.in, a.out);
+                     a.in, a.out, a.block_mask, a.mask_sb, a.mask_sh);
   return hipGetLastError();
 }
 
 template <bool IsBf16>
 hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
+  if (a.block_mask != nullptr)
+    return a.causal ? launch<IsBf16, 256, true, false, true>(a, s) : launch<IsBf16, 256, false, false, true>(a, s);
   if (!a.causal) return launch<IsBf16, 256, false>(a, s);
   if (a.window < a.N) return launch<IsBf16, 256, true, true>(a, s);
   return launch<IsBf16, 256, true>(a, s);

@@ -358,16 +358,16 @@ def test_bwd_dv_validation():
 
 
 def test_wide_head_validation():
-    """d = 256: the plain and sliding-window forward and backward (bf16 / fp16)
-    reach the pointer checks; fp32 and every variant they do not take return
-    FA_ERR_UNSUPPORTED."""
+    """d = 256: the plain, sliding-window and block-sparse forward and backward
+    (bf16 / fp16) reach the pointer checks; fp32 and every variant they do not
+    take return FA_ERR_UNSUPPORTED."""
     assert fwd(d=256, q=P[0] + 2) == FA_ERR_ALIGN
     assert fwd(d=256, dtype=fa.F16, mask=1, q=P[0] + 2) == FA_ERR_ALIGN
     assert fwd(d=256, dtype=fa.F32) == FA_ERR_UNSUPPORTED
     assert fwd(d=256, N=(1 << 22)) == FA_ERR_SHAPE      # one head spans 2 GiB
     assert fwd_w(4, d=256, N=64, q=P[0] + 2) == FA_ERR_ALIGN
     assert fwd_w(64, d=256, N=64, q=P[0] + 2) == FA_ERR_ALIGN   # a window >= N is plain causal
-    assert fwd_bs(d=256) == FA_ERR_UNSUPPORTED
+    assert fwd_bs(d=256, q=P[0] + 2) == FA_ERR_ALIGN
     assert fa.attn_fwd_dv_raw(P[0], P[1], P[2], P[3], P[4], 1, 1, 16, 256, 128, 0, 0.1, fa.BF16,
                               None) == FA_ERR_UNSUPPORTED
     assert fa.attn_fwd_dv_raw(P[0] + 2, P[1], P[2], P[3], P[4], 1, 1, 16, 256, 256, 0, 0.1, fa.BF16,
@@ -375,9 +375,9 @@ def test_wide_head_validation():
     assert bwd(d=256, q=P[0] + 2) == FA_ERR_ALIGN
     assert bwd(d=256, dtype=fa.F32) == FA_ERR_UNSUPPORTED
     assert bwd_w(4, d=256, N=64, q=P[0] + 2) == FA_ERR_ALIGN
-    assert fa.attn_bwd_block_sparse_raw(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], 1, 1, 64,
-                                        256, P[7], 1, 1, 0, 0.1, fa.BF16, P[1], 1 << 20,
-                                        None) == FA_ERR_UNSUPPORTED
+    assert fa.attn_bwd_block_sparse_raw(P[0] + 2, P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], 1, 1,
+                                        64, 256, P[7], 1, 1, 0, 0.1, fa.BF16, P[1], 1 << 20,
+                                        None) == FA_ERR_ALIGN
     assert fa.bwd_workspace_bytes(1, 1, 16, 256, fa.BF16) == 8 * 16
     assert kvo(d=256) == FA_ERR_UNSUPPORTED
     assert fa.kv_outer_workspace_bytes(1, 1, 16, 256, fa.BF16) == 0
@@ -388,14 +388,13 @@ def test_block_sparse_backward_workspace():
     counter per 128 keys and fp32 partial dK and dV of four chunks per key,
     each array on a 256-byte boundary."""
     up = lambda x: (x + 255) // 256 * 256
-    for B, H, N, d in ((1, 16, 8192, 128), (2, 3, 200, 64), (1, 1, 1, 96)):
+    for B, H, N, d in ((1, 16, 8192, 128), (2, 3, 200, 64), (1, 1, 1, 96), (1, 1, 16, 256)):
         bh = B * H
         cnt = up(8 * bh * N)
         part = up(cnt + 4 * bh * (-(-N // 128)))
         want = part + 4 * 4 * bh * N * 2 * d
         assert fa.bwd_block_sparse_workspace_bytes(B, H, N, d, fa.BF16) == want
     assert fa.bwd_block_sparse_workspace_bytes(1, 1, 16, 80, fa.BF16) == 0
-    assert fa.bwd_block_sparse_workspace_bytes(1, 1, 16, 256, fa.BF16) == 0
     need = fa.bwd_block_sparse_workspace_bytes(2, 3, 200, 64, fa.BF16)
     def bb(ws):
         return fa.attn_bwd_block_sparse_raw(P[0] + 2, P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], 2, 3,

@@ -86,6 +86,23 @@ def test_block_sparse_sweep(fa, dtype, d, causal):
         run_case(fa, x, dtype, causal, random_mask(mb, mh, n, dens, seed + 1, empty_row=(i == 3)))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_sweep_d256(fa, dtype, causal):
+    """Head dim 256 (its own kernel, 32-key blocks, two 64-row query blocks per
+    workgroup): random masks, broadcast or full mask axes, one query block
+    that sees nothing (O = 0, LSE = -inf)."""
+    cases = [(1, (1, 1), 0.5), (64, (1, 2), 0.5), (65, (2, 1), 0.6), (300, (1, 3), 0.4),
+             (777, (2, 2), 0.3)]
+    for i, (n, (b, h), dens) in enumerate(cases):
+        seed = 9650 + n + int(causal)
+        mb, mh = (1 if i % 2 else b), (h if i % 3 else 1)
+        log(f"case block-sparse dtype={dtype} d=256 causal={causal} B,H={b, h} N={n} "
+            f"mask {mb}x{mh} density={dens} seed={seed}")
+        x = workloads.random_inputs(b, h, n, 256, dtype, seed)
+        run_case(fa, x, dtype, causal, random_mask(mb, mh, n, dens, seed + 1, empty_row=(i == 3)))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_block_sparse_alternating_runs_sharp_rows(fa, causal):
     """Each query block sees runs of two key tiles separated by two hidden ones,
@@ -153,7 +170,7 @@ def bwd_case(fa, x, dtype, causal, mask):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_block_sparse_backward_sweep(fa, dtype, d, causal):
     cases = [(1, (1, 1), 0.5), (65, (2, 1), 0.6), (300, (1, 3), 0.4), (777, (1, 2), 0.3)]
