@@ -70,6 +70,10 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+// Tail rows r0 .. N-1 (at most 32) of an unmasked bf16 / fp16 forward with
+// d_v = d in {64, 96, 128}: one workgroup per head, keys split over its waves.
+hipError_t launch_fwd_tail_bf16(const FwdArgs& a, int64_t r0, hipStream_t s);
+hipError_t launch_fwd_tail_f16(const FwdArgs& a, int64_t r0, hipStream_t s);
 // d = 256 forward (plain masks, d_v = d): one 4-wave workgroup per CU
 hipError_t launch_fwd_wide_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_wide_f16(const FwdArgs& a, hipStream_t s);

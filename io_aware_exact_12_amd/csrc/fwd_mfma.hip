@@ -700,7 +700,16 @@ template <bool IsBf16, int D, bool Causal, int Mode, int DV = D>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int N = (int)a.N;
   const int BH = (int)(a.B * a.H);
-  const int n_qblocks = (N + kBM - 1) / kBM;
+  int n_qblocks = (N + kBM - 1) / kBM;
+  // Unmasked, with a last query block of at most 32 rows: that block would
+  // stream every key through one wave in a round of its own, so the tail
+  // kernel takes those rows with the keys split over its waves.
+  if (!Causal && Mode == kModePlain && DV == D && N % kBM != 0 && N % kBM <= 32) {
+    n_qblocks -= 1;
+    const hipError_t e = IsBf16 ? launch_fwd_tail_bf16(a, (int64_t)n_qblocks * kBM, stream)
+                                : launch_fwd_tail_f16(a, (int64_t)n_qblocks * kBM, stream);
+    if (e != hipSuccess || n_qblocks == 0) return e;
+  }
   const dim3 grid((unsigned)(n_qblocks * BH));
   // c = |scale| * log2(e).  A zero scale is run as the limit scale -> 0+:
   // with c = 1e-30 every exp2 argument c*(s - m) rounds to exactly 0 in fp32,
