@@ -112,7 +112,7 @@ def test_large_workload_sampled_rows(fa, name):
 
 # ------------------------------------------------------------------ sweep
 
-SWEEP_N = [1, 2, 15, 63, 64, 65, 127, 128, 129, 200, 1000]
+SWEEP_N = [1, 2, 15, 63, 64, 65, 127, 128, 129, 200, 257, 288, 289, 543, 1000]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
