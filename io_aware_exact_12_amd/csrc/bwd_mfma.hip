@@ -160,18 +160,29 @@ struct DkdvBlock {
                                            16 * (r >> 3) + (r & 7));
   }
 
-  // probability of register r of a half whose first query is qs0, given
-  // nl = -LSE2 of that query
-  template <bool kMasked>
-  __device__ __forceinline__ float prob(const f32x16& s, float nl, int qs0, int r) const {
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, nl));
-    if (!kMasked) return p;
-    const int qi = qs0 + 16 * (r >> 3) + 8 * g + (r & 7);
-    return ((Causal && my_k > qi) || (kWin && qi >= my_k + win) || qi >= N || my_k >= N) ? 0.f : p;
+  // Probabilities of the 16 registers of a half whose first query is qs0,
+  // from nl = -LSE2 of each register's query; with `masked` (wave-uniform:
+  // the tile touches the diagonal, a window edge or a sequence end) those of
+  // hidden (key, query) pairs are 0.  One code path serves both cases, so the
+  // tile loop holds a single copy of the half and no register copies at a join.
+  __device__ __forceinline__ void probs(const f32x16& s, const uint8_t* sb, int h, int qs0, bool masked,
+                                        float (&p)[16]) const {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const f32x2 nl = pair_vals(sb, Ld::kLse, h, 2 * e);
+      p[2 * e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e], c, nl[0]));
+      p[2 * e + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e + 1], c, nl[1]));
+    }
+    if (masked) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = qs0 + 16 * (r >> 3) + 8 * g + (r & 7);
+        if ((Causal && my_k > qi) || (kWin && qi >= my_k + win) || qi >= N || my_k >= N) p[r] = 0.f;
+      }
+    }
   }
 
-  template <bool kMasked>
-  __device__ __forceinline__ void half_v(const uint8_t* sb, int h, int qs0) {
+  __device__ __forceinline__ void half_v(const uint8_t* sb, int h, int qs0, bool masked) {
     const uint8_t* q = sb + Ld::kQ;
     const uint8_t* o = sb + Ld::kDO;
     // operand reads run two MFMAs ahead; the fences stop the compiler from
@@ -185,11 +196,10 @@ struct DkdvBlock {
       __builtin_amdgcn_sched_barrier(0);
     }
     u32x4 pw[2];
+    float p[16];
+    probs(s, sb, h, qs0, masked, p);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const f32x2 nl = pair_vals(sb, Ld::kLse, h, 2 * e);
-      pw[e >> 2][e & 3] = E::pack2(prob<kMasked>(s, nl[0], qs0, 2 * e), prob<kMasked>(s, nl[1], qs0, 2 * e + 1));
-    }
+    for (int e = 0; e < 8; ++e) pw[e >> 2][e & 3] = E::pack2(p[2 * e], p[2 * e + 1]);
     __builtin_amdgcn_sched_barrier(0);
     vec8 b[2] = {tr_opO(o, h, 0, 0), tr_opO(o, h, 0, 1 % kDBO)};
 #pragma unroll
@@ -201,8 +211,7 @@ struct DkdvBlock {
     }
   }
 
-  template <bool kMasked>
-  __device__ __forceinline__ void half_k(const uint8_t* sb, int h, int qs0) {
+  __device__ __forceinline__ void half_k(const uint8_t* sb, int h, int qs0, bool masked) {
     const uint8_t* q = sb + Ld::kQ;
     const uint8_t* o = sb + Ld::kDO;
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -219,13 +228,13 @@ struct DkdvBlock {
       __builtin_amdgcn_sched_barrier(0);
     }
     u32x4 sw[2];
+    float p[16];
+    probs(s, sb, h, qs0, masked, p);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int r = 2 * e;
-      const f32x2 nl = pair_vals(sb, Ld::kLse, h, r), dd = pair_vals(sb, Ld::kD, h, r);
-      const float d0 = prob<kMasked>(s, nl[0], qs0, r) * (dp[r] - dd[0]);
-      const float d1 = prob<kMasked>(s, nl[1], qs0, r + 1) * (dp[r + 1] - dd[1]);
-      sw[e >> 2][e & 3] = E::pack2(d0, d1);
+      const f32x2 dd = pair_vals(sb, Ld::kD, h, r);
+      sw[e >> 2][e & 3] = E::pack2(p[r] * (dp[r] - dd[0]), p[r + 1] * (dp[r + 1] - dd[1]));
     }
     __builtin_amdgcn_sched_barrier(0);
     vec8 b[2] = {tr_op(q, h, 0, 0), tr_op(q, h, 0, 1 % kDB)};
@@ -421,12 +430,7 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dkdv(
       const uint8_t* sb = smem + st * Ld::kStage;
       const bool m = masked(it);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (m)
-          blk.template half_v<true>(sb, h, it * kT + 32 * h);
-        else
-          blk.template half_v<false>(sb, h, it * kT + 32 * h);
-      }
+      for (int h = 0; h < 2; ++h) blk.half_v(sb, h, it * kT + 32 * h, m);
     }
     wait_copies();
     __syncthreads();
@@ -448,12 +452,7 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dkdv(
       const uint8_t* sb = smem + st * Ld::kStage;
       const bool m = masked(it);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (m)
-          blk.template half_k<true>(sb, h, it * kT + 32 * h);
-        else
-          blk.template half_k<false>(sb, h, it * kT + 32 * h);
-      }
+      for (int h = 0; h < 2; ++h) blk.half_k(sb, h, it * kT + 32 * h, m);
     }
     wait_copies();
     __syncthreads();
