@@ -573,10 +573,18 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dq(
     copy_tile<DV>(base + Ld::kV, v_h, N, it * kT, lv.sn, wave, srcO);
   };
 
-  // S^T and dP^T of key half kh of the tile in stage st, and P^T, with the
-  // masks applied when `masked` holds; register e of lane half g holds key
-  // ks0 + 16 (e >> 3) + 8 g + (e & 7).
-  auto scores = [&](auto masked, int st, int kh, int ks0, f32x16& p, f32x16& dp) {
+  // Whether key half ks0 .. ks0 + 31 hides some key from some query of this
+  // wave (causal diagonal, left edge of the window, end of the sequence); the
+  // other halves skip the per-element masks.  Rows past N need none: their
+  // LSE is +inf, so their probabilities are 0.
+  auto needs_mask = [&](int ks0) {
+    return (Causal && ks0 + 31 > qw0) || (kWin && ks0 <= qw0 + 31 - win) || ks0 + 32 > N;
+  };
+  // S^T and dP^T of key half kh of the tile in stage st, and P^T; register e
+  // of lane half g holds key ks0 + 16 (e >> 3) + 8 g + (e & 7).  One code path
+  // for both kinds of half, with a wave-uniform branch around the masks, so
+  // that the loop holds one copy and no register copies at a join.
+  auto scores_at = [&](int st, int kh, int ks0, f32x16& p, f32x16& dp) {
     const uint8_t* k_lds = smem + st * Ld::kStage + Ld::kK;
     const uint8_t* v_lds = smem + st * Ld::kStage + Ld::kV;
     f32x16 s = f32x16{};
@@ -588,27 +596,14 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dq(
       if (kk < kKsO) dp = E::mfma(row_frag<IsBf16, DV>(v_lds, r, g, kk), of[kk], dp);
     }
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int kj = ks0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
-      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c, -lse2));
-      if constexpr (decltype(masked)::value)
-        p[rr] = (kj >= N || (Causal && kj > my_q) || (kWin && kj <= my_q - win)) ? 0.f : pr;
-      else
-        p[rr] = pr;
+    for (int rr = 0; rr < 16; ++rr) p[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c, -lse2));
+    if (needs_mask(ks0)) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int kj = ks0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
+        if (kj >= N || (Causal && kj > my_q) || (kWin && kj <= my_q - win)) p[rr] = 0.f;
+      }
     }
-  };
-  // Whether key half ks0 .. ks0 + 31 hides some key from some query of this
-  // wave (causal diagonal, left edge of the window, end of the sequence); the
-  // other halves skip the per-element masks.  Rows past N need none: their
-  // LSE is +inf, so their probabilities are 0.
-  auto needs_mask = [&](int ks0) {
-    return (Causal && ks0 + 31 > qw0) || (kWin && ks0 <= qw0 + 31 - win) || ks0 + 32 > N;
-  };
-  auto scores_at = [&](int st, int kh, int ks0, f32x16& p, f32x16& dp) {
-    if (needs_mask(ks0))
-      scores(BoolTag<true>{}, st, kh, ks0, p, dp);
-    else
-      scores(BoolTag<false>{}, st, kh, ks0, p, dp);
   };
 
   // ---- pass 1: D = sum_j P_ij dP_ij
