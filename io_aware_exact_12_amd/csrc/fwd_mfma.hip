@@ -63,8 +63,15 @@ constexpr int kStages = 4;        // LDS ring depth of the K and of the V tiles
 constexpr int kBN = 64;           // keys per tile
 constexpr int kThreads = 64 * kWaves;
 // A block whose partial row sum (16 probabilities of one lane half) exceeds
-// this moves the reference maximum; it bounds every probability by 2^8.
-constexpr float kSumCap = 256.0f;
+// the cap moves the reference maximum, so every probability stays below it:
+// 2^15 for fp16, whose P operand reaches 65504, and 2^24 for bf16, which has
+// the fp32 exponent range.  The probabilities' relative precision does not
+// depend on their size, so a high cap only makes the costly raise rarer (with
+// sharp rows, scores of std 9, a cap of 2^8 raised the reference often enough
+// to slow the forward by about a fifth).  The price is range: the fp32
+// numerator sum of up to N probabilities times |V| must stay finite, which for
+// bf16 values bounds |V| by about 2^104 / N.
+template <bool IsBf16> constexpr float kSumCap = IsBf16 ? 16777216.0f : 32768.0f;
 // Exponent offset of a row that has no reference yet (every key seen so far
 // hidden): any visible score then gives probability +inf, so the row sum
 // exceeds kSumCap and the block moves the reference; a hidden one gives 0.
@@ -490,7 +497,7 @@ struct FwdBlock {
     // past its branch, right in front of the next block's first PV MFMA.
     asm volatile("" ::"v"(pw[0]), "v"(pw[1]));
     float s_tot = sum[0] + sum[1];
-    if (!kFirst && __builtin_amdgcn_ballot_w64(s_tot > kSumCap) != 0) {
+    if (!kFirst && __builtin_amdgcn_ballot_w64(s_tot > kSumCap<IsBf16>) != 0) {
       // rare: some probability of this block may exceed the cap (or a row
       // sees its first key).  The scores are formed again from LDS rather
       // than kept live through the block.

@@ -36,7 +36,9 @@ using namespace mfma;
 using namespace tiles;
 
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.f;
+// 2^15 for fp16 (its P operand reaches 65504), 2^24 for bf16 (fp32 exponent
+// range; bounds |V| by about 2^104 / N so that the fp32 numerator sum stays finite)
+template <bool IsBf16> constexpr float kLazy = IsBf16 ? 24.f : 15.f;
 constexpr int kB = 32;       // keys per block (one streamed tile)
 constexpr int kStages = 4;
 
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
       mx = xhalf_max(mx);
       // (-inf) - (-inf) is NaN and compares false: a row that has seen no key
       // yet keeps its reference until a block shows it one
-      if (__builtin_amdgcn_ballot_w64((mx - m) * c > kLazy) != 0) {
+      if (__builtin_amdgcn_ballot_w64((mx - m) * c > kLazy<IsBf16>) != 0) {
         const float m_new = fmaxf(m, mx);
         const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
         l *= alpha;

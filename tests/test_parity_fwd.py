@@ -190,6 +190,26 @@ def test_sharp_rows_fp32(fa, d):
         compare("LSE", lse, rl, LSE_TOL["fp32"])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [128, 256])
+def test_rising_row_maxima(dtype, d, fa):
+    """Sharp rows (q, k ~ N(0, 9)) plus a ramp added to every key, so that a
+    row's maximum keeps rising (or falling) along the keys by up to about 40 in
+    log2 units.  The kernels move a row's reference maximum only when a
+    probability would pass 2^15 (fp16) or 2^24 (bf16); these rows pass it at
+    many different blocks, and also stay below it for long runs."""
+    n = 1500
+    log(f"case rising row maxima dtype={dtype} d={d} N={n}")
+    x = workloads.random_inputs(1, 2, n, d, dtype, seed=80 + d, qk_std=3.0, v_dist="uniform")
+    ramp = np.linspace(0, 0.6, n, dtype=np.float32)[None, None, :, None]
+    x["k"] = workloads.round_to_dtype(x["k"] + ramp, dtype)
+    for causal in (False, True):
+        o, lse = run_fwd(fa, x, dtype, causal)
+        ro, rl = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=causal)
+        compare("O", o, ro, dtype)
+        compare("LSE", lse, rl, LSE_TOL[dtype])
+
+
 # ------------------------------------------------------------------ properties
 
 def test_deterministic(fa):
