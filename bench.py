@@ -41,8 +41,13 @@ METRIC = "attention fwd TFLOP/s (bf16, causal, T=8192, d=128) and % of MFMA peak
 WORKLOAD = "long_causal_bf16"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+# graph replays after the requested warm-up calls, so the timed calls run at
+# the clock the GPU holds under sustained load
+WARMUP_FLOOR_S = 0.5
 KERNEL_SOURCES = ("fwd_mfma.hip", "mfma_common.hpp")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fwd_long_causal_bf16_traffic.md")
+COUNTER_PROFILE = os.path.join(ROOT, "profiles", "fwd_long_causal_bf16_counters.md")
+NOMINAL_SCLK_MHZ = 2400.0       # the clock the published peaks are quoted at
 
 
 def kernel_source_hash() -> str:
@@ -53,20 +58,39 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary.
+def _profile_fields(path, keys):
+    """Machine-readable ``key: value`` lines of a committed rocprofv3 summary.
 
-    Returns None when no summary exists or when it was taken on a different
-    version of the kernel source than the one being benchmarked.
+    Returns None when the file is missing, lacks a key, or was taken on a
+    different version of the kernel source than the one being benchmarked.
     """
-    if not os.path.exists(TRAFFIC_PROFILE):
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_PROFILE).read()
+    text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or m_hash.group(1) != kernel_source_hash():
         return None
-    return float(m_bytes.group(1))
+    out = {}
+    for k in keys:
+        m = re.search(rf"^{k}:\s*([0-9.eE+-]+)\s*$", text, flags=re.M)
+        if not m:
+            return None
+        out[k] = float(m.group(1))
+    return out
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by the copy-kernel calibration)."""
+    f = _profile_fields(TRAFFIC_PROFILE, ["hbm_bytes_per_launch"])
+    return None if f is None else f["hbm_bytes_per_launch"]
+
+
+def measured_counters():
+    """MFMA busy share, shader clock and VALU / LDS instructions per MFMA of the
+    bench kernel, from the committed rocprofv3 SQ counter summary."""
+    return _profile_fields(COUNTER_PROFILE, ["mfma_busy_share", "sclk_mhz", "valu_insts_per_mfma",
+                                             "lds_insts_per_mfma"])
 
 
 def cpu_baseline(w, x, budget_s=12.0):
@@ -100,27 +124,41 @@ def cpu_baseline(w, x, budget_s=12.0):
             "seconds": round(dt, 3), "blas": blas, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
-def time_graph(step, steps, warmup, torch):
-    """Capture `steps` calls of step() in one HIP graph, replay it for the
-    warm-up, then time one replay with events; returns ms per call."""
-    step()
+def time_graph(step, steps, warmup, torch, floor_s=WARMUP_FLOOR_S):
+    """Capture `steps` calls of step() in one HIP graph and time one replay.
+
+    Warm-up: exactly `warmup` eager calls, then graph replays until at least
+    `floor_s` seconds of load have passed (sustained load lowers the shader
+    clock, so a short warm-up would time a cold GPU).  Returns ms per call of
+    the timed replay and a dict describing the warm-up actually run.
+    """
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for _ in range(steps):
             step()
     torch.cuda.synchronize()
-    n_rep = max(1, -(-warmup // steps))  # warm-up calls, rounded up to whole graphs
-    for _ in range(n_rep):
+    t0 = time.perf_counter()
+    n_rep = 0
+    while True:
         graph.replay()
+        n_rep += 1
+        if n_rep % 4 == 0 or floor_s <= 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= floor_s:
+                break
     torch.cuda.synchronize()
+    floor_dt = time.perf_counter() - t0
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     graph.replay()
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps, n_rep * steps
+    return start.elapsed_time(end) / steps, {"calls": warmup, "floor_calls": n_rep * steps,
+                                             "floor_s": round(floor_dt, 3)}
 
 
 def bwd_record(fa, workloads, torch, steps, warmup):
@@ -139,13 +177,13 @@ def bwd_record(fa, workloads, torch, steps, warmup):
         fa.attn_bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
                     workspace=ws, stream=torch.cuda.current_stream(dev))
 
-    # default warm-up: about half a second, as for the forward
     ms, warm = time_graph(step, steps, warmup, torch)
     assert all(torch.isfinite(t).all().item() for t in (dq, dk, dv))
     flops = w.bwd_flops()
     tflops = flops / (ms * 1e-3) / 1e12
     return {"metric": "attention bwd TFLOP/s (bf16, causal, T=4096, d=128)",
-            "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warm,
+            "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warm["calls"],
+            "warmup_floor": {"calls": warm["floor_calls"], "seconds": warm["floor_s"]},
             "ms_per_step": round(ms, 5),
             "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                        "mask": "causal", "scale": w.scale,
@@ -176,7 +214,8 @@ def window_record(fa, workloads, torch, steps, warmup):
     tflops = flops / (ms * 1e-3) / 1e12
     return {"metric": f"attention fwd TFLOP/s (bf16, causal sliding window {w.window}, "
                       f"T={w.N}, d={w.d})",
-            "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warm,
+            "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warm["calls"],
+            "warmup_floor": {"calls": warm["floor_calls"], "seconds": warm["floor_s"]},
             "ms_per_step": round(ms, 5),
             "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                        "mask": "causal", "window": w.window, "scale": w.scale,
@@ -211,7 +250,8 @@ def sparse_record(fa, workloads, torch, steps, warmup):
     band, n_global, n_random, _ = w.sparse
     return {"metric": f"attention fwd TFLOP/s (bf16, block-sparse {100 * float(mask.mean()):.1f} % of "
                       f"64x64 blocks, T={w.N}, d={w.d})",
-            "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warm,
+            "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warm["calls"],
+            "warmup_floor": {"calls": warm["floor_calls"], "seconds": warm["floor_s"]},
             "ms_per_step": round(ms, 5),
             "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                        "mask": "causal" if w.causal else "none",
@@ -270,7 +310,7 @@ def variants_record(fa, workloads, torch, steps, warmup):
     ws256 = torch.empty(fa.bwd_workspace_bytes(1, 16, 8192, 256, fa.BF16), dtype=torch.uint8, device=dev)
     rec("bwd_d256", lambda: fa.attn_bwd(q256, k256, v256, o256, lse256, do256, causal=True, dq=g256[0],
                                         dk=g256[1], dv=g256[2], workspace=ws256),
-        10 * 256 * (8192 * 8193 // 2) * 16, s=10, wm=30)
+        10 * 256 * (8192 * 8193 // 2) * 16, s=10, wm=3)
     # d = 256 with the sliding window of 1024 keys: W (W + 1) / 2 + (N - W) W pairs per head
     wpairs = (1024 * 1025 // 2 + (8192 - 1024) * 1024) * 16
     rec("fwd_d256_window", lambda: fa.attn_fwd(q256, k256, v256, causal=True, window=1024, out=o256),
@@ -280,7 +320,7 @@ def variants_record(fa, workloads, torch, steps, warmup):
     rec("bwd_d256_window", lambda: fa.attn_bwd(q256, k256, v256, o256, lse256w, do256, causal=True,
                                                window=1024, dq=g256[0], dk=g256[1], dv=g256[2],
                                                workspace=ws256),
-        10 * 256 * wpairs, s=10, wm=30)
+        10 * 256 * wpairs, s=10, wm=3)
     # d_v = 64 with d = 128: 2 d + 2 d_v FLOPs per visible pair
     xv = workloads.random_inputs(1, 16, 8192, 64, "bf16", seed=12)
     q, k = (dev_bf16(x[n]).contiguous() for n in "qk")
@@ -296,7 +336,7 @@ def variants_record(fa, workloads, torch, steps, warmup):
     ws64 = torch.empty(fa.bwd_workspace_bytes(1, 16, 8192, 128, fa.BF16), dtype=torch.uint8, device=dev)
     rec("bwd_d128_dv64", lambda: fa.attn_bwd(q, k, v64, o64, lse64, do64, causal=True, dq=g64[0],
                                              dk=g64[1], dv=g64[2], workspace=ws64),
-        (6 * 128 + 4 * 64) * (8192 * 8193 // 2) * 16, s=20, wm=100)
+        (6 * 128 + 4 * 64) * (8192 * 8193 // 2) * 16, s=20, wm=5)
     # backward of the block-sparse and the sliding-window workloads
     for name, wl in (("bwd_block_sparse", "long_sparse_bf16"), ("bwd_window", "long_window_bf16")):
         ww = workloads.WORKLOADS[wl]
@@ -318,7 +358,7 @@ def variants_record(fa, workloads, torch, steps, warmup):
                          device=dev)
         rec(name, lambda: fa.attn_bwd(qq, kk, vv, oo, ll, do, causal=ww.causal, dq=g[0], dk=g[1],
                                       dv=g[2], workspace=ws, **kw),
-            10 * ww.d * pairs * ww.B, s=20, wm=100)
+            10 * ww.d * pairs * ww.B, s=20, wm=5)
     return out
 
 
@@ -375,7 +415,8 @@ def kv_outer_record(fa, workloads, torch, steps, warmup):
     flops = w.fwd_flops()
     tflops = flops / (ms * 1e-3) / 1e12
     return {"metric": "attention fwd TFLOP/s, key/value-outer loop order (bf16, causal, T=8192, d=128)",
-            "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warm,
+            "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warm["calls"],
+            "warmup_floor": {"calls": warm["floor_calls"], "seconds": warm["floor_s"]},
             "ms_per_step": round(ms, 5),
             "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": "causal",
                        "order": "kv_outer", "workgroups": w.B * w.H},
@@ -387,16 +428,17 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # the GPU needs about half a second of load to reach steady clocks
-    ap.add_argument("--warmup", type=int, default=1500)
+    # untimed eager calls; graph replays then add at least WARMUP_FLOOR_S of
+    # load, which the GPU needs to reach its sustained clock
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--bwd-steps", type=int, default=40)
-    ap.add_argument("--bwd-warmup", type=int, default=300)
+    ap.add_argument("--bwd-warmup", type=int, default=10)
     ap.add_argument("--no-window", action="store_true",
                     help="skip the sliding-window forward measurement")
     ap.add_argument("--window-steps", type=int, default=200)
-    ap.add_argument("--window-warmup", type=int, default=1500)
+    ap.add_argument("--window-warmup", type=int, default=10)
     ap.add_argument("--no-sparse", action="store_true",
                     help="skip the block-sparse forward measurement")
     ap.add_argument("--no-variants", action="store_true",
@@ -460,13 +502,15 @@ def main():
     flops = w.fwd_flops()
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic()
+    counters = measured_counters()
     record = {
         "metric": METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": warm,
+        "warmup": args.warmup,
+        "warmup_floor": {"calls": warm["floor_calls"], "seconds": warm["floor_s"]},
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -480,6 +524,18 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
+                     # HBM bytes per launch measured by FETCH_SIZE / WRITE_SIZE, over
+                     # this run's launch time
+                     "hbm_gbs": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1),
+                     "hbm_peak_gbs": PEAK_HBM_GBS,
+                     # MFMA pipe busy share and shader clock from the SQ counters
+                     # (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE) of the same kernel
+                     "mfma_busy": None if counters is None else counters["mfma_busy_share"],
+                     "sclk_mhz": None if counters is None else counters["sclk_mhz"],
+                     "frac_at_sclk": None if counters is None else round(
+                         tflops / (PEAK_BF16_TFLOPS * counters["sclk_mhz"] / NOMINAL_SCLK_MHZ), 4),
+                     "valu_insts_per_mfma": None if counters is None else counters["valu_insts_per_mfma"],
+                     "lds_insts_per_mfma": None if counters is None else counters["lds_insts_per_mfma"],
                      "kernel": "fwd_kernel<bf16, d=128, causal>",
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": w.fwd_bytes(),
@@ -494,8 +550,8 @@ def main():
         record["attn_fwd_block_sparse"] = sparse_record(fa, workloads, torch, args.window_steps,
                                                         args.window_warmup)
     if not args.no_variants:
-        record["variants"] = variants_record(fa, workloads, torch, 50, 300)
-        record["configs"] = configs_record(fa, workloads, torch, 50, 300)
+        record["variants"] = variants_record(fa, workloads, torch, 50, 10)
+        record["configs"] = configs_record(fa, workloads, torch, 50, 10)
     if not args.no_kv_outer:
         record["attn_fwd_kv_outer"] = kv_outer_record(fa, workloads, torch, args.kv_steps,
                                                       args.kv_warmup)

@@ -192,6 +192,36 @@ def kv_outer_workspace_bytes(B, H, N, d, dtype_code):
     return lib().attn_fwd_kv_outer_workspace_bytes(B, H, N, d, dtype_code)
 
 
+def check_buffer(t, name, shape, dtype, device, contiguous=True):
+    """Reject a caller-supplied output or scratch tensor that does not match what
+    the kernels will write through its raw pointer: its shape, dtype and device
+    must be the given ones, and it must be contiguous (or, with
+    ``contiguous=False``, have a contiguous last axis)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not contiguous and t.dim() > 0 and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous last axis")
+
+
+def check_workspace(ws, need, device):
+    """A workspace must be a contiguous uint8 tensor of at least ``need`` bytes on ``device``."""
+    import torch
+    if ws.dtype != torch.uint8:
+        raise TypeError(f"workspace must be uint8, got {ws.dtype}")
+    if ws.device != device:
+        raise ValueError(f"workspace must be on {device}, got {ws.device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} needed")
+
+
 def _torch_dtype_code(t):
     import torch
     codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
@@ -221,14 +251,20 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, *, out=N
     for t in (q, k, v):
         if not t.is_cuda or t.stride(-1) != 1:
             raise ValueError("q, k, v must be device tensors with a contiguous last axis")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one device")
     B, H, N, d = q.shape
     dv = v.shape[-1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q) if dv == d else torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    else:
+        check_buffer(out, "out", (B, H, N, dv), q.dtype, q.device, contiguous=False)
     if return_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif return_lse:
+        check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     if dv != d:
@@ -311,11 +347,17 @@ def attn_fwd_kv_outer(q, k, v, causal: bool = False, scale: float | None = None,
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        check_buffer(out, "out", (B, H, N, d), q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
     need = kv_outer_workspace_bytes(B, H, N, d, code)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        check_workspace(workspace, need, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = lib().attn_fwd_kv_outer(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -350,14 +392,16 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     for t in (q, k, v, o, dout):
         if not t.is_cuda or t.stride(-1) != 1:
             raise ValueError("inputs must be device tensors with a contiguous last axis")
-    if not lse.is_cuda or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous device tensor")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape[:3]):
-        raise ValueError("lse must be float32 [B, H, N]")
+    if any(t.device != q.device for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o and dout must be on one device")
+    check_buffer(lse, "lse", tuple(shape[:3]), torch.float32, q.device)
     B, H, N, d = shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     code = _torch_dtype_code(q)
+    for g, name, like in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        if g is not None:
+            check_buffer(g, name, tuple(like.shape), like.dtype, q.device, contiguous=False)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -365,6 +409,8 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
         B, H, N, d, code)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        check_workspace(workspace, need, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -428,3 +474,4 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if st != 0:
         raise FaError(st, "attn_bwd")
     return dq, dk, dv
+

@@ -263,7 +263,9 @@ int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse
                 void* stream) {
   if (dv < 1) return FA_ERR_SHAPE;
   if (dv != 64 && dv != 96 && dv != 128 && dv != 256) return FA_ERR_UNSUPPORTED;
-  if (N > 0 && N * dv * (dtype == FA_F32 ? 4 : 2) > INT32_MAX - 1024) return FA_ERR_SHAPE;
+  // bound N first: N * dv * 4 then cannot overflow int64
+  if (N > 0 && (N > INT32_MAX / 2 || N * dv * (dtype == FA_F32 ? 4 : 2) > INT32_MAX - 1024))
+    return FA_ERR_SHAPE;
   return fwd_impl(q, k, v, o, lse, B, H, N, d, mask, N, scale, dtype, stream, nullptr, nullptr,
                   nullptr, nullptr, 0, 0, dv);
 }
@@ -274,7 +276,9 @@ int attn_bwd_dv(const void* q, const void* k, const void* v, const void* o, cons
                 size_t workspace_bytes, void* stream) {
   if (d_v < 1) return FA_ERR_SHAPE;
   if (d_v != 64 && d_v != 96 && d_v != 128 && d_v != 256) return FA_ERR_UNSUPPORTED;
-  if (N > 0 && N * d_v * (dtype == FA_F32 ? 4 : 2) > INT32_MAX - 1024) return FA_ERR_SHAPE;
+  // bound N first: N * d_v * 4 then cannot overflow int64
+  if (N > 0 && (N > INT32_MAX / 2 || N * d_v * (dtype == FA_F32 ? 4 : 2) > INT32_MAX - 1024))
+    return FA_ERR_SHAPE;
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, N, scale, dtype, workspace,
                   workspace_bytes, stream, nullptr, nullptr, nullptr, 0, 0, d_v);
 }
@@ -324,7 +328,10 @@ const char* fa_status_str(int status) {
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_MASK: return "unknown mask";
     case FA_ERR_SCALE: return "scale is not finite";
-    case FA_ERR_UNSUPPORTED: return "unsupported: head dimension must be 64, 96 or 128 (backward: fp16/bf16 only)";
+    case FA_ERR_UNSUPPORTED:
+      return "unsupported: head dimension must be 64, 96, 128 or 256 (256: fp16/bf16 and plain, "
+             "strided, window or block-sparse calls only), d_v must be d or (d, d_v) in {(128, 64), "
+             "(64, 128)}; the backward and the key/value-outer forward take fp16/bf16 only";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "the HIP runtime rejected a launch";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";

@@ -16,7 +16,9 @@
 // into dS = P (dP - D), where dP and D nearly cancel on a row's dominant
 // keys; so D is formed from the recomputed P and dP in fp32 instead.
 //
-// Two kernels, no atomics, so the result is deterministic:
+// Two kernels whose sums run in a fixed order, so the result is deterministic
+// (the only atomic is the block-sparse split path's per-key-block counter,
+// which picks the workgroup that adds the partial sums, in chunk order):
 //   * bwd_dq:     a workgroup keeps 128 query rows resident (Q^T and dO^T in
 //                 registers) and streams 64-key tiles of K and V through LDS
 //                 twice: pass 1 accumulates D = sum_j P dP and stores it in

@@ -40,10 +40,11 @@
 //  * exp is exp2 with scale*log2(e) folded into one FMA per score.  The
 //    probabilities of a block are taken against the current reference maximum
 //    without first computing the block's own maximum; the block's fp32
-//    partial row sums reveal whether any probability exceeded 2^8, and only
-//    then is the reference raised to the true running maximum,
-//    a and l rescaled and the block's probabilities recomputed.  Any reference
-//    value gives the same a / l and LSE; the check keeps probabilities <= 256.
+//    partial row sums reveal whether any probability may exceed the cap
+//    (2^15 for fp16, 2^24 for bf16, kSumCap below), and only then is the
+//    reference raised to the true running maximum, a and l rescaled and the
+//    block's probabilities recomputed.  Any reference value gives the same
+//    a / l and LSE; the check keeps every probability below the cap.
 //  * Causal: tiles entirely above a wave's rows are skipped, the mask is only
 //    evaluated on blocks that cross the diagonal or the sequence end.
 #include <hip/hip_runtime.h>

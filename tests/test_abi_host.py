@@ -401,3 +401,57 @@ def test_block_sparse_backward_workspace():
                                             200, 64, P[7], 1, 1, 0, 0.125, fa.BF16, P[1], ws, None)
     assert bb(need - 1) == FA_ERR_WORKSPACE
     assert bb(need) == FA_ERR_ALIGN        # big enough: reaches the pointer checks
+
+
+# ------------------------------------------------------------------ caller buffers
+
+def test_binding_rejects_mismatched_buffers():
+    """The binding passes raw pointers, so every caller-supplied output or
+    scratch tensor is checked against what the kernels write through it:
+    shape, dtype, device and contiguity (host tensors stand in for device
+    ones; the device compared is q's)."""
+    torch = pytest.importorskip("torch")
+    from io_aware_exact_12_amd._binding import check_buffer, check_workspace
+    cpu = torch.device("cpu")
+    good = torch.empty((2, 3, 5, 64), dtype=torch.bfloat16)
+    check_buffer(good, "out", (2, 3, 5, 64), torch.bfloat16, cpu)          # accepted
+    with pytest.raises(ValueError, match="shape"):                          # too small an out
+        check_buffer(torch.empty((2, 3, 4, 64), dtype=torch.bfloat16), "out", (2, 3, 5, 64),
+                     torch.bfloat16, cpu)
+    with pytest.raises(TypeError, match="float16"):                         # another 16-bit type
+        check_buffer(good, "out", (2, 3, 5, 64), torch.float16, cpu)
+    with pytest.raises(TypeError, match="float32"):                         # bf16 lse
+        check_buffer(torch.empty((2, 3, 5), dtype=torch.bfloat16), "lse", (2, 3, 5), torch.float32, cpu)
+    with pytest.raises(ValueError, match="shape"):                          # lse of another shape
+        check_buffer(torch.empty((2, 3, 6), dtype=torch.float32), "lse", (2, 3, 5), torch.float32, cpu)
+    with pytest.raises(ValueError, match="on"):                             # another device
+        check_buffer(good.to("meta"), "dq", (2, 3, 5, 64), torch.bfloat16, cpu)
+    with pytest.raises(ValueError, match="contiguous"):                     # strided lse
+        check_buffer(torch.empty((2, 3, 10), dtype=torch.float32)[..., ::2], "lse", (2, 3, 5),
+                     torch.float32, cpu)
+    t = torch.empty((2, 5, 3, 64), dtype=torch.bfloat16).transpose(1, 2)    # [B][N][H][d] view
+    check_buffer(t, "dq", (2, 3, 5, 64), torch.bfloat16, cpu, contiguous=False)
+    with pytest.raises(ValueError, match="last axis"):
+        check_buffer(torch.empty((2, 3, 5, 128), dtype=torch.bfloat16)[..., ::2], "dq",
+                     (2, 3, 5, 64), torch.bfloat16, cpu, contiguous=False)
+    ws = torch.empty(100, dtype=torch.uint8)
+    check_workspace(ws, 100, cpu)
+    with pytest.raises(ValueError, match="needed"):
+        check_workspace(ws, 101, cpu)
+    with pytest.raises(TypeError, match="uint8"):
+        check_workspace(torch.empty(100, dtype=torch.int8), 100, cpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        check_workspace(torch.empty(200, dtype=torch.uint8)[::2], 100, cpu)
+    with pytest.raises(ValueError, match="on"):
+        check_workspace(ws.to("meta"), 100, cpu)
+
+
+def test_dv_calls_reject_huge_n_before_multiplying():
+    """attn_fwd_dv / attn_bwd_dv bound N before forming N * d_v * 4, so a huge
+    N is a shape error, not an overflowed product."""
+    L = fa.lib()
+    huge = 1 << 61
+    assert fa.attn_fwd_dv_raw(16, 16, 16, 16, None, 1, 1, huge, 128, 64, 0, 0.1, fa.BF16, None) == FA_ERR_SHAPE
+    assert fa.attn_bwd_dv_raw(16, 16, 16, 16, 16, 16, 16, 16, 16, 1, 1, huge, 128, 64, 0, 0.1,
+                              fa.BF16, 16, 1 << 20, None) == FA_ERR_SHAPE
+    assert L is not None

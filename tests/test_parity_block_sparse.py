@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+import whole_output
 import workloads
 
 torch = pytest.importorskip("torch")
@@ -145,16 +146,19 @@ def test_block_sparse_all_hidden(fa):
     run_case(fa, x, "bf16", False, np.zeros((1, 1, 4, 4), np.uint8))
 
 
-def test_block_sparse_bench_workload_sampled_rows(fa):
+def test_block_sparse_bench_workload_all_rows(fa):
     """The measured block-sparse workload (B=1, H=16, N=8192, d=128, bf16; band,
-    global and random blocks) at full size, on sampled rows of every head."""
+    global and random blocks) at full size, every row of every head."""
     w = workloads.WORKLOADS["long_sparse_bf16"]
     x = workloads.make_inputs(w)
     mask = workloads.block_sparse_mask(w.N, w.H, *w.sparse)
-    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(4090, 4100), np.arange(w.N - 8, w.N),
-                                     np.random.default_rng(9800).integers(0, w.N, 40)]))
     log(f"case block-sparse bench workload {w.name}")
-    run_case(fa, x, "bf16", w.causal, mask, rows=rows)
+    q, k, v = (torch.from_numpy(x[n]).to("cuda").to(torch.bfloat16).contiguous() for n in "qkv")
+    o, lse = fa.attn_fwd(q, k, v, causal=w.causal, block_mask=torch.from_numpy(mask).to("cuda"))
+    torch.cuda.synchronize()
+    whole_output.compare_fwd_all_rows(o.float().cpu().numpy(), lse.cpu().numpy(), x, w.causal,
+                                      w.scale, TOL["bf16"], TOL["lse"], block_mask=mask,
+                                      label=f"{w.name} ")
 
 
 def bwd_case(fa, x, dtype, causal, mask):

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+import whole_output
 import workloads
 
 torch = pytest.importorskip("torch")
@@ -66,8 +67,8 @@ def test_dv_forward_sweep(fa, dtype, d, dv, causal):
         compare("LSE", lse.cpu().numpy(), rl, "fp32" if dtype == "fp32" else "lse")
 
 
-def test_dv_long_head_sampled_rows(fa):
-    """A long head (B=1, H=4, N=4099, d=128, dv=64, causal) on sampled rows."""
+def test_dv_long_head_all_rows(fa):
+    """A long head (B=1, H=4, N=4099, d=128, dv=64, causal), every row."""
     n = 4099
     xq = workloads.random_inputs(1, 4, n, 128, "bf16", 9990)
     xv = workloads.random_inputs(1, 4, n, 64, "bf16", 9991)
@@ -76,11 +77,9 @@ def test_dv_long_head_sampled_rows(fa):
     log("case dv long head")
     o, lse = fa.attn_fwd(q, k, v, causal=True)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(n - 70, n),
-                                     np.random.default_rng(9992).integers(0, n, 60)]))
-    ro, rl = oracle.dense_fwd(xq["q"], xq["k"], xv["v"], causal=True, rows=rows)
-    compare("O", o.float().cpu().numpy()[:, :, rows], ro, "bf16")
-    compare("LSE", lse.cpu().numpy()[:, :, rows], rl, "lse")
+    whole_output.compare_fwd_all_rows(o.float().cpu().numpy(), lse.cpu().numpy(), xq, True,
+                                      1.0 / np.sqrt(128), TOL["bf16"], TOL["lse"], v=xv["v"],
+                                      label="d=128 dv=64 ")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])

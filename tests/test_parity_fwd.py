@@ -6,9 +6,8 @@ element.  Tolerances: fp32 max |err| <= 1e-5 on O and LSE; fp16/bf16
 |err| <= 2e-2 + 1e-2 |ref| on O.  The LSE is an fp32 output computed from the
 rounded inputs in fp32 whatever the input type, so for fp16/bf16 inputs it is
 held to |err| <= 1e-4 + 1e-5 |ref| (fp32 score sums, exp2 and a row sum of up
-to 8192 fp32 probabilities).  Full-size workloads compare a
-sample of rows (first, last, tile and block boundaries, the ragged tail and
-random rows of every head); the dense oracle computes those rows exactly.
+to 8192 fp32 probabilities).  Full-size workloads compare every row of every
+head, the dense oracle running head by head on blocks of rows.
 """
 import math
 import sys
@@ -17,6 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
+import whole_output
 import workloads
 
 torch = pytest.importorskip("torch")
@@ -98,16 +98,15 @@ def test_gpt2s_causal_bf16_full(fa):
 
 
 @pytest.mark.parametrize("name", ["long_causal_bf16", "ragged_sharp_fp16", "fwd_bwd_causal_bf16"])
-def test_large_workload_sampled_rows(fa, name):
+def test_large_workload_all_rows(fa, name):
+    """The three full-size forward workloads, every row of every head."""
     w = workloads.WORKLOADS[name]
     log(f"case {w}")
     x = workloads.make_inputs(w)
     o, lse = run_fwd(fa, x, w.dtype, w.causal)
-    rows = sample_rows(w.N, seed=w.seed)
-    ro, rl = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, rows=rows)
-    compare("O[rows]", o[:, :, rows], ro, w.dtype)
-    compare("LSE[rows]", lse[:, :, rows], rl, LSE_TOL[w.dtype])
-    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    whole_output.compare_fwd_all_rows(o, lse, x, w.causal, w.scale, TOL[w.dtype],
+                                      TOL[LSE_TOL[w.dtype]], label=f"{name} ")
+    assert np.isfinite(lse).all()
 
 
 # ------------------------------------------------------------------ sweep

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+import whole_output
 import workloads
 
 torch = pytest.importorskip("torch")
@@ -86,16 +87,18 @@ def test_kv_outer_scales_and_sharp_rows(fa):
     run_case(fa, xs, "fp16", False)
 
 
-def test_kv_outer_bench_workload_sampled_rows(fa):
-    """The long causal head (B=1, H=16, N=8192, d=128, bf16) on sampled rows of
-    every head, and the whole output against the query-outer kernel."""
+def test_kv_outer_bench_workload_all_rows(fa):
+    """The long causal head (B=1, H=16, N=8192, d=128, bf16), every row of every
+    head against the oracle, and the whole output against the query-outer
+    kernel."""
     w = workloads.WORKLOADS["long_causal_bf16"]
     x = workloads.make_inputs(w)
-    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(250, 262), np.arange(w.N - 8, w.N),
-                                     np.random.default_rng(8200).integers(0, w.N, 40)]))
     log(f"case kv_outer bench workload {w.name}")
-    run_case(fa, x, "bf16", True, rows=rows)
     q, k, v = (to_dev(x[n], "bf16") for n in "qkv")
+    o, lse = fa.attn_fwd_kv_outer(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    whole_output.compare_fwd_all_rows(o.float().cpu().numpy(), lse.cpu().numpy(), x, True, w.scale,
+                                      TOL["o"], TOL["lse"], label=f"{w.name} kv_outer ")
     o1, l1 = fa.attn_fwd_kv_outer(q, k, v, causal=True)
     o2, l2 = fa.attn_fwd(q, k, v, causal=True)
     torch.cuda.synchronize()

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
+import whole_output
 import workloads
 
 torch = pytest.importorskip("torch")
@@ -93,25 +94,29 @@ def test_window_fwd_sweep_d256(fa, dtype):
              dtype, 150)
 
 
-def test_window_fwd_long_sampled_rows(fa):
+def fwd_all_rows(fa, x, w, label):
+    q, k, v = (to_dev(x[n], "bf16") for n in "qkv")
+    o, lse = fa.attn_fwd(q, k, v, causal=True, window=w)
+    torch.cuda.synchronize()
+    whole_output.compare_fwd_all_rows(o.float().cpu().numpy(), lse.cpu().numpy(), x, True,
+                                      1.0 / np.sqrt(x["q"].shape[-1]), TOL["bf16"], TOL["lse"],
+                                      window=w, label=label)
+
+
+def test_window_fwd_long_all_rows(fa):
     n, w = 4099, 1000
     log(f"case window fwd long N={n} W={w}")
     x = workloads.random_inputs(1, 4, n, 128, "bf16", seed=7100)
-    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(990, 1010), np.arange(n - 70, n),
-                                     np.random.default_rng(7101).integers(0, n, 200)]))
-    fwd_case(fa, x, "bf16", w, rows=rows)
+    fwd_all_rows(fa, x, w, f"N={n} W={w} ")
 
 
-def test_window_bench_workload_sampled_rows(fa):
+def test_window_bench_workload_all_rows(fa):
     """The benchmarked window workload at full size (B=1, H=16, N=8192, d=128,
-    W=1024, bf16), in the launch the benchmark times, on sampled rows of
-    every head: the first window, its edge, the tail and random rows."""
+    W=1024, bf16), in the launch the benchmark times, every row of every head."""
     w = workloads.WORKLOADS["long_window_bf16"]
     log(f"case window bench workload {w.name} N={w.N} W={w.window}")
     x = workloads.make_inputs(w)
-    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(1016, 1032), np.arange(w.N - 8, w.N),
-                                     np.random.default_rng(7150).integers(0, w.N, 40)]))
-    fwd_case(fa, x, "bf16", w.window, rows=rows)
+    fwd_all_rows(fa, x, w.window, f"{w.name} ")
 
 
 def test_window_at_least_n_equals_causal(fa):
