@@ -22,8 +22,9 @@
  * always a dense [B][H][N] float array.
  *
  * Ownership.  All pointers belong to the caller; the library never allocates,
- * frees or retains them, and holds no mutable global state.  ``o`` must not
- * overlap q, k or v.
+ * frees or retains them.  Its only mutable global state is the fixed scratch
+ * array of attn_bwd_noalloc (one copy per GPU) and the table of its device
+ * addresses.  ``o`` must not overlap q, k or v.
  *
  * Streams and errors.  Work is enqueued on ``stream`` (a hipStream_t; NULL is
  * the default stream) and the call returns without waiting.  Every argument
@@ -62,7 +63,8 @@ enum fa_status {
   FA_ERR_HIP = 8,         /* the HIP runtime rejected a launch                  */
   FA_ERR_ALIGN = 9,       /* a tensor pointer is not 16-byte aligned            */
   FA_ERR_WINDOW = 10,     /* sliding window < 1                                 */
-  FA_ERR_STRIDE = 11      /* a stride is unusable (see attn_fwd_strided)        */
+  FA_ERR_STRIDE = 11,     /* a stride is unusable (see attn_fwd_strided)        */
+  FA_ERR_SCRATCH = 12     /* the problem exceeds attn_bwd_noalloc's fixed scratch */
 };
 
 /*
@@ -167,6 +169,31 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
                     int64_t B, int64_t H, int64_t N, int64_t d, int64_t window,
                     float scale, int dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.
+ *
+ * Same arguments, results and errors as attn_bwd (all mask, scale, dtype and
+ * head-dimension rules included; the gradients are bitwise those of attn_bwd),
+ * except that the scratch attn_bwd takes from `workspace` lives in a fixed
+ * array of 8 MiB inside the library, so B * H * N may not exceed
+ * attn_bwd_noalloc_max_rows() = 1,048,576 query rows (FA_ERR_SCRATCH
+ * otherwise).  The call allocates nothing.  Each GPU holds its own copy of
+ * the array from the first call on it until the process ends, and every call
+ * on that GPU uses it: calls that overlap in time on one GPU (other streams,
+ * other threads) race on it and must be serialised by the caller.  Nothing in
+ * it needs to start at zero: every scratch value the kernels read is written
+ * earlier in the same call.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int64_t B, int64_t H, int64_t N, int64_t d,
+                     int mask, float scale, int dtype, void* stream);
+
+/* Largest B * H * N that attn_bwd_noalloc accepts. */
+size_t attn_bwd_noalloc_max_rows(void);
 
 /* Bytes of workspace attn_bwd needs for these sizes (8 * B * H * N today);
  * 0 if the sizes, d or dtype are invalid. */

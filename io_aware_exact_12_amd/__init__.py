@@ -9,6 +9,7 @@ from ._binding import (BF16, F16, F32, MASK_CAUSAL, MASK_NONE, FaError,  # noqa:
                        attn_fwd_kv_outer_raw, attn_fwd_raw, attn_fwd_window_raw,
                        attn_fwd_strided_raw, attn_bwd_strided_raw, attn_fwd_block_sparse_raw,
                        attn_fwd_dv_raw, attn_bwd_dv_raw,
-                       attn_bwd_block_sparse_raw,
+                       attn_bwd_block_sparse_raw, attn_bwd_noalloc, attn_bwd_noalloc_raw,
+                       noalloc_max_rows,
                        bwd_workspace_bytes, bwd_block_sparse_workspace_bytes, declared_symbols, kv_outer_workspace_bytes, lib,
                        status_str)

@@ -76,6 +76,11 @@ def lib():
         L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.attn_bwd_block_sparse_workspace_bytes.restype = ctypes.c_size_t
         L.attn_bwd_block_sparse_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        L.attn_bwd_noalloc.restype = ctypes.c_int
+        L.attn_bwd_noalloc.argtypes = [vp] * 9 + [i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                                  ctypes.c_int, vp]
+        L.attn_bwd_noalloc_max_rows.restype = ctypes.c_size_t
+        L.attn_bwd_noalloc_max_rows.argtypes = []
         L.fa_status_str.restype = ctypes.c_char_p
         L.fa_status_str.argtypes = [ctypes.c_int]
         L.fa_abi_version.restype = ctypes.c_int
@@ -105,6 +110,17 @@ def attn_bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, scale, dty
     """Direct call of the C entry point with integer pointers; returns the status."""
     return lib().attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, scale, dtype, ws,
                           ws_bytes, stream)
+
+
+def attn_bwd_noalloc_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, scale, dtype, stream):
+    """Direct call of the allocation-free backward entry point; returns the status."""
+    return lib().attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, scale, dtype,
+                                  stream)
+
+
+def noalloc_max_rows():
+    """Largest B * H * N the allocation-free backward accepts."""
+    return lib().attn_bwd_noalloc_max_rows()
 
 
 def attn_fwd_window_raw(q, k, v, o, lse, B, H, N, d, window, scale, dtype, stream):
@@ -475,3 +491,35 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
         raise FaError(st, "attn_bwd")
     return dq, dk, dv
 
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, *,
+                     dq, dk, dv, stream=None):
+    """attn_bwd through the allocation-free entry point (``attn_bwd_noalloc``):
+    the caller passes dq, dk and dv, and the backward's scratch is the
+    library's fixed per-GPU array, so nothing is allocated here or in the
+    library.  Contiguous [B, H, N, d] fp16 / bf16 tensors only; B * H * N at
+    most ``noalloc_max_rows()``.  Calls that overlap on one GPU race on the
+    shared scratch."""
+    import torch
+    shape = q.shape
+    for t in (k, v, o, dout):
+        if t.shape != shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, o and dout must share one [B, H, N, d] shape, dtype and device")
+    for t in (q, k, v, o, dout):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous device tensors")
+    check_buffer(lse, "lse", tuple(shape[:3]), torch.float32, q.device)
+    for g, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        check_buffer(g, name, tuple(shape), q.dtype, q.device)
+    B, H, N, d = shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = attn_bwd_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), B, H, N, d, MASK_CAUSAL if causal else MASK_NONE,
+                              float(scale), _torch_dtype_code(q), stream.cuda_stream)
+    if st != 0:
+        raise FaError(st, "attn_bwd_noalloc")
+    return dq, dk, dv

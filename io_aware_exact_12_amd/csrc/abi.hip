@@ -3,13 +3,14 @@
 #include <hip/hip_runtime.h>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa_attn.h"
 #include "fa_internal.hpp"
 
 namespace {
 
-constexpr int kAbiVersion = 10;
+constexpr int kAbiVersion = 11;
 // Block-sparse: mask blocks of 64 x 64; a query block of the forward lists at
 // most this many key tiles (its LDS list).
 constexpr int64_t kMaxSparseTiles = 2048;
@@ -202,6 +203,35 @@ int kv_outer_impl(const void* q, const void* k, const void* v, void* o, float* l
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// ---------------------------------------------------------------- allocation-free backward
+// attn_bwd_noalloc takes its scratch (the backward's two fp32 terms per query
+// row, fa::bwd_workspace_bytes) from this fixed array instead of a caller
+// workspace.  Every GPU the library runs on holds its own copy until the
+// process ends; calls on one GPU share it, so calls that overlap in time on
+// one GPU race on it.
+constexpr size_t kScratchBytes = (size_t)8 << 20;  // B * H * N <= 1,048,576 query rows
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device (with that device current) and kept.  In host code the array's name
+// is only a host-side stand-in: kernels get this address, never the name.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -229,6 +259,22 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              void* stream) {
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, N, scale, dtype, workspace,
                   workspace_bytes, stream);
+}
+
+size_t attn_bwd_noalloc_max_rows(void) { return kScratchBytes / 8; }
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                     int64_t d, int mask, float scale, int dtype, void* stream) {
+  // the shape checks bound B * H * N before the scratch size is formed
+  const int st = check_common(B, H, N, d, mask, scale, dtype);
+  if (st != FA_OK) return st;
+  if (fa::bwd_workspace_bytes(B, H, N) > kScratchBytes) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int e = scratch_of_current_device(&ws);
+  if (e != FA_OK) return e;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, mask, N, scale, dtype, ws,
+                  kScratchBytes, stream);
 }
 
 int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -337,6 +383,9 @@ const char* fa_status_str(int status) {
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_WINDOW: return "sliding window must be >= 1";
     case FA_ERR_STRIDE: return "a stride is negative, not a multiple of 16 bytes, below d (rows), or makes output rows overlap";
+    case FA_ERR_SCRATCH:
+      return "B * H * N exceeds the fixed scratch of the allocation-free backward "
+             "(attn_bwd_noalloc_max_rows() query rows)";
     default: return "unknown status";
   }
 }

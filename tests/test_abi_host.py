@@ -14,7 +14,7 @@ import io_aware_exact_12_amd as fa
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_DTYPE, FA_ERR_MASK, FA_ERR_SCALE, \
     FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_ALIGN, FA_ERR_WINDOW, \
-    FA_ERR_STRIDE = range(12)
+    FA_ERR_STRIDE, FA_ERR_SCRATCH = range(13)
 
 # fake, never-dereferenced addresses: validation fails before any use
 P = [0x10000 * (i + 1) for i in range(8)]
@@ -30,17 +30,18 @@ def test_library_exports_every_declared_symbol():
     assert {"attn_fwd", "attn_bwd", "attn_fwd_window", "attn_bwd_window", "attn_bwd_workspace_bytes",
             "attn_fwd_kv_outer", "attn_fwd_kv_outer_workspace_bytes", "attn_fwd_strided",
             "attn_bwd_strided", "attn_fwd_block_sparse", "attn_bwd_block_sparse", "attn_fwd_dv",
-            "attn_bwd_dv", "attn_bwd_block_sparse_workspace_bytes",
+            "attn_bwd_dv", "attn_bwd_block_sparse_workspace_bytes", "attn_bwd_noalloc",
+            "attn_bwd_noalloc_max_rows",
             "fa_status_str",
             "fa_abi_version"} <= set(declared)
     lib = ctypes.CDLL(fa._binding.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
-    assert fa.lib().fa_abi_version() == 10
+    assert fa.lib().fa_abi_version() == 11
 
 
 def test_status_strings():
-    for st in range(12):
+    for st in range(13):
         assert fa.status_str(st) and fa.status_str(st) != "unknown status"
     assert fa.status_str(123) == "unknown status"
 
