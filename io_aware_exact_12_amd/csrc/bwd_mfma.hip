@@ -479,6 +479,239 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dkdv(
   if (store) store_row<IsBf16, D>(dK + head_out, blk.my_k, out.sn, blk.g, blk.acc, dk_mul);
 }
 
+// ---------------------------------------------------------------- dK, dV (wave pairs)
+// Plain and sliding-window masks, d = d_v <= 128.  A workgroup of 8 waves
+// keeps 128 keys resident; waves w and w + 4 (one SIMD) share keys
+// kw0 .. kw0 + 31 and split the work on each streamed 64-query tile:
+//   wave A (w < 4): S = Q K^T, P = exp2(c S - LSE2), P to LDS;  dV^T += dO^T P
+//   wave B (w >= 4):  dP = dO V^T;  P from LDS, dS = P (dP - D); dK^T += Q^T dS
+// In the first phase of a tile A forms the scores and probabilities while B
+// forms dP; a workgroup barrier hands P over; in the second phase A
+// accumulates dV while B forms dS and accumulates dK.  S is formed once per
+// (query, key) pair instead of once in each of two passes, and the Q and dO
+// tiles stream through LDS once.  The arithmetic of every result is that of
+// the two-pass kernel above (same MFMA chains, same fp32 P and dS formulas),
+// so the gradients are bitwise the same.
+constexpr int kPW = 8;            // waves of the pair kernel
+constexpr int kPThr = 64 * kPW;
+
+template <int D> struct PairLds {
+  using St = DkdvLds<D, D>;
+  static constexpr int kStage = St::kStage;          // Q, dO, -LSE log2(e), D of 64 queries
+  static constexpr int kP = 2 * kStage;              // P of [pair][half]: 16 fp32 a lane
+  static constexpr int kPHalf = 64 * 16 * 4;         // 4 KB
+  static constexpr int kBytes = kP + 4 * 2 * kPHalf;
+  static_assert(kBytes <= 160 * 1024, "fits the LDS of a CU");
+};
+
+// This wave's copies of a 64-row streamed tile when 8 waves share them:
+// copy i of wave w fills LDS bytes [(w + 8 i) KB, +1 KB).
+template <int D> struct PairCopy {
+  using T = STile<D>;
+  static constexpr int kPerWave = T::kCopies / kPW;
+  static_assert(kPerWave * kPW == T::kCopies, "tile copies split evenly over 8 waves");
+  static __device__ __forceinline__ void sources(int wave, int lane, uint32_t row_bytes,
+                                                 uint32_t (&src)[kPerWave]) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int byte = (wave + kPW * i) * 1024 + 16 * lane;
+      const int r = byte / T::kRowBytes, phys = (byte % T::kRowBytes) / 16;
+      src[i] = (uint32_t)tile_row(r) * row_bytes + (uint32_t)(16 * (phys ^ T::swz(r)));
+    }
+  }
+  static __device__ __forceinline__ void copy(uint32_t lds_addr, const uint16_t* base, int rows, int row0,
+                                              int64_t sn, int wave, const uint32_t (&src)[kPerWave]) {
+    const int left = rows - row0;
+    const i32x4 rs = make_rsrc(base + (int64_t)row0 * sn,
+                               left > 0 ? (uint32_t)(left - 1) * (uint32_t)(2 * sn) + (uint32_t)T::kDataBytes : 0u);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) dma16(rs, lds_addr + (uint32_t)((wave + kPW * i) * 1024), src[i]);
+  }
+};
+
+// Workgroup barrier that waits for this wave's LDS traffic only (the HBM ->
+// LDS copies in flight keep going; they are waited for at the end of a tile).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <bool IsBf16, int D, bool Causal, int Mode>
+__global__ __launch_bounds__(kPThr, 1) void bwd_dkdv_pair(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ NLse, const float* __restrict__ Dsum,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int win, int H, int BH, float c,
+    float dk_mul, uint32_t k_sign, Layout in, Layout out) {
+  using E = Elt<IsBf16>;
+  using vec8 = typename E::vec8;
+  using Ld = PairLds<D>;
+  using St = DkdvLds<D, D>;
+  using PC = PairCopy<D>;
+  static_assert(Mode == kModePlain || Mode == kModeWindow, "plain and window masks");
+  constexpr bool kWin = Causal && Mode == kModeWindow;
+  constexpr int kKs = D / 16, kDB = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair = wave & 3;
+  const bool role_a = wave < 4;  // wave-uniform
+  const int bh = blockIdx.x % BH;
+  const int kblk = blockIdx.x / BH;  // heaviest (earliest keys) first
+  const int b = bh / H, h = bh - b * H;
+  const int64_t head = b * in.sb + h * in.sh, head_out = b * out.sb + h * out.sh;
+  const int k0 = kblk * kRes, kw0 = k0 + 32 * pair;
+
+  DkdvBlock<IsBf16, D, Causal, Mode, D> blk;
+  blk.init(lane, N, win, kw0, c);
+
+  const int n_tiles = kWin ? min((N + kT - 1) / kT, (k0 + kRes - 1 + win - 1) / kT + 1) : (N + kT - 1) / kT;
+  const int t_first = Causal ? k0 / kT : 0;
+  const int n_it = n_tiles - t_first;
+  const uint16_t* q_h = Q + head;
+  const uint16_t* do_h = dO + head;
+  const float* nl_h = NLse + (int64_t)bh * N;
+  const float* d_h = Dsum + (int64_t)bh * N;
+  uint32_t src[PC::kPerWave];
+  PC::sources(wave, lane, (uint32_t)(2 * in.sn), src);
+  const uint32_t lds0 = lds_u32(smem);
+
+  auto issue = [&](int it, int st) {
+    const int qt0 = it * kT;
+    const uint32_t base = lds0 + (uint32_t)(st * Ld::kStage);
+    PC::copy(base + St::kQ, q_h, N, qt0, in.sn, wave, src);
+    PC::copy(base + St::kDO, do_h, N, qt0, in.sn, wave, src);
+    const int left = N - qt0;
+    if (wave < 2) {
+      const i32x4 rs = make_rsrc(wave == 0 ? nl_h + qt0 : d_h + qt0, left > 0 ? (uint32_t)left * 4u : 0u);
+      dma4(rs, base + (uint32_t)(wave == 0 ? St::kLse : St::kD), (uint32_t)lane * 4u);
+    }
+  };
+  auto live = [&](int it) {
+    return kw0 < N && !(Causal && it * kT + kT - 1 < kw0) && !(kWin && it * kT > kw0 + 31 + win - 1);
+  };
+  auto masked = [&](int it) {
+    const int qt0 = it * kT;
+    return (Causal && qt0 < kw0 + 32) || (kWin && qt0 + kT - 1 >= kw0 + win) || qt0 + kT > N ||
+           kw0 + 32 > N;
+  };
+  // P of (this pair, half hh): 16 fp32 a lane as four 16-byte chunks, chunk j
+  // of lane l at 16 (64 j + l) (each chunk write / read is 1 KB contiguous)
+  float* const pbuf = reinterpret_cast<float*>(smem + Ld::kP + pair * 2 * Ld::kPHalf);
+  auto p_at = [&](int hh, int j) { return reinterpret_cast<f32x4*>(pbuf + hh * (Ld::kPHalf / 4)) + 64 * j + lane; };
+
+  issue(t_first, 0);
+  wait_copies();
+  __syncthreads();
+  blk.zero();
+  if (role_a) {
+    load_resident<IsBf16, D>(blk.kf, K + head, N, blk.my_k, in.sn, blk.g, k_sign);
+    for (int i = 0; i < n_it; ++i) {
+      const int it = t_first + i, st = i & 1;
+      if (i + 1 < n_it) issue(it + 1, st ^ 1);
+      const uint8_t* sb = smem + st * Ld::kStage;
+      const bool lv = live(it);
+      u32x4 pw[2][2];
+      if (lv) {
+        const bool m = masked(it);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint8_t* q = sb + St::kQ;
+          f32x16 s = f32x16{};
+          vec8 a[2] = {blk.row_op(q, hh, 0), blk.row_op(q, hh, 1)};
+#pragma unroll
+          for (int kk = 0; kk < kKs; ++kk) {
+            s = E::mfma(a[kk & 1], blk.kf[kk], s);
+            if (kk + 2 < kKs) a[kk & 1] = blk.row_op(q, hh, kk + 2);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          float p[16];
+          blk.probs(s, sb, hh, it * kT + 32 * hh, m, p);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pw[hh][e >> 2][e & 3] = E::pack2(p[2 * e], p[2 * e + 1]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) *p_at(hh, j) = f32x4{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
+        }
+      }
+      lds_barrier();  // P handed to wave B
+      if (lv) {
+        const uint8_t* o = sb + St::kDO;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          vec8 bq[2] = {blk.tr_op(o, hh, 0, 0), blk.tr_op(o, hh, 0, 1 % kDB)};
+#pragma unroll
+          for (int i2 = 0; i2 < 2 * kDB; ++i2) {
+            const int tt = i2 / kDB, db = i2 % kDB;
+            blk.acc[db] = E::mfma(bq[i2 & 1], __builtin_bit_cast(vec8, pw[hh][tt]), blk.acc[db]);
+            if (i2 + 2 < 2 * kDB) bq[i2 & 1] = blk.tr_op(o, hh, (i2 + 2) / kDB, (i2 + 2) % kDB);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      wait_copies();
+      __syncthreads();
+    }
+    if (kw0 < N && blk.my_k < N) store_row<IsBf16, D>(dV + head_out, blk.my_k, out.sn, blk.g, blk.acc, 1.f);
+  } else {
+    load_resident<IsBf16, D>(blk.vf, V + head, N, blk.my_k, in.sn, blk.g, 0u);
+    for (int i = 0; i < n_it; ++i) {
+      const int it = t_first + i, st = i & 1;
+      if (i + 1 < n_it) issue(it + 1, st ^ 1);
+      const uint8_t* sb = smem + st * Ld::kStage;
+      const bool lv = live(it);
+      f32x16 dp[2];
+      if (lv) {
+        const uint8_t* o = sb + St::kDO;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          dp[hh] = f32x16{};
+          vec8 a[2] = {blk.row_opO(o, hh, 0), blk.row_opO(o, hh, 1)};
+#pragma unroll
+          for (int kk = 0; kk < kKs; ++kk) {
+            dp[hh] = E::mfma(a[kk & 1], blk.vf[kk], dp[hh]);
+            if (kk + 2 < kKs) a[kk & 1] = blk.row_opO(o, hh, kk + 2);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      lds_barrier();  // P from wave A
+      if (lv) {
+        const uint8_t* q = sb + St::kQ;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          float p[16];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 v4 = *p_at(hh, j);
+            p[4 * j] = v4[0], p[4 * j + 1] = v4[1], p[4 * j + 2] = v4[2], p[4 * j + 3] = v4[3];
+          }
+          u32x4 sw[2];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 2 * e;
+            const f32x2 dd = blk.pair_vals(sb, St::kD, hh, r);
+            sw[e >> 2][e & 3] = E::pack2(p[r] * (dp[hh][r] - dd[0]), p[r + 1] * (dp[hh][r + 1] - dd[1]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          vec8 bq[2] = {blk.tr_op(q, hh, 0, 0), blk.tr_op(q, hh, 0, 1 % kDB)};
+#pragma unroll
+          for (int i2 = 0; i2 < 2 * kDB; ++i2) {
+            const int tt = i2 / kDB, db = i2 % kDB;
+            blk.acc[db] = E::mfma(bq[i2 & 1], __builtin_bit_cast(vec8, sw[tt]), blk.acc[db]);
+            if (i2 + 2 < 2 * kDB) bq[i2 & 1] = blk.tr_op(q, hh, (i2 + 2) / kDB, (i2 + 2) % kDB);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      wait_copies();
+      __syncthreads();
+    }
+    if (kw0 < N && blk.my_k < N) store_row<IsBf16, D>(dK + head_out, blk.my_k, out.sn, blk.g, blk.acc, dk_mul);
+  }
+}
+
 // ---------------------------------------------------------------- D and dQ
 // Per wave: 32 resident queries (lane column = query).  Key tiles of 64 rows
 // (K, V) stream through two LDS stages, twice.  For each 32-key half:
@@ -705,6 +938,12 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dK = scale dS^T Q; a negative scale flips the resident K instead of Q
+  if constexpr (DV == D && D <= 128 && Mode != kModeSparse) {
+    hipLaunchKernelGGL((bwd_dkdv_pair<IsBf16, D, Causal, Mode>), dim3((unsigned)(nblk * BH)), dim3(kPThr), 0,
+                       st, q, k, v, dout, nlse, dsum, static_cast<uint16_t*>(a.dk),
+                       static_cast<uint16_t*>(a.dv), N, win, (int)a.H, BH, c, a.scale, q_sign, a.in, a.out);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((bwd_dkdv<IsBf16, D, Causal, Mode, DV>), dim3((unsigned)kgrid), dim3(kThr), 0, st,
                      q, k, v, dout, nlse, dsum, static_cast<uint16_t*>(a.dk),
                      static_cast<uint16_t*>(a.dv), N, win, (int)a.H, BH, c, a.scale, q_sign, a.in, a.out,
