@@ -156,6 +156,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
     const int64_t nb = (N + 63) / 64;
     if ((mask_b != 1 && mask_b != B) || (mask_h != 1 && mask_h != H)) return FA_ERR_SHAPE;
     if (nb > kMaxSparseTiles) return FA_ERR_UNSUPPORTED;
+    // the dK/dV grid: up to kBwdSparseSplit workgroups per 128-key block and head
+    if (((N + 127) / 128) * B * H > kMaxGrid / fa::kBwdSparseSplit) return FA_ERR_SHAPE;
     a.block_mask = block_mask;
     a.mask_sh = mask_h == 1 ? 0 : nb * nb;
     a.mask_sb = mask_b == 1 ? 0 : mask_h * nb * nb;

@@ -256,7 +256,7 @@ struct DkdvBlock {
 // workgroup, which writes fp32 partial dK^T and dV^T to the workspace; the
 // last of them to finish (a per-key-block counter, zeroed by the dQ kernel)
 // adds the partials in chunk order, so the result stays deterministic.
-constexpr int kSplit = 4, kChunk = 32;
+constexpr int kSplit = kBwdSparseSplit, kChunk = 32;
 struct SplitArgs {
   int* cnt;        // [B*H][key blocks of kRes], zeroed by bwd_dq each call
   float* part_dv;  // [kSplit][B*H][N][d_v]

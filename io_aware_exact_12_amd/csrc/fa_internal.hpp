@@ -66,6 +66,10 @@ struct BwdArgs {
   Layout outv;     // dv
 };
 
+// The block-sparse backward cuts a key block's list of query tiles into at
+// most this many chunks, each run by a dK/dV workgroup of its own.
+constexpr int kBwdSparseSplit = 4;
+
 // Launchers return the hipError_t of the launch (hipSuccess when enqueued).
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s);

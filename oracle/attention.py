@@ -141,6 +141,32 @@ def dense_probs(q, k, causal=False, scale=None, window=None, block_mask=None):
     return np.where(seen, e / np.where(seen, e.sum(axis=-1, keepdims=True), 1.0), 0.0)
 
 
+def _tile_summary(t, v_tile):
+    """Summary of one tile for each row: its largest score m_t, the sum
+    l_t = sum_j exp(t_j - m_t) and the d_v-wide a_t = sum_j exp(t_j - m_t) v_j.
+    A row whose scores in the tile are all -inf (masked) has m_t = -inf,
+    l_t = 0 and a_t = 0: the summary of no key."""
+    m_t = t.max(axis=1)
+    seen = np.isfinite(m_t)
+    e = np.where(seen[:, None], np.exp(t - np.where(seen, m_t, 0.0)[:, None]), 0.0)
+    return m_t, e.sum(axis=1), e @ v_tile
+
+
+def _merge(first, second):
+    """Combine the summaries of two disjoint key sets into the summary of
+    their union: both are moved to the larger maximum before they are added,
+    a summary of no key (m = -inf) weighing 0.  The operation is associative
+    and commutative, so the result does not depend on how the keys were
+    grouped into tiles or in what order the tiles came."""
+    m1, l1, a1 = first
+    m2, l2, a2 = second
+    m = np.maximum(m1, m2)
+    ref = np.where(np.isfinite(m), m, 0.0)
+    w1 = np.where(np.isfinite(m1), np.exp(m1 - ref), 0.0)
+    w2 = np.where(np.isfinite(m2), np.exp(m2 - ref), 0.0)
+    return m, w1 * l1 + w2 * l2, w1[:, None] * a1 + w2[:, None] * a2
+
+
 def online_fwd(q, k, v, causal=False, scale=None, query_block=2, key_block=2, trace=None,
                window=None):
     """Tiled forward with the online softmax, one head at a time.
@@ -148,30 +174,28 @@ def online_fwd(q, k, v, causal=False, scale=None, query_block=2, key_block=2, tr
     Loop order: query blocks outside, key/value blocks inside; each query block
     keeps its row state resident while every key tile passes ("Flash Attention:
     IO-Aware Exact Attention", section "Loop order changes which data is
-    reloaded").  Row state per query: running maximum ``m`` (starts at -inf),
-    denominator ``l`` (starts at 0) and the d_v-wide unnormalised numerator ``a``
-    (starts at 0).  For a tile of scores t and values V_tile the update is the
-    one of section "Online softmax makes tiling exact" of the same page (the
-    displayed formulas did not survive extraction; this is the reading that
-    the page's own NumPy check, the two-block worked example on Road to
-    Intelligence "FlashAttention", section "The trick that makes tiling
-    possible", and section 03 of "FlashAttention -- the same attention, made
-    memory-aware" all agree on):
+    reloaded").  The row state is a running maximum ``m``, a denominator ``l``
+    and a d_v-wide unnormalised numerator ``a`` (section "Online softmax makes
+    tiling exact" of the same page; its displayed formulas did not survive
+    extraction, and this is the reading that the page's own CPU check, the
+    two-block worked example on Road to Intelligence "FlashAttention", section
+    "The trick that makes tiling possible", and section 03 of "FlashAttention
+    -- the same attention, made memory-aware" agree on).
 
-        m' = max(m, max_j t_j)
-        alpha = exp(m - m')                 (alpha = 0 while no key was seen)
-        p_j = exp(t_j - m')
-        l' = alpha * l + sum_j p_j
-        a' = alpha * a + sum_j p_j V_tile[j]
-
-    and at the end O = a / l (one division, the FlashAttention-2 form of the
-    unnormalised accumulator), LSE = m + ln l.
+    Here the state is the merge (``_merge``) of the summaries (``_tile_summary``)
+    of the tiles seen so far: a row starts from the summary of no key
+    (m = -inf, l = 0, a = 0), and each tile's summary is merged into it.  The
+    merge moves both sides to the new maximum m' = max(m, m_t): the old state
+    is scaled by alpha = exp(m - m') (zero while no key was seen), the tile's
+    by exp(m_t - m'), which is the page's update l' = alpha l + sum_j p_j,
+    a' = alpha a + sum_j p_j V_tile[j] with p_j = exp(t_j - m').  At the end
+    O = a / l (one division, the unnormalised FlashAttention-2 form) and
+    LSE = m + ln l.
 
     Masked keys (causal j > i, or j <= i - window) have t_j = -inf and
-    contribute p_j = 0.  A tile in which every key of a row is masked leaves
-    that row's state unchanged.
-    Tail tiles are simply shorter (keys beyond N do not exist); tiles larger
-    than N are allowed.
+    contribute nothing; a row all of whose keys so far are masked keeps the
+    summary of no key.  Tail tiles are simply shorter (keys beyond N do not
+    exist); tiles larger than N are allowed.
 
     ``trace``, when a list, receives one dict per (query block, key tile) with
     copies of the state after that tile: keys ``row0``, ``col0``, ``m``, ``l``, ``a``.
@@ -194,9 +218,7 @@ def online_fwd(q, k, v, causal=False, scale=None, query_block=2, key_block=2, tr
         for row0 in range(0, n_q, query_block):
             rows = np.arange(row0, min(n_q, row0 + query_block))
             query = qf[h, rows]
-            m = np.full(len(rows), -np.inf)
-            ell = np.zeros(len(rows))
-            a = np.zeros((len(rows), dv))
+            state = (np.full(len(rows), -np.inf), np.zeros(len(rows)), np.zeros((len(rows), dv)))
             for col0 in range(0, n_k, key_block):
                 cols = np.arange(col0, min(n_k, col0 + key_block))
                 t = (query @ kf[h, cols].T) * scale
@@ -204,20 +226,12 @@ def online_fwd(q, k, v, causal=False, scale=None, query_block=2, key_block=2, tr
                     t = np.where(cols[None, :] <= rows[:, None], t, -np.inf)
                 if window is not None:
                     t = np.where(cols[None, :] > rows[:, None] - int(window), t, -np.inf)
-                m_new = np.maximum(m, t.max(axis=1))
-                seen = np.isfinite(m_new)          # rows with at least one visible key so far
-                m_safe = np.where(seen, m_new, 0.0)
-                alpha = np.where(np.isfinite(m), np.exp(m - m_safe), 0.0)
-                p = np.where(seen[:, None], np.exp(t - m_safe[:, None]), 0.0)
-                ell_new = alpha * ell + p.sum(axis=1)
-                a_new = alpha[:, None] * a + p @ vf[h, cols]
-                # a row whose keys were all masked so far keeps its initial state
-                m = np.where(seen, m_new, m)
-                ell = np.where(seen, ell_new, ell)
-                a = np.where(seen[:, None], a_new, a)
+                state = _merge(state, _tile_summary(t, vf[h, cols]))
                 if trace is not None:
+                    m, ell, a = state
                     trace.append({"head": h, "row0": row0, "col0": col0,
                                   "m": m.copy(), "l": ell.copy(), "a": a.copy()})
+            m, ell, a = state
             out[h, rows] = a / ell[:, None]
             lse[h, rows] = m + np.log(ell)
     return out.reshape(lead + (n_q, dv)), lse.reshape(lead + (n_q,))

@@ -456,3 +456,13 @@ def test_dv_calls_reject_huge_n_before_multiplying():
     assert fa.attn_bwd_dv_raw(16, 16, 16, 16, 16, 16, 16, 16, 16, 1, 1, huge, 128, 64, 0, 0.1,
                               fa.BF16, 16, 1 << 20, None) == FA_ERR_SHAPE
     assert L is not None
+
+
+def test_block_sparse_backward_grid_bound():
+    """The split block-sparse backward runs up to four dK/dV workgroups per
+    128-key block and head; a problem whose grid would pass 2^31 - 1 is a
+    shape error before any launch."""
+    st = fa.attn_bwd_block_sparse_raw(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0] + 0x100000,
+                                      1, 1 << 30, 16, 64, P[1] + 0x100000, 1, 1, 0, 0.1, fa.BF16,
+                                      P[2] + 0x100000, (1 << 63) - 1, None)
+    assert st == FA_ERR_SHAPE

@@ -345,6 +345,63 @@ def test_loop_order_ledger_causal_by_hand():
         oracle.loop_order_ledger(6, 2, 2, 2, 2, "diagonal")
 
 
+def test_tile_merge_is_order_free():
+    """The online state is a fold of per-tile summaries with a merge that is
+    associative and commutative: any grouping or order of the key tiles gives
+    the dense row statistics (m, l, a) of all keys, to rounding."""
+    from oracle.attention import _merge, _tile_summary
+    rng = np.random.default_rng(5)
+    t = rng.normal(0, 3, (4, 13))
+    t[1, :5] = -np.inf          # masked keys
+    t[2, :] = -np.inf           # a row with no visible key
+    vv = rng.normal(0, 1, (13, 3))
+    cuts = [(0, 3), (3, 4), (4, 9), (9, 13)]
+    parts = [_tile_summary(t[:, a:b], vv[a:b]) for a, b in cuts]
+    none = (np.full(4, -np.inf), np.zeros(4), np.zeros((4, 3)))
+    left = none
+    for p_ in parts:
+        left = _merge(left, p_)
+    right = _merge(_merge(parts[3], parts[1]), _merge(parts[2], _merge(parts[0], none)))
+    whole = _tile_summary(t, vv)
+    for got in (left, right):
+        np.testing.assert_array_equal(got[0], whole[0])
+        np.testing.assert_allclose(got[1], whole[1], rtol=1e-13, atol=0)
+        np.testing.assert_allclose(got[2], whole[2], rtol=1e-13, atol=1e-15)
+    assert np.isneginf(left[0][2]) and left[1][2] == 0 and not left[2][2].any()
+    # and the summary of all keys is the definition: l e^m = sum_j e^{t_j}
+    row = 0
+    np.testing.assert_allclose(whole[1][row] * np.exp(whole[0][row]), np.exp(t[row]).sum(), rtol=1e-13)
+
+
+def test_loop_order_ledger_ragged_by_hand():
+    """N = 5, d = 3, d_v = 2, two-row query blocks [0,2) [2,4) [4,5) and
+    three-key tiles [0,3) [3,5): none of the sizes divides another.  Counted by
+    hand from the loop nests of "Loop order changes which data is reloaded".
+
+    Unmasked, key/value outer: K and V read once (15, 10); each of the two
+    tiles reads all 5 query rows (2 x 15 = 30); the second tile reloads the
+    output rows and both statistics (10, 10); every visit writes them back
+    (2 x 10, 2 x 10).  Query outer: Q once (15), every block reads all keys
+    (3 x 15 = 45 K, 3 x 10 = 30 V), O and the LSE written once (10, 5).
+
+    Causal: block [0,2) sees tile [0,3) only; the others see both.  Key/value
+    outer: tile 0 visits all three blocks (Q 15, O write 10, statistics 10),
+    tile 1 the last two (Q 9, O read 6, statistics read 6, O write 6,
+    statistics write 6).  Query outer: K 9 + 15 + 15 = 39, V 6 + 10 + 10 = 26."""
+    kv = oracle.loop_order_ledger(5, 3, 2, 2, 3, "kv_outer")
+    assert kv == {"Q_read": 30, "K_read": 15, "V_read": 10, "O_read": 10, "O_write": 20,
+                  "stat_read": 10, "stat_write": 20, "total": 115}
+    qo = oracle.loop_order_ledger(5, 3, 2, 2, 3, "q_outer")
+    assert qo == {"Q_read": 15, "K_read": 45, "V_read": 30, "O_read": 0, "O_write": 10,
+                  "stat_read": 0, "stat_write": 5, "total": 105}
+    kvc = oracle.loop_order_ledger(5, 3, 2, 2, 3, "kv_outer", causal=True)
+    assert kvc == {"Q_read": 24, "K_read": 15, "V_read": 10, "O_read": 6, "O_write": 16,
+                   "stat_read": 6, "stat_write": 16, "total": 93}
+    qoc = oracle.loop_order_ledger(5, 3, 2, 2, 3, "q_outer", causal=True)
+    assert qoc == {"Q_read": 15, "K_read": 39, "V_read": 26, "O_read": 0, "O_write": 10,
+                   "stat_read": 0, "stat_write": 5, "total": 95}
+
+
 def _mutant_kv_outer(q, k, v, qb, kb, bug):
     """A copy of the key/value-outer merge with one deliberate mistake."""
     n, dv = q.shape[0], v.shape[1]
