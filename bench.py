@@ -50,6 +50,11 @@ COUNTER_PROFILE = os.path.join(ROOT, "profiles", "fwd_long_causal_bf16_counters.
 NOMINAL_SCLK_MHZ = 2400.0       # the clock the published peaks are quoted at
 
 
+def progress(msg):
+    """A progress line on stderr (stdout carries the one JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -498,6 +503,7 @@ def main():
 
     ms, warm = time_graph(step, args.steps, args.warmup, torch)
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    progress(f"forward {w.name}: {ms * 1e3:.1f} us per call")
 
     flops = w.fwd_flops()
     tflops = flops / (ms * 1e-3) / 1e12
@@ -543,20 +549,27 @@ def main():
     }
     if not args.no_bwd:
         record["attn_bwd"] = bwd_record(fa, workloads, torch, args.bwd_steps, args.bwd_warmup)
+        progress("backward done")
     if not args.no_window:
         record["attn_fwd_window"] = window_record(fa, workloads, torch, args.window_steps,
                                                   args.window_warmup)
+        progress("window forward done")
     if not args.no_sparse:
         record["attn_fwd_block_sparse"] = sparse_record(fa, workloads, torch, args.window_steps,
                                                         args.window_warmup)
+        progress("block-sparse forward done")
     if not args.no_variants:
         record["variants"] = variants_record(fa, workloads, torch, 50, 10)
+        progress("variants done")
         record["configs"] = configs_record(fa, workloads, torch, 50, 10)
+        progress("per-workload forwards done")
     if not args.no_kv_outer:
         record["attn_fwd_kv_outer"] = kv_outer_record(fa, workloads, torch, args.kv_steps,
                                                       args.kv_warmup)
+        progress("key/value-outer forward done")
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(w, x)
+        progress("cpu baseline done")
         record["cpu_baseline"]["gpu_over_cpu"] = round(record["value"] / record["cpu_baseline"]["value"], 1)
     print(json.dumps(record), flush=True)
 

@@ -27,7 +27,14 @@
 //                 operands in registers, dK^T and dV^T accumulated in
 //                 registers) and streams 64-query tiles of Q, dO, LSE and D
 //                 through LDS.  It runs after bwd_dq on the same stream.
-// Both main kernels use the 32x32x16 MFMA with the resident index in the lane
+// For d = d_v <= 128 under plain and sliding-window masks, each of the two
+// runs as a wave-pair kernel instead (bwd_dq_pair, bwd_dkdv_pair): the two
+// waves of a SIMD share 32 resident rows and split each streamed tile's
+// products between them, so S is formed once per (query, key) pair in each
+// kernel and every tile streams once.  bwd_dq_pair forms dQ in one pass from
+// D~ = rowsum(dO * O) and corrects it with the exact D at the end (the
+// identity is stated at the kernel).
+// All of them use the 32x32x16 MFMA with the resident index in the lane
 // column, so per-row (or per-key) scalars stay lane-local.  Tile rows are
 // stored in LDS in the permuted order that makes a 32-row block's MFMA output
 // hold 8 consecutive rows per lane half, so P and dS are reused as MFMA
@@ -906,6 +913,277 @@ __global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dq(
   store_row<IsBf16, D>(dQ + (b * out.sb + h * out.sh), my_q, out.sn, g, dq, dq_mul);
 }
 
+// ---------------------------------------------------------------- dQ (wave pairs, one pass)
+// Plain and sliding-window masks, d = d_v <= 128.  A workgroup of 8 waves
+// keeps 128 queries resident; waves w and w + 4 (one SIMD) share queries
+// qw0 .. qw0 + 31 and stream the 64-key tiles of K and V once:
+//   wave A (w < 4):  S^T = K Q^T, P^T = exp2(c S^T - LSE2), P (fp32) to LDS
+//   wave B (w >= 4): dP^T = V dO^T;  P from LDS;  D_i += sum_j P_ij dP_ij;
+//                    dQ~^T += K^T (P (dP - D~))^T,  B^T += K^T P^T
+// with D~_i = dO_i . O_i from the stored output and B_i = sum_j P_ij k_j.
+// Since
+//     dQ_i / scale = sum_j P_ij (dP_ij - D_i) k_j
+//                  = dQ~_i - (D_i - D~_i) B_i
+// (exact), one pass gives dQ with the exact row term D_i = sum_j P_ij dP_ij:
+// D~ only keeps the operand P (dP - D~) as small as P (dP - D) (O's rounding
+// moves D~ by about 2^-9 relative, and that difference reaches dQ through the
+// fp32 correction, not through a bf16 operand).  D is accumulated in the
+// order of the two-pass kernel, so the dK/dV kernel that reads it is
+// unchanged bit for bit.
+//
+// Wave B's two K^T products share each transpose read of K, so a 32 x 64
+// block costs 48 KB of LDS operand and P traffic against 64 MFMAs.  Wave A
+// runs one key tile ahead of wave B: in step i it forms P of tile i while B
+// consumes P of tile i - 1, which the barrier ending step i - 1 handed over.
+// K tiles sit in a ring of three LDS slots (A reads tile i, B tile i - 1,
+// tile i + 1 is in flight), V tiles and P sets in rings of two.
+template <int D> struct DqPairLds {
+  static constexpr int kTile = STile<D>::kBytes;     // one 64-row tile of K or V
+  static constexpr int kK = 0;                       // K ring: tile t in slot t % 3
+  static constexpr int kV = 3 * kTile;               // V ring: slot t % 2
+  static constexpr int kP = kV + 2 * kTile;          // P ring: set t % 2 of [pair][key half]
+  static constexpr int kPHalf = 64 * 16 * 4;         // 4 KB: 16 fp32 a lane
+  static constexpr int kPSet = 4 * 2 * kPHalf;
+  static constexpr int kBytes = kP + 2 * kPSet;
+  static_assert(kBytes <= 160 * 1024, "fits the LDS of a CU");
+};
+
+template <bool IsBf16, int D, bool Causal, int Mode>
+__global__ __launch_bounds__(kPThr, 1) void bwd_dq_pair(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ Dsum, float* __restrict__ NLse, uint16_t* __restrict__ dQ, int N, int win, int H,
+    int BH, int n_qblocks, float c, float dq_mul, uint32_t q_sign, Layout in, Layout out) {
+  using E = Elt<IsBf16>;
+  using vec8 = typename E::vec8;
+  using Ld = DqPairLds<D>;
+  using PC = PairCopy<D>;
+  using T = STile<D>;
+  typedef __attribute__((address_space(3))) const vec8 lds_vec8;
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  static_assert(Mode == kModePlain || Mode == kModeWindow, "plain and window masks");
+  constexpr bool kWin = Causal && Mode == kModeWindow;
+  constexpr int kKs = D / 16, kDB = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Ld::kBytes];
+
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair = wave & 3;
+  const bool role_a = wave < 4;
+  const int bh = blockIdx.x % BH;
+  int qb = blockIdx.x / BH;
+  if (Causal) qb = n_qblocks - 1 - qb;  // heaviest first
+  const int b = bh / H, h = bh - b * H;
+  const int64_t head = b * in.sb + h * in.sh;
+  const int q0 = qb * kRes, qw0 = q0 + 32 * pair, my_q = qw0 + l32;
+  const bool q_ok = my_q < N;
+  const float lse2 = q_ok ? LSE[(int64_t)bh * N + my_q] * 1.4426950408889634f : INFINITY;
+
+  const int last_row = min(N, q0 + kRes) - 1;
+  const int n_tiles = Causal ? last_row / kT + 1 : (N + kT - 1) / kT;
+  const int t_lo = kWin ? max(0, q0 - win + 1) / kT : 0;
+  const int n_it = n_tiles - t_lo;
+  const bool pair_live = qw0 < N;
+  const uint16_t* k_h = K + head;
+  const uint16_t* v_h = V + head;
+  uint32_t src[PC::kPerWave];
+  PC::sources(wave, lane, (uint32_t)(2 * in.sn), src);
+  const uint32_t lds0 = lds_u32(smem);
+  auto issue_k = [&](int i) {
+    PC::copy(lds0 + (uint32_t)(Ld::kK + (i % 3) * Ld::kTile), k_h, N, (t_lo + i) * kT, in.sn, wave, src);
+  };
+  auto issue_v = [&](int i) {
+    PC::copy(lds0 + (uint32_t)(Ld::kV + (i & 1) * Ld::kTile), v_h, N, (t_lo + i) * kT, in.sn, wave, src);
+  };
+  // whether key half ks0 .. ks0 + 31 lies wholly outside what this pair's
+  // queries see, and whether it can hide some key from some of them
+  auto skip_half = [&](int ks0) {
+    return !pair_live || (Causal && ks0 > qw0 + 31) || (kWin && ks0 + 31 <= qw0 - win) || ks0 >= N;
+  };
+  auto needs_mask = [&](int ks0) {
+    return (Causal && ks0 + 31 > qw0) || (kWin && ks0 <= qw0 + 31 - win) || ks0 + 32 > N;
+  };
+  // LDS addresses are kept per lane and per slot in registers (advanced by a
+  // scalar from one step to the next, and hidden from the compiler by an
+  // empty asm), so that a key half, k step or P chunk only adds a constant in
+  // the instruction's offset field.  Otherwise the compiler keeps every
+  // (lane offset + constant) sum of the loop live, which does not fit.
+  auto hide = [](uint32_t& a) { asm("" : "+v"(a)); };
+  auto row_at = [](uint32_t a) { return *(lds_vec8*)(uintptr_t)a; };
+  auto tr_at = [](uint32_t lo, uint32_t hi) {
+    const auto l = E::read_tr((const lds_void*)(uintptr_t)lo);
+    const auto u = E::read_tr((const lds_void*)(uintptr_t)hi);
+    return __builtin_shufflevector(l, u, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // k slot step from tile i to tile i + 1 in the ring of three
+  auto k_step = [](int i) { return (uint32_t)(i % 3 == 2 ? -2 * Ld::kTile : Ld::kTile); };
+  // P of (set, this pair, key half kh): chunk j of lane l at 16 (64 j + l)
+  uint32_t pb = lds0 + (uint32_t)(Ld::kP + pair * 2 * Ld::kPHalf + 16 * lane);  // set 0
+  auto p_step = [](int i) { return (uint32_t)(i & 1 ? -Ld::kPSet : Ld::kPSet); };
+  // the row operand of k step kk: LDS row l32 (+ 32 in the second key half), chunk 2 kk + g
+  auto row_off = [&](int kk) { return (uint32_t)T::at(l32, 2 * kk + g); };
+
+  issue_k(0);
+  wait_copies();
+  __syncthreads();
+  if (role_a) {
+    vec8 qf[kKs];
+    load_resident<IsBf16, D>(qf, Q + head, N, my_q, in.sn, g, q_sign);
+    uint32_t kb[kKs];  // K rows, slot of tile i
+#pragma unroll
+    for (int kk = 0; kk < kKs; ++kk) kb[kk] = lds0 + (uint32_t)Ld::kK + row_off(kk);
+    // step i: P of tile i (step n_it only meets the barrier)
+    for (int i = 0; i <= n_it; ++i) {
+      if (i + 1 < n_it) issue_k(i + 1);
+      if (i < n_it) issue_v(i);
+      if (i < n_it) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const int ks0 = (t_lo + i) * kT + 32 * kh;
+          if (skip_half(ks0)) continue;
+          constexpr uint32_t kHalfRows = 32 * T::kRowBytes;
+          f32x16 s = f32x16{};
+          // operand reads run two MFMAs ahead; the fences keep the compiler
+          // from hoisting all of them into registers
+          vec8 a[2] = {row_at(kb[0] + kh * kHalfRows), row_at(kb[1] + kh * kHalfRows)};
+#pragma unroll
+          for (int kk = 0; kk < kKs; ++kk) {
+            s = E::mfma(a[kk & 1], qf[kk], s);
+            if (kk + 2 < kKs) a[kk & 1] = row_at(kb[kk + 2] + kh * kHalfRows);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          float p[16];
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) p[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c, -lse2));
+          if (needs_mask(ks0)) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+              const int kj = ks0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
+              if (kj >= N || (Causal && kj > my_q) || (kWin && kj <= my_q - win)) p[rr] = 0.f;
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *(lds_f32x4*)(uintptr_t)(pb + kh * Ld::kPHalf + 1024 * j) =
+                f32x4{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
+        }
+      }
+      const uint32_t ks = k_step(i), ps = p_step(i);
+#pragma unroll
+      for (int kk = 0; kk < kKs; ++kk) kb[kk] += ks, hide(kb[kk]);
+      pb += ps;
+      hide(pb);
+      wait_copies();
+      __syncthreads();
+    }
+  } else {
+    vec8 of[kKs];
+    load_resident<IsBf16, D>(of, dO + head, N, my_q, in.sn, g, 0u);
+    // D~ = dO . O of this lane's query (its d range, then the other half's)
+    float dt = 0.f;
+    {
+      vec8 oo[kKs];
+      load_resident<IsBf16, D>(oo, O + head, N, my_q, in.sn, g, 0u);
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dt = __builtin_fmaf((float)of[ks][e], (float)oo[ks][e], dt);
+    }
+    const float dtil = xhalf_sum(dt);
+    uint32_t vb[kKs], kt_lo[kDB], kt_hi[kDB];  // V rows and K^T reads, slots of tile i - 1
+#pragma unroll
+    for (int kk = 0; kk < kKs; ++kk) vb[kk] = lds0 + (uint32_t)Ld::kV + row_off(kk);
+    {
+      // transpose reads of d block db: logical rows 4 g + s / 4 and 8 more
+      // (s = lane % 16), k step t adding 16 rows
+      const int grp = lane >> 4, s16 = lane & 15, r0 = 4 * g + (s16 >> 2);
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const int col = 2 * (16 * (grp & 1) + 4 * (s16 & 3)) + 64 * db;
+        kt_lo[db] = lds0 + (uint32_t)(Ld::kK + T::at(r0, col >> 4) + (col & 15));
+        kt_hi[db] = lds0 + (uint32_t)(Ld::kK + T::at(r0 + 8, col >> 4) + (col & 15));
+      }
+    }
+    f32x16 dq[kDB], bacc[kDB];
+#pragma unroll
+    for (int i = 0; i < kDB; ++i) dq[i] = f32x16{}, bacc[i] = f32x16{};
+    float dpart = 0.f;
+    // step i: the products of tile i - 1 (step 0 only meets the barrier)
+    for (int i = 0; i <= n_it; ++i) {
+      if (i + 1 < n_it) issue_k(i + 1);
+      if (i < n_it) issue_v(i);
+      if (i > 0) {
+        const int it = i - 1;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const int ks0 = (t_lo + it) * kT + 32 * kh;
+          if (skip_half(ks0)) continue;
+          constexpr uint32_t kHalfRows = 32 * T::kRowBytes, kStepRows = 16 * T::kRowBytes;
+          f32x16 dp = f32x16{};
+          vec8 a[2] = {row_at(vb[0] + kh * kHalfRows), row_at(vb[1] + kh * kHalfRows)};
+#pragma unroll
+          for (int kk = 0; kk < kKs; ++kk) {
+            dp = E::mfma(a[kk & 1], of[kk], dp);
+            if (kk + 2 < kKs) a[kk & 1] = row_at(vb[kk + 2] + kh * kHalfRows);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          float p[16];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 v4 = *(lds_f32x4*)(uintptr_t)(pb + kh * Ld::kPHalf + 1024 * j);
+            p[4 * j] = v4[0], p[4 * j + 1] = v4[1], p[4 * j + 2] = v4[2], p[4 * j + 3] = v4[3];
+          }
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) dpart = __builtin_fmaf(p[rr], dp[rr], dpart);
+          u32x4 sw[2], pw[2];
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) {
+            sw[e >> 3][(e & 7) >> 1] = E::pack2(p[e] * (dp[e] - dtil), p[e + 1] * (dp[e + 1] - dtil));
+            pw[e >> 3][(e & 7) >> 1] = E::pack2(p[e], p[e + 1]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // K^T operand i2 = (d block i2 / 2, k step 2 kh + i2 % 2) feeds dQ~ and B
+          auto kt_op = [&](int t, int db) {
+            const uint32_t o = (2 * kh + t) * kStepRows;
+            return tr_at(kt_lo[db] + o, kt_hi[db] + o);
+          };
+          vec8 kt[2] = {kt_op(0, 0), kt_op(1, 0)};
+#pragma unroll
+          for (int i2 = 0; i2 < 2 * kDB; ++i2) {
+            const int db = i2 >> 1, t = i2 & 1;
+            dq[db] = E::mfma(kt[t], __builtin_bit_cast(vec8, sw[t]), dq[db]);
+            bacc[db] = E::mfma(kt[t], __builtin_bit_cast(vec8, pw[t]), bacc[db]);
+            if (i2 + 2 < 2 * kDB) kt[t] = kt_op(t, db + 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // slots of tile i
+        const uint32_t ks = k_step(it), vs = (uint32_t)(it & 1 ? -Ld::kTile : Ld::kTile);
+#pragma unroll
+        for (int kk = 0; kk < kKs; ++kk) vb[kk] += vs, hide(vb[kk]);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) kt_lo[db] += ks, kt_hi[db] += ks, hide(kt_lo[db]), hide(kt_hi[db]);
+        pb += p_step(it);
+        hide(pb);
+      }
+      wait_copies();
+      __syncthreads();
+    }
+    const float dsum = xhalf_sum(dpart);
+    if (!pair_live || !q_ok) return;
+    if (g == 0) {
+      Dsum[(int64_t)bh * N + my_q] = dsum;
+      NLse[(int64_t)bh * N + my_q] = -lse2;  // read by the dK/dV kernel
+    }
+    const float delta = dsum - dtil;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[db][r] = __builtin_fmaf(-delta, bacc[db][r], dq[db][r]);
+    store_row<IsBf16, D>(dQ + (b * out.sb + h * out.sh), my_q, out.sn, g, dq, dq_mul);
+  }
+}
+
 template <bool IsBf16, int D, bool Causal, int Mode, int DV = D>
 hipError_t launch(const BwdArgs& a, hipStream_t st) {
   const int N = (int)a.N;
@@ -932,9 +1210,17 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
   }
   const int kgrid = Mode == kModeSparse ? nblk * BH * kSplit : nblk * BH;
   // dQ (and D into the workspace) first; dK, dV read D afterwards on the same stream
-  hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal, Mode, DV>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st, q,
-                     k, v, dout, a.lse, dsum, nlse, static_cast<uint16_t*>(a.dq), N, win, (int)a.H, BH,
-                     nblk, c, a.scale, q_sign, a.in, a.out, a.lv, a.block_mask, a.mask_sb, a.mask_sh, split);
+  if constexpr (DV == D && D <= 128 && Mode != kModeSparse) {
+    hipLaunchKernelGGL((bwd_dq_pair<IsBf16, D, Causal, Mode>), dim3((unsigned)(nblk * BH)), dim3(kPThr), 0, st,
+                       q, k, v, static_cast<const uint16_t*>(a.o), dout, a.lse, dsum, nlse,
+                       static_cast<uint16_t*>(a.dq), N, win, (int)a.H, BH, nblk, c, a.scale, q_sign, a.in,
+                       a.out);
+  } else {
+    hipLaunchKernelGGL((bwd_dq<IsBf16, D, Causal, Mode, DV>), dim3((unsigned)(nblk * BH)), dim3(kThr), 0, st,
+                       q, k, v, dout, a.lse, dsum, nlse, static_cast<uint16_t*>(a.dq), N, win, (int)a.H,
+                       BH, nblk, c, a.scale, q_sign, a.in, a.out, a.lv, a.block_mask, a.mask_sb, a.mask_sh,
+                       split);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dK = scale dS^T Q; a negative scale flips the resident K instead of Q
