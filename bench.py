@@ -196,7 +196,7 @@ def bwd_record(fa, workloads, torch, steps, warmup):
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                         "kernels": "bwd_dq + bwd_dkdv (one call)",
+                         "kernels": "bwd_dq_pair + bwd_dkdv_pair (one call)",
                          "algorithmic_flops_per_launch": flops}}
 
 
