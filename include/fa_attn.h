@@ -247,7 +247,7 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
  * k are [B][H][N][d]: the pages define V as N x d_v ("Flash Attention:
  * IO-Aware Exact Attention", section "Why intermediate matrices cost memory
  * traffic"), and the scores only need q and k to share d.  Supported
- * (d, dv): (128, 64), (64, 128), and dv == d (the attn_fwd kernels);
+ * (d, dv): d and dv in {64, 96, 128} (dv == d runs the attn_fwd kernels);
  * FA_ERR_UNSUPPORTED for other pairs, FA_ERR_SHAPE for dv < 1.
  */
 int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -263,7 +263,7 @@ int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse
  * recomputed S = q k^T, dq = scale dS k and dk = scale dS^T q stay over d
  * (V is N x d_v in "Flash Attention: IO-Aware Exact Attention", section "Why
  * intermediate matrices cost memory traffic").  Supported
- * (d, d_v): (128, 64), (64, 128), and d_v == d (the attn_bwd kernels);
+ * (d, d_v): d and d_v in {64, 96, 128} (d_v == d runs the attn_bwd kernels);
  * FA_ERR_UNSUPPORTED for other pairs and for FA_F32, FA_ERR_SHAPE for
  * d_v < 1.  The workspace is as for attn_bwd (attn_bwd_workspace_bytes).
  */

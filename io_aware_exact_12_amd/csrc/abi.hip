@@ -87,7 +87,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
                 fa::dense_layout(H, N, d), fa::dense_layout(H, N, d), fa::dense_layout(H, N, d)};
   a.dv = d;
   if (dv != 0 && dv != d) {  // v and o rows of dv elements, dense
-    if (!((d == 128 && dv == 64) || (d == 64 && dv == 128))) return FA_ERR_UNSUPPORTED;
+    if (!fa::dv_pair_built(d, dv)) return FA_ERR_UNSUPPORTED;
     a.dv = dv;
     a.out = fa::dense_layout(H, N, dv);
   }
@@ -168,7 +168,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   // d = 256: d_v = d
   if (d == 256 && dvw != 0 && dvw != d) return FA_ERR_UNSUPPORTED;
   if (dvw != 0 && dvw != d) {  // v, o, dout and dv rows of dvw elements, dense
-    if (!((d == 128 && dvw == 64) || (d == 64 && dvw == 128))) return FA_ERR_UNSUPPORTED;
+    if (!fa::dv_pair_built(d, dvw)) return FA_ERR_UNSUPPORTED;
     a.dvw = dvw;
     a.lv = a.outv = fa::dense_layout(H, N, dvw);
   }

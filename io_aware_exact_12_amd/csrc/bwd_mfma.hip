@@ -1248,13 +1248,20 @@ hipError_t dispatch_d(const BwdArgs& a, hipStream_t s) {
   return launch<IsBf16, D, true, kModePlain>(a, s);
 }
 
+template <bool IsBf16, int D, int DV>
+hipError_t launch_dv(const BwdArgs& a, hipStream_t s) {
+  return a.causal ? launch<IsBf16, D, true, kModePlain, DV>(a, s) : launch<IsBf16, D, false, kModePlain, DV>(a, s);
+}
+
 template <bool IsBf16>
 hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
-  // d_v != d (plain masks only): q, k, dq, dk rows of d, v, o, dout, dv rows of d_v
-  if (a.dvw == 64 && a.d == 128)
-    return a.causal ? launch<IsBf16, 128, true, kModePlain, 64>(a, s) : launch<IsBf16, 128, false, kModePlain, 64>(a, s);
-  if (a.dvw == 128 && a.d == 64)
-    return a.causal ? launch<IsBf16, 64, true, kModePlain, 128>(a, s) : launch<IsBf16, 64, false, kModePlain, 128>(a, s);
+  // d_v != d (plain masks only): q, k, dq, dk rows of d, v, o, dout, dv rows
+  // of d_v; d, d_v in {64, 96, 128}
+  if (a.dvw != a.d) {
+    if (a.d == 128) return a.dvw == 64 ? launch_dv<IsBf16, 128, 64>(a, s) : launch_dv<IsBf16, 128, 96>(a, s);
+    if (a.d == 96) return a.dvw == 64 ? launch_dv<IsBf16, 96, 64>(a, s) : launch_dv<IsBf16, 96, 128>(a, s);
+    return a.dvw == 96 ? launch_dv<IsBf16, 64, 96>(a, s) : launch_dv<IsBf16, 64, 128>(a, s);
+  }
   if (a.d == 256) {  // plain masks, the sliding window and block masks
     if (a.block_mask != nullptr)
       return a.causal ? launch<IsBf16, 256, true, kModeSparse>(a, s) : launch<IsBf16, 256, false, kModeSparse>(a, s);

@@ -70,6 +70,13 @@ struct BwdArgs {
 // most this many chunks, each run by a dK/dV workgroup of its own.
 constexpr int kBwdSparseSplit = 4;
 
+// Widths of v (and o, dout, dv) rows other than d that the MFMA and fp32
+// kernels are built for: d and d_v in {64, 96, 128}, d_v != d.
+inline bool dv_pair_built(int64_t d, int64_t dv) {
+  const bool d_ok = d == 64 || d == 96 || d == 128, dv_ok = dv == 64 || dv == 96 || dv == 128;
+  return d_ok && dv_ok && d != dv;
+}
+
 // Launchers return the hipError_t of the launch (hipSuccess when enqueued).
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s);

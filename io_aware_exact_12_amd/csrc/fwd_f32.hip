@@ -196,8 +196,17 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
-  if (a.dv == 64 && a.d == 128) return a.causal ? launch<128, true, 64>(a, s) : launch<128, false, 64>(a, s);
-  if (a.dv == 128 && a.d == 64) return a.causal ? launch<64, true, 128>(a, s) : launch<64, false, 128>(a, s);
+  // d_v != d: d, d_v in {64, 96, 128}
+  if (a.dv != a.d) {
+    if (a.d == 128)
+      return a.dv == 64 ? (a.causal ? launch<128, true, 64>(a, s) : launch<128, false, 64>(a, s))
+                        : (a.causal ? launch<128, true, 96>(a, s) : launch<128, false, 96>(a, s));
+    if (a.d == 96)
+      return a.dv == 64 ? (a.causal ? launch<96, true, 64>(a, s) : launch<96, false, 64>(a, s))
+                        : (a.causal ? launch<96, true, 128>(a, s) : launch<96, false, 128>(a, s));
+    return a.dv == 96 ? (a.causal ? launch<64, true, 96>(a, s) : launch<64, false, 96>(a, s))
+                      : (a.causal ? launch<64, true, 128>(a, s) : launch<64, false, 128>(a, s));
+  }
   if (a.d == 128) return a.causal ? launch<128, true>(a, s) : launch<128, false>(a, s);
   if (a.d == 96) return a.causal ? launch<96, true>(a, s) : launch<96, false>(a, s);
   return a.causal ? launch<64, true>(a, s) : launch<64, false>(a, s);

@@ -394,7 +394,9 @@ struct FwdBlock {
   template <int kSlots>
   static constexpr int slot_of(int e, int st) {
     return kSlots == 16 ? e + (st == 0 ? 0 : st == 1 ? 2 : 5)
+         : kSlots == 14 ? (7 * e) / 8 + (st == 0 ? 0 : st == 1 ? 2 : 5)
          : kSlots == 12 ? (3 * e) / 4 + (st == 0 ? 0 : st == 1 ? 2 : 4)
+         : kSlots == 10 ? (5 * e) / 8 + (st == 0 ? 0 : st == 1 ? 2 : 4)
          : (kSlots == 8 || kSlots == 6) ? e / 2 + st
                         : (e / 4 + st < 3 ? e / 4 + st : 3);
   }
@@ -421,8 +423,9 @@ struct FwdBlock {
   template <int kMask, bool kFirst = false, int kHalf = 0>
   __device__ __forceinline__ void block(int u) {
     constexpr int kMfmas = (kFirst ? 0 : kPV) + kKs;
-    static_assert(kMfmas == 16 || kMfmas == 12 || kMfmas == 8 || kMfmas == 6 || kMfmas == 4,
-                  "slot schedules exist for 4, 6, 8, 12 and 16 MFMAs");
+    static_assert(kMfmas == 16 || kMfmas == 14 || kMfmas == 12 || kMfmas == 10 || kMfmas == 8 ||
+                      kMfmas == 6 || kMfmas == 4,
+                  "slot schedules exist for 4, 6, 8, 10, 12, 14 and 16 MFMAs");
     auto slot = [](int e, int st) { return slot_of<kMfmas>(e, st); };
     // K operand of block u+1: K tile (u+1)/2, half (u+1)&1
     const uint8_t* kt = k_stage(((u + 1) >> 1) & 3) + k_base + ((u + 1) & 1) * 32 * L::kKStride;
@@ -741,13 +744,19 @@ hipError_t dispatch_d(const FwdArgs& a, hipStream_t s) {
   return launch<IsBf16, D, true, kModePlain>(a, s);
 }
 
+template <bool IsBf16, int D, int DV>
+hipError_t launch_dv(const FwdArgs& a, hipStream_t s) {
+  return a.causal ? launch<IsBf16, D, true, kModePlain, DV>(a, s) : launch<IsBf16, D, false, kModePlain, DV>(a, s);
+}
+
 template <bool IsBf16>
 hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
-  // d_v != d (plain masks only): q, k rows of d, v, o rows of d_v
-  if (a.dv == 64 && a.d == 128)
-    return a.causal ? launch<IsBf16, 128, true, kModePlain, 64>(a, s) : launch<IsBf16, 128, false, kModePlain, 64>(a, s);
-  if (a.dv == 128 && a.d == 64)
-    return a.causal ? launch<IsBf16, 64, true, kModePlain, 128>(a, s) : launch<IsBf16, 64, false, kModePlain, 128>(a, s);
+  // d_v != d (plain masks only): q, k rows of d, v, o rows of d_v; d, d_v in {64, 96, 128}
+  if (a.dv != a.d) {
+    if (a.d == 128) return a.dv == 64 ? launch_dv<IsBf16, 128, 64>(a, s) : launch_dv<IsBf16, 128, 96>(a, s);
+    if (a.d == 96) return a.dv == 64 ? launch_dv<IsBf16, 96, 64>(a, s) : launch_dv<IsBf16, 96, 128>(a, s);
+    return a.dv == 96 ? launch_dv<IsBf16, 64, 96>(a, s) : launch_dv<IsBf16, 64, 128>(a, s);
+  }
   if (a.d == 128) return dispatch_d<IsBf16, 128>(a, s);
   return a.d == 96 ? dispatch_d<IsBf16, 96>(a, s) : dispatch_d<IsBf16, 64>(a, s);
 }

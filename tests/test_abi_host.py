@@ -333,9 +333,9 @@ def test_dv_validation():
         return fa.attn_fwd_dv_raw(q, P[1], P[2], P[3], P[4], a["B"], a["H"], a["N"], d, dv, a["mask"],
                                   a["scale"], a["dtype"], None)
     assert fdv(128, 0) == FA_ERR_SHAPE
-    for d, dv in ((128, 96), (96, 64), (64, 96), (128, 32), (64, 256)):
+    for d, dv in ((128, 32), (64, 256), (256, 128), (128, 256), (80, 64), (64, 80)):
         assert fdv(d, dv) == FA_ERR_UNSUPPORTED, (d, dv)
-    for d, dv in ((128, 64), (64, 128), (128, 128), (96, 96)):
+    for d, dv in ((128, 64), (64, 128), (128, 96), (96, 128), (96, 64), (64, 96), (128, 128), (96, 96)):
         assert fdv(d, dv, q=P[0] + 2) == FA_ERR_ALIGN, (d, dv)  # accepted: reaches the pointer checks
     assert fdv(128, 64, q=None) == FA_ERR_NULL
     assert fdv(64, 128, N=(1 << 23)) == FA_ERR_SHAPE           # v rows of a head span 2 GiB
@@ -348,11 +348,11 @@ def test_bwd_dv_validation():
         return fa.attn_bwd_dv_raw(q, P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], a["B"], a["H"],
                                   a["N"], d, dv, a["mask"], a["scale"], a["dtype"], P[1], a["ws"], None)
     assert bdv(128, 0) == FA_ERR_SHAPE
-    for d, dv in ((128, 96), (96, 64), (64, 96), (128, 32), (64, 256)):
+    for d, dv in ((128, 32), (64, 256), (256, 128), (128, 256), (80, 64), (64, 80)):
         assert bdv(d, dv) == FA_ERR_UNSUPPORTED, (d, dv)
     assert bdv(128, 64, dtype=fa.F32) == FA_ERR_UNSUPPORTED
     assert bdv(128, 64, ws=8) == FA_ERR_WORKSPACE
-    for d, dv in ((128, 64), (64, 128), (128, 128), (96, 96)):
+    for d, dv in ((128, 64), (64, 128), (128, 96), (96, 128), (96, 64), (64, 96), (128, 128), (96, 96)):
         assert bdv(d, dv, q=P[0] + 2) == FA_ERR_ALIGN, (d, dv)  # accepted: reaches the pointer checks
     assert bdv(128, 64, q=None) == FA_ERR_NULL
     assert bdv(64, 128, N=(1 << 23), ws=1 << 40) == FA_ERR_SHAPE  # v rows of a head span 2 GiB

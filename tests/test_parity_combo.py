@@ -70,7 +70,7 @@ def draw_case(rng, backward):
     dtypes = ("bf16", "fp16") if backward else ("bf16", "fp16", "fp32")
     c = {"kind": KINDS[rng.integers(len(KINDS))], "dtype": dtypes[rng.integers(len(dtypes))]}
     if c["kind"] == "dv":
-        c["d"], c["dv"] = ((128, 64), (64, 128))[rng.integers(2)]
+        c["d"], c["dv"] = ((128, 64), (64, 128), (128, 96), (96, 128), (96, 64), (64, 96))[rng.integers(6)]
     else:
         ds = (64, 96, 128) if c["dtype"] == "fp32" else (64, 96, 128, 256)
         c["d"] = c["dv"] = int(ds[rng.integers(len(ds))])

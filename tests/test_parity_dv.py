@@ -1,7 +1,7 @@
 """GPU parity with values of another width (attn_fwd_dv, attn_bwd_dv).
 
-q and k are [B, H, N, d], v, o and dout [B, H, N, dv] with (d, dv) in
-{(128, 64), (64, 128)}.  The HIP results are compared element by element with
+q and k are [B, H, N, d], v, o and dout [B, H, N, dv] with d and dv in
+{64, 96, 128}, d != dv (all six pairs).  The HIP results are compared element by element with
 the float64 oracle (``oracle.dense_fwd`` and ``oracle.dense_bwd``, which take v
 of any width) on the same dtype-rounded inputs: O, dQ, dK, dV within
 2e-2 + 1e-2 |ref| (fp16/bf16) or 1e-5 (fp32), the fp32 LSE within
@@ -21,6 +21,7 @@ pytestmark = pytest.mark.gpu
 
 TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
 TOL = {"fp32": (1e-5, 0.0), "fp16": (2e-2, 1e-2), "bf16": (2e-2, 1e-2), "lse": (1e-4, 1e-5)}
+PAIRS = [(128, 64), (64, 128), (128, 96), (96, 128), (96, 64), (64, 96)]
 
 
 @pytest.fixture(scope="module")
@@ -48,7 +49,7 @@ def compare(name, got, ref, tol):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("d,dv", [(128, 64), (64, 128)])
+@pytest.mark.parametrize("d,dv", PAIRS)
 @pytest.mark.parametrize("causal", [False, True])
 def test_dv_forward_sweep(fa, dtype, d, dv, causal):
     for i, n in enumerate([1, 31, 65, 257, 300, 777]):
@@ -83,7 +84,7 @@ def test_dv_long_head_all_rows(fa):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("d,dv", [(128, 64), (64, 128)])
+@pytest.mark.parametrize("d,dv", PAIRS)
 @pytest.mark.parametrize("causal", [False, True])
 def test_dv_backward_sweep(fa, dtype, d, dv, causal):
     for i, n in enumerate([1, 31, 65, 257, 300, 777]):
@@ -104,9 +105,9 @@ def test_dv_backward_sweep(fa, dtype, d, dv, causal):
 
 
 def test_dv_backward_long_head(fa):
-    """A longer head (B=1, H=2, N=2113, causal, bf16) for both pairs."""
+    """A longer head (B=1, H=2, N=2113, causal, bf16) for every pair."""
     n = 2113
-    for d, dv in ((128, 64), (64, 128)):
+    for d, dv in PAIRS:
         xq = workloads.random_inputs(1, 2, n, d, "bf16", 9993 + d)
         xv = workloads.random_inputs(1, 2, n, dv, "bf16", 9994 + dv, with_do=True)
         dev = lambda x: torch.from_numpy(x).to("cuda").to(torch.bfloat16).contiguous()
