@@ -84,10 +84,10 @@ enum fa_status {
  *   d        head dimension of q, k and v: 64, 96, 128 or 256.  d = 256
  *            takes FA_F16 or FA_BF16 (FA_ERR_UNSUPPORTED for FA_F32) and
  *            runs a kernel of its own: one workgroup per CU that keeps the
- *            256-wide accumulators of 128 queries in registers.  The calls
- *            below that add d_v != d or the key/value-outer order return
- *            FA_ERR_UNSUPPORTED for d = 256; attn_bwd, attn_bwd_strided, the
- *            sliding-window and the block-sparse calls take it.
+ *            256-wide accumulators of 128 queries in registers.  The
+ *            key/value-outer call returns FA_ERR_UNSUPPORTED for d = 256;
+ *            attn_bwd, attn_bwd_strided, the sliding-window, the
+ *            block-sparse and the d_v != d calls take it.
  *   mask     enum fa_mask.
  *   scale    finite multiplier of the raw dot products (any sign; usually
  *            1/sqrt(d)).
@@ -247,8 +247,10 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
  * k are [B][H][N][d]: the pages define V as N x d_v ("Flash Attention:
  * IO-Aware Exact Attention", section "Why intermediate matrices cost memory
  * traffic"), and the scores only need q and k to share d.  Supported
- * (d, dv): d and dv in {64, 96, 128} (dv == d runs the attn_fwd kernels);
- * FA_ERR_UNSUPPORTED for other pairs, FA_ERR_SHAPE for dv < 1.
+ * (d, dv): d and dv in {64, 96, 128, 256} (dv == d runs the attn_fwd
+ * kernels; a pair with a 256-wide side runs the d = 256 kernel and takes
+ * FA_F16 or FA_BF16 only); FA_ERR_UNSUPPORTED for other pairs, FA_ERR_SHAPE
+ * for dv < 1.
  */
 int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse,
                 int64_t B, int64_t H, int64_t N, int64_t d, int64_t dv,
@@ -263,7 +265,8 @@ int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse
  * recomputed S = q k^T, dq = scale dS k and dk = scale dS^T q stay over d
  * (V is N x d_v in "Flash Attention: IO-Aware Exact Attention", section "Why
  * intermediate matrices cost memory traffic").  Supported
- * (d, d_v): d and d_v in {64, 96, 128} (d_v == d runs the attn_bwd kernels);
+ * (d, d_v): d and d_v in {64, 96, 128, 256} (d_v == d runs the attn_bwd
+ * kernels);
  * FA_ERR_UNSUPPORTED for other pairs and for FA_F32, FA_ERR_SHAPE for
  * d_v < 1.  The workspace is as for attn_bwd (attn_bwd_workspace_bytes).
  */

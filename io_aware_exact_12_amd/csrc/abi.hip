@@ -106,15 +106,16 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.mask_sb = mask_b == 1 ? 0 : mask_h * nb * nb;
   }
   a.lv = a.dv == d ? a.in : fa::dense_layout(H, N, a.dv);
-  // d = 256: bf16 / fp16, d_v = d
-  if (d == 256 && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  // d = 256 or d_v = 256: bf16 / fp16 (the wide kernel)
+  const bool wide = d == 256 || a.dv == 256;
+  if (wide && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
     return FA_ERR_ALIGN;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (d == 256) {
+  if (wide) {
     e = dtype == FA_BF16 ? fa::launch_fwd_wide_bf16(a, s) : fa::launch_fwd_wide_f16(a, s);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
   }
@@ -165,8 +166,6 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   a.dvw = d;
   a.lv = a.in;
   a.outv = a.out;
-  // d = 256: d_v = d
-  if (d == 256 && dvw != 0 && dvw != d) return FA_ERR_UNSUPPORTED;
   if (dvw != 0 && dvw != d) {  // v, o, dout and dv rows of dvw elements, dense
     if (!fa::dv_pair_built(d, dvw)) return FA_ERR_UNSUPPORTED;
     a.dvw = dvw;

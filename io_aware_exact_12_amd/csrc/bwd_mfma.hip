@@ -312,12 +312,12 @@ __device__ __forceinline__ void sum_rows_f32(const float* base, int64_t slot, in
   }
 }
 
-// Workgroups per CU: two below d = 256; at d = 256 one, so that each wave
+// Workgroups per CU: two below d = 256; with a 256-wide side one, so that each wave
 // may hold 512 registers (its resident operands alone take 128).
-template <int D> constexpr int kBwdOcc = D > 128 ? 1 : 2;
+template <int D, int DV = D> constexpr int kBwdOcc = (D > 128 || DV > 128) ? 1 : 2;
 
 template <bool IsBf16, int D, bool Causal, int Mode, int DV>
-__global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dkdv(
+__global__ __launch_bounds__(kThr, (kBwdOcc<D, DV>)) void bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ NLse, const float* __restrict__ Dsum,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int win, int H, int BH, float c,
@@ -734,7 +734,7 @@ template <int D, int DV = D> struct DqLds {
 };
 
 template <bool IsBf16, int D, bool Causal, int Mode, int DV>
-__global__ __launch_bounds__(kThr, kBwdOcc<D>) void bwd_dq(
+__global__ __launch_bounds__(kThr, (kBwdOcc<D, DV>)) void bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dsum,
     float* __restrict__ NLse, uint16_t* __restrict__ dQ, int N, int win, int H, int BH, int n_qblocks,
@@ -1258,6 +1258,12 @@ hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
   // d_v != d (plain masks only): q, k, dq, dk rows of d, v, o, dout, dv rows
   // of d_v; d, d_v in {64, 96, 128}
   if (a.dvw != a.d) {
+    if (a.dvw == 256)
+      return a.d == 64 ? launch_dv<IsBf16, 64, 256>(a, s)
+           : a.d == 96 ? launch_dv<IsBf16, 96, 256>(a, s) : launch_dv<IsBf16, 128, 256>(a, s);
+    if (a.d == 256)
+      return a.dvw == 64 ? launch_dv<IsBf16, 256, 64>(a, s)
+           : a.dvw == 96 ? launch_dv<IsBf16, 256, 96>(a, s) : launch_dv<IsBf16, 256, 128>(a, s);
     if (a.d == 128) return a.dvw == 64 ? launch_dv<IsBf16, 128, 64>(a, s) : launch_dv<IsBf16, 128, 96>(a, s);
     if (a.d == 96) return a.dvw == 64 ? launch_dv<IsBf16, 96, 64>(a, s) : launch_dv<IsBf16, 96, 128>(a, s);
     return a.dvw == 96 ? launch_dv<IsBf16, 64, 96>(a, s) : launch_dv<IsBf16, 64, 128>(a, s);

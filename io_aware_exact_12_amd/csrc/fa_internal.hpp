@@ -70,11 +70,13 @@ struct BwdArgs {
 // most this many chunks, each run by a dK/dV workgroup of its own.
 constexpr int kBwdSparseSplit = 4;
 
-// Widths of v (and o, dout, dv) rows other than d that the MFMA and fp32
-// kernels are built for: d and d_v in {64, 96, 128}, d_v != d.
+// Widths of v (and o, dout, dv) rows other than d that the kernels are built
+// for: d and d_v in {64, 96, 128, 256}, d_v != d.  A pair with a 256 side runs
+// the d = 256 kernels (bf16 / fp16 only); the others run the MFMA kernels of
+// d <= 128 and the fp32 path.
 inline bool dv_pair_built(int64_t d, int64_t dv) {
-  const bool d_ok = d == 64 || d == 96 || d == 128, dv_ok = dv == 64 || dv == 96 || dv == 128;
-  return d_ok && dv_ok && d != dv;
+  auto ok = [](int64_t x) { return x == 64 || x == 96 || x == 128 || x == 256; };
+  return ok(d) && ok(dv) && d != dv;
 }
 
 // Launchers return the hipError_t of the launch (hipSuccess when enqueued).

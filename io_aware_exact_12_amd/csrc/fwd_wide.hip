@@ -60,8 +60,15 @@ template <int D> struct BlockTile {
 };
 
 // MFMA slot of step st (0 scale, 1 exp2, 2 pack and partial sum) of score
-// pair e among the 16 score MFMAs of a block.
-constexpr int slot_of(int e, int st) { return e + (st == 0 ? 0 : st == 1 ? 2 : 5); }
+// pair e among the kKs score MFMAs of a block (16 at d = 256; 8, 6 or 4 when
+// only the values are 256 wide).  Each step lands a few slots after the one
+// it depends on.
+template <int kKs>
+constexpr int slot_of(int e, int st) {
+  return kKs == 16 ? e + (st == 0 ? 0 : st == 1 ? 2 : 5)
+       : (kKs == 8 || kKs == 6) ? e / 2 + st
+                                : (e / 4 + st < 3 ? e / 4 + st : 3);
+}
 
 // kWin (causal only): a sliding window of `win` keys, key j visible to query
 // i iff i - win < j <= i.  Blocks left of every query's window are skipped
@@ -73,12 +80,14 @@ constexpr int slot_of(int e, int st) { return e + (st == 0 ? 0 : st == 1 ? 2 : 5
 // blocks sees and walks their 32-key halves as its blocks; a wave masks the
 // blocks of tiles its own query block does not see, and a row that sees no
 // key stores O = 0 and LSE = -inf.
-template <bool IsBf16, int D, bool Causal, bool kWin, bool kSparse>
+// DV is the width of the V and O rows: D = DV = 256, or one of them 256 and
+// the other 64, 96 or 128 (plain masks only).
+template <bool IsBf16, int D, bool Causal, bool kWin, bool kSparse, int DV = D>
 __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int win, int H, int BH, int n_qblocks,
-    float c, uint32_t q_sign, Layout lq, Layout in, Layout out, const uint8_t* __restrict__ bmask,
-    int64_t m_sb, int64_t m_sh) {
+    float c, uint32_t q_sign, Layout lq, Layout in, Layout lv, Layout out,
+    const uint8_t* __restrict__ bmask, int64_t m_sb, int64_t m_sh) {
   static_assert(!kWin || Causal, "the sliding window is causal");
   static_assert(!(kWin && kSparse), "one of the two masks");
   static_assert(2 * kB == kSparseBlock && kRes % kSparseBlock == 0, "mask tiles are two blocks");
@@ -86,10 +95,12 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
   using vec8 = typename E::vec8;
   using T = STile<D>;
   using BT = BlockTile<D>;
-  constexpr int kKs = D / 16, kDB = D / 32;
-  constexpr int kStage = 2 * BT::kBytes;  // K tile, then V tile
+  using BTV = BlockTile<DV>;
+  constexpr int kKs = D / 16, kDB = DV / 32;
+  constexpr int kStage = BT::kBytes + BTV::kBytes;  // K tile, then V tile
   static_assert(kStages * kStage + kSparseBytes <= 160 * 1024, "the ring and the tile list fit the LDS");
-  static_assert(kKs == 16, "the probability schedule spreads 8 score pairs over 16 MFMAs");
+  static_assert(DV == D || !(kWin || kSparse), "d_v != d with plain masks only");
+  static_assert(kKs == 16 || kKs == 8 || kKs == 6 || kKs == 4, "slot maps exist for 4, 6, 8 and 16 MFMAs");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage + (kSparse ? kSparseBytes : 0)];
 
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
@@ -142,24 +153,29 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
   // first block of the workgroup and of this wave (sliding window; 0 without)
   const int u_first = kWin ? max(0, q0 - win + 1) / kB : 0;
   const int u_lo = kWin ? max(0, qw0 - win + 1) / kB : 0;
-  const int64_t head = b * in.sb + h * in.sh;
-  const uint16_t* k_h = K + head;
-  const uint16_t* v_h = V + head;
-  uint32_t src[BT::kPerWave];
+  if constexpr (DV == D) lv = in;  // one layout: the d_v addressing folds away
+  const uint16_t* k_h = K + (b * in.sb + h * in.sh);
+  const uint16_t* v_h = V + (b * lv.sb + h * lv.sh);
+  uint32_t src[BT::kPerWave], src_v[BTV::kPerWave];
   BT::sources(wave, lane, (uint32_t)(2 * in.sn), src);
+  BTV::sources(wave, lane, (uint32_t)(2 * lv.sn), src_v);
   const uint32_t lds0 = lds_u32(smem);
-  // copies of block u's K and V rows into its stage: 2 kPerWave per wave
+  // copies of block u's K and V rows into its stage: BT::kPerWave +
+  // BTV::kPerWave per wave
   auto issue = [&](int u) {
     const int row0 = ks_of(u), left = N - row0;
-    const uint32_t bytes = left > 0 ? (uint32_t)(left - 1) * (uint32_t)(2 * in.sn) + (uint32_t)T::kDataBytes : 0u;
-    const i32x4 rk = make_rsrc(k_h + (int64_t)row0 * in.sn, bytes);
-    const i32x4 rv = make_rsrc(v_h + (int64_t)row0 * in.sn, bytes);
+    const uint32_t kbytes =
+        left > 0 ? (uint32_t)(left - 1) * (uint32_t)(2 * in.sn) + (uint32_t)T::kDataBytes : 0u;
+    const uint32_t vbytes =
+        left > 0 ? (uint32_t)(left - 1) * (uint32_t)(2 * lv.sn) + (uint32_t)STile<DV>::kDataBytes : 0u;
+    const i32x4 rk = make_rsrc(k_h + (int64_t)row0 * in.sn, kbytes);
+    const i32x4 rv = make_rsrc(v_h + (int64_t)row0 * lv.sn, vbytes);
     const uint32_t base = lds0 + (uint32_t)((u & (kStages - 1)) * kStage);
 #pragma unroll
     for (int i = 0; i < BT::kPerWave; ++i) dma16(rk, base + (uint32_t)((wave + kW * i) * 1024), src[i]);
 #pragma unroll
-    for (int i = 0; i < BT::kPerWave; ++i)
-      dma16(rv, base + (uint32_t)(BT::kBytes + (wave + kW * i) * 1024), src[i]);
+    for (int i = 0; i < BTV::kPerWave; ++i)
+      dma16(rv, base + (uint32_t)(BT::kBytes + (wave + kW * i) * 1024), src_v[i]);
   };
   auto k_tile = [&](int u) { return smem + (u & (kStages - 1)) * kStage; };
   auto v_tile = [&](int u) { return smem + (u & (kStages - 1)) * kStage + BT::kBytes; };
@@ -241,15 +257,15 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
           }
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            if (t == slot_of(e, 0)) {
+            if (t == slot_of<kKs>(e, 0)) {
               pr[2 * e] = __builtin_fmaf(s_cur[2 * e], c, neg_mc);
               pr[2 * e + 1] = __builtin_fmaf(s_cur[2 * e + 1], c, neg_mc);
             }
-            if (t == slot_of(e, 1)) {
+            if (t == slot_of<kKs>(e, 1)) {
               pr[2 * e] = __builtin_amdgcn_exp2f(pr[2 * e]);
               pr[2 * e + 1] = __builtin_amdgcn_exp2f(pr[2 * e + 1]);
             }
-            if (t == slot_of(e, 2)) {
+            if (t == slot_of<kKs>(e, 2)) {
               pw[e >> 2][e & 3] = E::pack2(pr[2 * e], pr[2 * e + 1]);
               sum[e & 1] += pr[2 * e] + pr[2 * e + 1];
             }
@@ -265,12 +281,12 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
 
       // O^T += V^T P^T of block u; operand reads two MFMAs ahead
       const uint8_t* vt = v_tile(u);
-      vec8 va[2] = {tr_frag<IsBf16, D>(vt, lane, 0, 0), tr_frag<IsBf16, D>(vt, lane, 0, 1)};
+      vec8 va[2] = {tr_frag<IsBf16, DV>(vt, lane, 0, 0), tr_frag<IsBf16, DV>(vt, lane, 1 / kDB, 1 % kDB)};
 #pragma unroll
       for (int i = 0; i < 2 * kDB; ++i) {
         const int tt = i / kDB, db = i % kDB;
         acc[db] = E::mfma(va[i & 1], __builtin_bit_cast(vec8, pw[tt]), acc[db]);
-        if (i + 2 < 2 * kDB) va[i & 1] = tr_frag<IsBf16, D>(vt, lane, (i + 2) / kDB, (i + 2) % kDB);
+        if (i + 2 < 2 * kDB) va[i & 1] = tr_frag<IsBf16, DV>(vt, lane, (i + 2) / kDB, (i + 2) % kDB);
         __builtin_amdgcn_sched_barrier(0);
       }
       s_cur = s_next;
@@ -278,7 +294,7 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
     // block u+2's tiles must be in LDS for S(u+2) in the next block; the
     // copies just issued (block u+3) may stay in flight
     if (more)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * BT::kPerWave));  // vmcnt(2 kPerWave)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (BT::kPerWave + BTV::kPerWave));  // the latest block's copies
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
@@ -287,12 +303,12 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
   const float l_tot = xhalf_sum(l);
   if (my_q >= N) return;
   const float inv = (!kSparse || l_tot > 0.f) ? 1.0f / l_tot : 0.f;  // a row with no key: O = 0
-  store_row<IsBf16, D>(O + (b * out.sb + h * out.sh), my_q, out.sn, g, acc, inv);
+  store_row<IsBf16, DV>(O + (b * out.sb + h * out.sh), my_q, out.sn, g, acc, inv);
   if (LSE != nullptr && g == 0)
     LSE[(int64_t)bh * N + my_q] = ((m == -INFINITY ? 0.f : m * c) + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
-template <bool IsBf16, int D, bool Causal, bool kWin = false, bool kSparse = false>
+template <bool IsBf16, int D, bool Causal, bool kWin = false, bool kSparse = false, int DV = D>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int N = (int)a.N;
   const int BH = (int)(a.B * a.H);
@@ -302,16 +318,29 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const float c = a.scale != 0.f ? __builtin_fabsf(a.scale) * 1.4426950408889634f : 1e-30f;
   const uint32_t q_sign = a.scale < 0.f ? 0x80008000u : 0u;
   const int win = (int)(a.window < a.N ? a.window : a.N);
-  hipLaunchKernelGGL((fwd_wide_kernel<IsBf16, D, Causal, kWin, kSparse>), dim3((unsigned)(n_qblocks * BH)),
+  hipLaunchKernelGGL((fwd_wide_kernel<IsBf16, D, Causal, kWin, kSparse, DV>), dim3((unsigned)(n_qblocks * BH)),
                      dim3(kThr), 0, stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<uint16_t*>(a.o), a.lse, N, win, (int)a.H, BH, n_qblocks, c, q_sign, a.lq,
-                     a.in, a.out, a.block_mask, a.mask_sb, a.mask_sh);
+                     a.in, a.lv, a.out, a.block_mask, a.mask_sb, a.mask_sh);
   return hipGetLastError();
+}
+
+template <bool IsBf16, int D, int DV>
+hipError_t launch_dv(const FwdArgs& a, hipStream_t s) {
+  return a.causal ? launch<IsBf16, D, true, false, false, DV>(a, s) : launch<IsBf16, D, false, false, false, DV>(a, s);
 }
 
 template <bool IsBf16>
 hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
+  // d_v != d with one of them 256 (plain masks only)
+  if (a.dv != a.d) {
+    if (a.d == 256)
+      return a.dv == 64 ? launch_dv<IsBf16, 256, 64>(a, s)
+           : a.dv == 96 ? launch_dv<IsBf16, 256, 96>(a, s) : launch_dv<IsBf16, 256, 128>(a, s);
+    return a.d == 64 ? launch_dv<IsBf16, 64, 256>(a, s)
+         : a.d == 96 ? launch_dv<IsBf16, 96, 256>(a, s) : launch_dv<IsBf16, 128, 256>(a, s);
+  }
   if (a.block_mask != nullptr)
     return a.causal ? launch<IsBf16, 256, true, false, true>(a, s) : launch<IsBf16, 256, false, false, true>(a, s);
   if (!a.causal) return launch<IsBf16, 256, false>(a, s);

@@ -333,9 +333,12 @@ def test_dv_validation():
         return fa.attn_fwd_dv_raw(q, P[1], P[2], P[3], P[4], a["B"], a["H"], a["N"], d, dv, a["mask"],
                                   a["scale"], a["dtype"], None)
     assert fdv(128, 0) == FA_ERR_SHAPE
-    for d, dv in ((128, 32), (64, 256), (256, 128), (128, 256), (80, 64), (64, 80)):
+    for d, dv in ((128, 32), (256, 32), (80, 64), (64, 80), (256, 512)):
         assert fdv(d, dv) == FA_ERR_UNSUPPORTED, (d, dv)
-    for d, dv in ((128, 64), (64, 128), (128, 96), (96, 128), (96, 64), (64, 96), (128, 128), (96, 96)):
+    for d, dv in ((256, 64), (128, 256)):                      # the d = 256 kernels: no fp32
+        assert fdv(d, dv, dtype=fa.F32) == FA_ERR_UNSUPPORTED, (d, dv)
+    for d, dv in ((128, 64), (64, 128), (128, 96), (96, 128), (96, 64), (64, 96), (128, 128), (96, 96),
+                  (256, 64), (256, 96), (256, 128), (64, 256), (96, 256), (128, 256)):
         assert fdv(d, dv, q=P[0] + 2) == FA_ERR_ALIGN, (d, dv)  # accepted: reaches the pointer checks
     assert fdv(128, 64, q=None) == FA_ERR_NULL
     assert fdv(64, 128, N=(1 << 23)) == FA_ERR_SHAPE           # v rows of a head span 2 GiB
@@ -348,20 +351,22 @@ def test_bwd_dv_validation():
         return fa.attn_bwd_dv_raw(q, P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0], a["B"], a["H"],
                                   a["N"], d, dv, a["mask"], a["scale"], a["dtype"], P[1], a["ws"], None)
     assert bdv(128, 0) == FA_ERR_SHAPE
-    for d, dv in ((128, 32), (64, 256), (256, 128), (128, 256), (80, 64), (64, 80)):
+    for d, dv in ((128, 32), (256, 32), (80, 64), (64, 80), (256, 512)):
         assert bdv(d, dv) == FA_ERR_UNSUPPORTED, (d, dv)
+    assert bdv(256, 128, dtype=fa.F32) == FA_ERR_UNSUPPORTED
     assert bdv(128, 64, dtype=fa.F32) == FA_ERR_UNSUPPORTED
     assert bdv(128, 64, ws=8) == FA_ERR_WORKSPACE
-    for d, dv in ((128, 64), (64, 128), (128, 96), (96, 128), (96, 64), (64, 96), (128, 128), (96, 96)):
+    for d, dv in ((128, 64), (64, 128), (128, 96), (96, 128), (96, 64), (64, 96), (128, 128), (96, 96),
+                  (256, 64), (256, 96), (256, 128), (64, 256), (96, 256), (128, 256)):
         assert bdv(d, dv, q=P[0] + 2) == FA_ERR_ALIGN, (d, dv)  # accepted: reaches the pointer checks
     assert bdv(128, 64, q=None) == FA_ERR_NULL
     assert bdv(64, 128, N=(1 << 23), ws=1 << 40) == FA_ERR_SHAPE  # v rows of a head span 2 GiB
 
 
 def test_wide_head_validation():
-    """d = 256: the plain, sliding-window and block-sparse forward and backward
-    (bf16 / fp16) reach the pointer checks; fp32 and every variant they do not
-    take return FA_ERR_UNSUPPORTED."""
+    """d = 256: the plain, sliding-window, block-sparse and d_v != d forward and
+    backward (bf16 / fp16) reach the pointer checks; fp32 and every variant
+    they do not take return FA_ERR_UNSUPPORTED."""
     assert fwd(d=256, q=P[0] + 2) == FA_ERR_ALIGN
     assert fwd(d=256, dtype=fa.F16, mask=1, q=P[0] + 2) == FA_ERR_ALIGN
     assert fwd(d=256, dtype=fa.F32) == FA_ERR_UNSUPPORTED
@@ -369,7 +374,9 @@ def test_wide_head_validation():
     assert fwd_w(4, d=256, N=64, q=P[0] + 2) == FA_ERR_ALIGN
     assert fwd_w(64, d=256, N=64, q=P[0] + 2) == FA_ERR_ALIGN   # a window >= N is plain causal
     assert fwd_bs(d=256, q=P[0] + 2) == FA_ERR_ALIGN
-    assert fa.attn_fwd_dv_raw(P[0], P[1], P[2], P[3], P[4], 1, 1, 16, 256, 128, 0, 0.1, fa.BF16,
+    assert fa.attn_fwd_dv_raw(P[0] + 2, P[1], P[2], P[3], P[4], 1, 1, 16, 256, 128, 0, 0.1, fa.BF16,
+                              None) == FA_ERR_ALIGN         # d_v != d with a 256 side: accepted
+    assert fa.attn_fwd_dv_raw(P[0], P[1], P[2], P[3], P[4], 1, 1, 16, 256, 128, 0, 0.1, fa.F32,
                               None) == FA_ERR_UNSUPPORTED
     assert fa.attn_fwd_dv_raw(P[0] + 2, P[1], P[2], P[3], P[4], 1, 1, 16, 256, 256, 0, 0.1, fa.BF16,
                               None) == FA_ERR_ALIGN
