@@ -174,9 +174,9 @@ def test_sharp_rows_rescaling(fa):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_sharp_rows_fp32(fa, d):
-    """fp32 inputs with scores of std 9 and an increasing trend, held to 1e-5:
-    the fp32 path splits each row's keys over four waves, whose running maxima
-    differ widely before they are merged."""
+    """fp32 inputs with scores of std 9 and an increasing trend, held to 1e-5
+    (two heads: the row-per-wave kernel, whose running maximum moves block by
+    block)."""
     n = 777
     log(f"case sharp rows fp32 d={d} N={n}")
     x = workloads.random_inputs(1, 2, n, d, "fp32", seed=70 + d, qk_std=3.0, v_dist="uniform")
@@ -187,6 +187,45 @@ def test_sharp_rows_fp32(fa, d):
         ro, rl = oracle.dense_fwd(x["q"], x["k"], x["v"], causal=causal)
         compare("O", o, ro, "fp32")
         compare("LSE", lse, rl, LSE_TOL["fp32"])
+
+
+@pytest.mark.parametrize("kind", ["plain", "causal", "window", "sparse", "dv"])
+def test_fp32_tiled_kernel(fa, kind):
+    """fp32 launches that fill the GPU with 64-row workgroups (B*H*ceil(N/64) >= 256:
+    here 20 heads of N = 777) run the tiled fp32 kernel, whose rows' keys are split
+    over four waves and merged; smaller launches run the row-per-wave kernel, which
+    the sweeps cover.  Sharp rows (q, k ~ N(0, 9)) with a ramp on the keys, so the
+    waves' running maxima differ widely before the merge; every head is compared."""
+    n, h = 777, 20
+    d, dv = (128, 64) if kind == "dv" else (64, 64)
+    log(f"case fp32 tiled kernel kind={kind} H={h} N={n} d={d} dv={dv}")
+    x = workloads.random_inputs(1, h, n, d, "fp32", seed=4321, qk_std=3.0, v_dist="uniform")
+    ramp = np.linspace(0, 2, n, dtype=np.float32)[None, None, :, None]
+    x["k"] = (x["k"] + ramp).astype(np.float32)
+    v = workloads.random_inputs(1, h, n, dv, "fp32", seed=4322)["v"] if kind == "dv" else x["v"]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").contiguous()
+    q, k, vt = dev(x["q"]), dev(x["k"]), dev(v)
+    causal = kind in ("causal", "window", "dv")
+    kw, okw = {}, {}
+    if kind == "window":
+        kw["window"] = okw["window"] = 100
+    if kind == "sparse":
+        rng = np.random.default_rng(77)
+        nb = -(-n // 64)
+        bm = (rng.random((1, h, nb, nb)) < 0.5).astype(np.uint8)
+        kw["block_mask"] = torch.from_numpy(bm).to("cuda")
+        okw["block_mask"] = bm
+    o, lse = fa.attn_fwd(q, k, vt, causal=causal, **kw)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    for hh in range(h):
+        sl = (slice(0, 1), slice(hh, hh + 1))
+        hk = {} if "block_mask" not in okw else {"block_mask": okw["block_mask"][:, hh:hh + 1]}
+        if "window" in okw:
+            hk["window"] = okw["window"]
+        ro, rl = oracle.dense_fwd(x["q"][sl], x["k"][sl], v[sl], causal=causal, **hk)
+        compare(f"O[h={hh}]", o[sl], ro, "fp32")
+        compare(f"LSE[h={hh}]", lse[sl], rl, LSE_TOL["fp32"])
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
