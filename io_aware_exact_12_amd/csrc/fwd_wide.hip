@@ -41,6 +41,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 template <bool IsBf16> constexpr float kLazy = IsBf16 ? 24.f : 15.f;
 constexpr int kB = 32;       // keys per block (one streamed tile)
 constexpr int kStages = 4;
+constexpr int kAhead = 2;    // LDS operand reads issued this many MFMAs before their use
 
 // A 32-row streamed tile: the first half of STile<D>'s format.
 template <int D> struct BlockTile {
@@ -244,16 +245,16 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
         constexpr bool kNext = decltype(next)::value;
         const uint8_t* kt = k_tile(u + 1);
         float pr[16];
-        vec8 ka[2];
+        vec8 ka[kAhead];
         if constexpr (kNext) {
-          ka[0] = row_frag<IsBf16, D>(kt, l32, g, 0);
-          ka[1] = row_frag<IsBf16, D>(kt, l32, g, 1);
+#pragma unroll
+          for (int r = 0; r < kAhead && r < kKs; ++r) ka[r] = row_frag<IsBf16, D>(kt, l32, g, r);
         }
 #pragma unroll
         for (int t = 0; t < kKs; ++t) {
           if constexpr (kNext) {
-            s_next = E::mfma(ka[t & 1], qf[t], t == 0 ? f32x16{} : s_next);
-            if (t + 2 < kKs) ka[t & 1] = row_frag<IsBf16, D>(kt, l32, g, t + 2);
+            s_next = E::mfma(ka[t % kAhead], qf[t], t == 0 ? f32x16{} : s_next);
+            if (t + kAhead < kKs) ka[t % kAhead] = row_frag<IsBf16, D>(kt, l32, g, t + kAhead);
           }
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -281,12 +282,15 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
 
       // O^T += V^T P^T of block u; operand reads two MFMAs ahead
       const uint8_t* vt = v_tile(u);
-      vec8 va[2] = {tr_frag<IsBf16, DV>(vt, lane, 0, 0), tr_frag<IsBf16, DV>(vt, lane, 1 / kDB, 1 % kDB)};
+      vec8 va[kAhead];
+#pragma unroll
+      for (int r = 0; r < kAhead && r < 2 * kDB; ++r) va[r] = tr_frag<IsBf16, DV>(vt, lane, r / kDB, r % kDB);
 #pragma unroll
       for (int i = 0; i < 2 * kDB; ++i) {
         const int tt = i / kDB, db = i % kDB;
-        acc[db] = E::mfma(va[i & 1], __builtin_bit_cast(vec8, pw[tt]), acc[db]);
-        if (i + 2 < 2 * kDB) va[i & 1] = tr_frag<IsBf16, DV>(vt, lane, (i + 2) / kDB, (i + 2) % kDB);
+        acc[db] = E::mfma(va[i % kAhead], __builtin_bit_cast(vec8, pw[tt]), acc[db]);
+        if (i + kAhead < 2 * kDB)
+          va[i % kAhead] = tr_frag<IsBf16, DV>(vt, lane, (i + kAhead) / kDB, (i + kAhead) % kDB);
         __builtin_amdgcn_sched_barrier(0);
       }
       s_cur = s_next;
