@@ -132,11 +132,16 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
  *     dq = scale dS k,  dk = scale dS^T q.
  *
  *   q, k, v, dout     [B][H][N][d] inputs of type dtype.
- *   o                 [B][H][N][d] forward output of type dtype.  Checked like
- *                     the other pointers but not read: the row term
- *                     D_i = sum_j P_ij dP_ij (= dout_i . o_i in exact
+ *   o                 [B][H][N][d] forward output of type dtype.  The row
+ *                     term D_i = sum_j P_ij dP_ij (= dout_i . o_i in exact
  *                     arithmetic) is formed from the recomputed P and dP in
- *                     fp32, which keeps o's rounding out of dS.
+ *                     fp32, which keeps o's rounding out of dS.  For
+ *                     d = d_v <= 128 under plain and window masks the dq
+ *                     kernel also reads o: it accumulates dq with the
+ *                     estimate dout_i . o_i and corrects it with the exact D
+ *                     at the end, so o moves only the rounding of dq, not its
+ *                     value in exact arithmetic.  The other paths check o but
+ *                     do not read it.
  *   lse               [B][H][N] fp32 natural-log log-sum-exp returned by
  *                     attn_fwd for the same q, k, v, mask and scale.
  *   dq, dk, dv        [B][H][N][d] outputs of type dtype (must not overlap the
@@ -145,7 +150,7 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
  *                     bytes, 16-byte aligned, owned by the caller; its
  *                     contents are scratch on return.
  *   mask, scale, B, H, N, d, stream: as for attn_fwd (d = 256 runs the
- *                     same two kernels at one workgroup per CU).
+ *                     two-pass kernels at one workgroup per CU).
  *   dtype             FA_F16 or FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED).
  *
  * Deterministic: no atomics are used.  FA_ERR_WORKSPACE if workspace is NULL
