@@ -341,6 +341,14 @@ struct FwdBlock {
   __device__ __forceinline__ void apply_mask(int u, f32x16& st) const {
     // register r of lane half g holds key kpos(u) + 16 (r >> 3) + 8 g + (r & 7)
     const int k0 = kpos(u);
+    // Wave-uniform: a block whose keys every row of the wave sees (none past
+    // the first row's diagonal or the sequence end, none left of the last
+    // row's window) needs no selects.  In a step that may need masks only a
+    // wave's diagonal block (and a block at the sequence end or the window
+    // edge) does.
+    const bool cut_right = k0 + 31 > (Causal ? min(q0, N - 1) : N - 1);
+    const bool cut_left = kMask == kMaskWindow && kWin && k0 <= q0 + 31 - win;
+    if (!cut_right && !cut_left) return;
     const int lim = (Causal ? min(my_q, N - 1) : N - 1) - k0 - 8 * g;
     const int lo = my_q - win + 1 - k0 - 8 * g;
 #pragma unroll
