@@ -189,7 +189,7 @@ def test_sharp_rows_fp32(fa, d):
         compare("LSE", lse, rl, LSE_TOL["fp32"])
 
 
-@pytest.mark.parametrize("kind", ["plain", "causal", "window", "sparse", "dv"])
+@pytest.mark.parametrize("kind", ["plain", "causal", "window", "sparse", "dv", "strided"])
 def test_fp32_tiled_kernel(fa, kind):
     """fp32 launches that fill the GPU with 64-row workgroups (B*H*ceil(N/64) >= 256:
     here 20 heads of N = 777) run the tiled fp32 kernel, whose rows' keys are split
@@ -204,8 +204,10 @@ def test_fp32_tiled_kernel(fa, kind):
     x["k"] = (x["k"] + ramp).astype(np.float32)
     v = workloads.random_inputs(1, h, n, dv, "fp32", seed=4322)["v"] if kind == "dv" else x["v"]
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").contiguous()
+    if kind == "strided":  # [B][N][H][d] storage seen as [B][H][N][d] views
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3))).to("cuda").transpose(1, 2)
     q, k, vt = dev(x["q"]), dev(x["k"]), dev(v)
-    causal = kind in ("causal", "window", "dv")
+    causal = kind in ("causal", "window", "dv", "strided")
     kw, okw = {}, {}
     if kind == "window":
         kw["window"] = okw["window"] = 100
