@@ -16,7 +16,7 @@
 // into dS = P (dP - D), where dP and D nearly cancel on a row's dominant
 // keys; so D is formed from the recomputed P and dP in fp32 instead.
 //
-// Two kernels whose sums run in a fixed order, so the result is deterministic
+// Two kernels per call, whose sums run in a fixed order, so the result is deterministic
 // (the only atomic is the block-sparse split path's per-key-block counter,
 // which picks the workgroup that adds the partial sums, in chunk order):
 //   * bwd_dq:     a workgroup keeps 128 query rows resident (Q^T and dO^T in
@@ -1256,7 +1256,7 @@ hipError_t launch_dv(const BwdArgs& a, hipStream_t s) {
 template <bool IsBf16>
 hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
   // d_v != d (plain masks only): q, k, dq, dk rows of d, v, o, dout, dv rows
-  // of d_v; d, d_v in {64, 96, 128}
+  // of d_v; d, d_v in {64, 96, 128, 256}
   if (a.dvw != a.d) {
     if (a.dvw == 256)
       return a.d == 64 ? launch_dv<IsBf16, 64, 256>(a, s)

@@ -397,7 +397,7 @@ struct FwdBlock {
   }
 
   // MFMA slot of step st (0 scale, 1 exp2, 2 pack and partial sum) of score
-  // pair e, for blocks of 16, 12 (d = 96), 8, 6 or 4 MFMA slots.  Steps that
+  // pair e, for blocks of 16, 14, 12 (d = 96), 10, 8, 6 or 4 MFMA slots.  Steps that
   // land in the same slot run in program order.
   template <int kSlots>
   static constexpr int slot_of(int e, int st) {
