@@ -5,4 +5,4 @@ by the benchmark's ``cpu_baseline`` leg, never by the product path.  It shares n
 code with the HIP library.
 """
 from .attention import (dense_bwd, dense_fwd, dense_probs, loop_order_ledger,  # noqa: F401
-                        online_fwd, online_fwd_kv_outer, transfer_ledger)
+                        online_fwd, online_fwd_kv_outer, sampled_bwd, transfer_ledger)

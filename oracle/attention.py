@@ -399,6 +399,53 @@ def dense_bwd(q, k, v, do, causal=False, scale=None, window=None, block_mask=Non
     return dq, dk, dv, o, lse
 
 
+def sampled_bwd(q, k, v, do, causal=False, scale=None, rows=(), cols=(), chunk=1024):
+    """The gradients of dense_bwd for one head ([N, d] arrays, d_v for v and
+    do), restricted to the listed query rows (dQ) and key columns (dK, dV), for
+    sequences whose N x N matrices do not fit in memory.
+
+    Same definitions as dense_bwd: P = exp(S - LSE), dP = dO V^T,
+    D_i = sum_c dO_ic O_ic, dS = P * (dP - D), dQ = scale dS K,
+    dK = scale dS^T Q, dV = P^T dO.  Every query row enters dK and dV of a key,
+    so the rows are visited in chunks: each chunk forms its scores against all
+    keys, its LSE, O and D, adds its share of dK and dV of the listed keys, and
+    gives dQ of the listed rows it holds.  Returns ``(dq, dk, dv)`` in float64,
+    shaped [len(rows), d], [len(cols), d], [len(cols), d_v].
+    """
+    q = _as64(q)
+    k = _as64(k)
+    v = _as64(v)
+    do = _as64(do)
+    n = q.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[-1])
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    dq = np.zeros((len(rows), q.shape[1]))
+    dk = np.zeros((len(cols), k.shape[1]))
+    dv = np.zeros((len(cols), v.shape[1]))
+    for r0 in range(0, n, chunk):
+        r = np.arange(r0, min(n, r0 + chunk))
+        s = _scores(q, k, scale, causal, rows=r)           # [c, N]
+        m = s.max(axis=-1, keepdims=True)
+        lse = m + np.log(np.exp(s - m).sum(axis=-1, keepdims=True))
+        p = np.exp(s - lse)
+        o = p @ v
+        D = (do[r] * o).sum(axis=-1, keepdims=True)
+        # the listed keys: dV_j = sum_i P_ij dO_i, dK_j = scale sum_i dS_ij q_i
+        pc = p[:, cols]
+        dsc = pc * (do[r] @ v[cols].T - D)
+        dv += pc.T @ do[r]
+        dk += scale * (dsc.T @ q[r])
+        # the listed rows in this chunk: dQ_i = scale sum_j dS_ij k_j
+        mine = np.nonzero((rows >= r0) & (rows < r0 + len(r)))[0]
+        if len(mine):
+            loc = rows[mine] - r0
+            ds = p[loc] * (do[rows[mine]] @ v.T - D[loc])
+            dq[mine] = scale * (ds @ k)
+    return dq, dk, dv
+
+
 def transfer_ledger(n, d, dv, query_block, key_block):
     """Count element transfers of the explorer's declared dense and tiled schedules.
 

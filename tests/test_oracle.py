@@ -634,6 +634,23 @@ def test_backward_dv_differs_from_d_against_torch_autograd(d, dv):
             np.testing.assert_allclose(a, b.numpy(), rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_backward_against_torch_autograd(causal):
+    """sampled_bwd (row chunks of 7, so rows and columns cross chunk edges, and
+    d_v != d) against float64 autograd on the listed rows and key columns."""
+    n = 40
+    q, k = _rand(1, n, 8, seed=301)[0], _rand(1, n, 8, seed=302)[0]
+    v, do = _rand(1, n, 5, seed=303)[0], _rand(1, n, 5, seed=304)[0]
+    rows, cols = [0, 6, 7, 20, 39], [0, 1, 13, 38, 39]
+    dq, dk, dv = oracle.sampled_bwd(q, k, v, do, causal=causal, rows=rows, cols=cols, chunk=7)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None], is_causal=causal)
+    to.backward(torch.from_numpy(do)[None])
+    np.testing.assert_allclose(dq, tq.grad.numpy()[rows], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy()[cols], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy()[cols], rtol=1e-10, atol=1e-12)
+
+
 def test_backward_invariants():
     q, k, v, do = (_rand(2, 17, 6, seed=s) for s in (48, 49, 50, 51))
     for causal in (False, True):
