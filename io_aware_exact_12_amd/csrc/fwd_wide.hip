@@ -99,6 +99,8 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
   using BTV = BlockTile<DV>;
   constexpr int kKs = D / 16, kDB = DV / 32;
   constexpr int kStage = BT::kBytes + BTV::kBytes;  // K tile, then V tile
+  constexpr int kCopies = BT::kPerWave + BTV::kPerWave;
+  static_assert(kCopies <= 15, "the vmcnt wait holds the copies of one block");
   static_assert(kStages * kStage + kSparseBytes <= 160 * 1024, "the ring and the tile list fit the LDS");
   static_assert(DV == D || !(kWin || kSparse), "d_v != d with plain masks only");
   static_assert(kKs == 16 || kKs == 8 || kKs == 6 || kKs == 4, "slot maps exist for 4, 6, 8 and 16 MFMAs");
@@ -161,22 +163,36 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
   BT::sources(wave, lane, (uint32_t)(2 * in.sn), src);
   BTV::sources(wave, lane, (uint32_t)(2 * lv.sn), src_v);
   const uint32_t lds0 = lds_u32(smem);
-  // copies of block u's K and V rows into its stage: BT::kPerWave +
-  // BTV::kPerWave per wave
-  auto issue = [&](int u) {
-    const int row0 = ks_of(u), left = N - row0;
+  // copies of block u's K and V rows into its stage: kCopies per wave, K's
+  // first.  A block past the last one gets empty buffer ranges: its copies
+  // read nothing and land in the stage that no wave reads any more.
+  struct Copies {
+    i32x4 rk, rv;
+    uint32_t base;
+  };
+  auto prepare = [&](int u, bool real) {
+    const int row0 = ks_of(u), left = real ? N - row0 : 0;
     const uint32_t kbytes =
         left > 0 ? (uint32_t)(left - 1) * (uint32_t)(2 * in.sn) + (uint32_t)T::kDataBytes : 0u;
     const uint32_t vbytes =
         left > 0 ? (uint32_t)(left - 1) * (uint32_t)(2 * lv.sn) + (uint32_t)STile<DV>::kDataBytes : 0u;
-    const i32x4 rk = make_rsrc(k_h + (int64_t)row0 * in.sn, kbytes);
-    const i32x4 rv = make_rsrc(v_h + (int64_t)row0 * lv.sn, vbytes);
-    const uint32_t base = lds0 + (uint32_t)((u & (kStages - 1)) * kStage);
+    Copies cp;
+    cp.rk = make_rsrc(k_h + (int64_t)row0 * in.sn, kbytes);
+    cp.rv = make_rsrc(v_h + (int64_t)row0 * lv.sn, vbytes);
+    cp.base = lds0 + (uint32_t)((u & (kStages - 1)) * kStage);
+    return cp;
+  };
+  auto copy = [&](const Copies& cp, int i) {
+    if (i < BT::kPerWave)
+      dma16(cp.rk, cp.base + (uint32_t)((wave + kW * i) * 1024), src[i]);
+    else
+      dma16(cp.rv, cp.base + (uint32_t)(BT::kBytes + (wave + kW * (i - BT::kPerWave)) * 1024),
+            src_v[i - BT::kPerWave]);
+  };
+  auto issue = [&](int u) {
+    const Copies cp = prepare(u, true);
 #pragma unroll
-    for (int i = 0; i < BT::kPerWave; ++i) dma16(rk, base + (uint32_t)((wave + kW * i) * 1024), src[i]);
-#pragma unroll
-    for (int i = 0; i < BTV::kPerWave; ++i)
-      dma16(rv, base + (uint32_t)(BT::kBytes + (wave + kW * i) * 1024), src_v[i]);
+    for (int i = 0; i < kCopies; ++i) copy(cp, i);
   };
   auto k_tile = [&](int u) { return smem + (u & (kStages - 1)) * kStage; };
   auto v_tile = [&](int u) { return smem + (u & (kStages - 1)) * kStage + BT::kBytes; };
@@ -203,12 +219,20 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
   if (wave_live && u_lo == u_first) s_cur = first_scores(u_first);
 
   for (int u = u_first; u < n_blk; ++u) {
-    const bool more = u + kStages - 1 < n_blk;
-    if (more) issue(u + kStages - 1);  // into the stage block u-1 left
+    // block u+3 goes into the stage block u-1 left.  A wave that computes
+    // block u spreads its copies over the score MFMAs, so that the texture
+    // unit moves them while the matrix cores work; the others issue them at
+    // once.
+    const Copies cp = prepare(u + kStages - 1, u + kStages - 1 < n_blk);
+    const bool busy = wave_live && u >= u_lo && u <= u_last;
+    if (!busy) {
+#pragma unroll
+      for (int i = 0; i < kCopies; ++i) copy(cp, i);
+    }
     // a wave whose window starts after the workgroup's first block forms the
     // scores of its first block from the resident tile
     if (kWin && wave_live && u == u_lo && u_lo > u_first) s_cur = first_scores(u);
-    if (wave_live && u >= u_lo && u <= u_last) {
+    if (busy) {
       const int ks0 = ks_of(u);
       // register rr of lane half g holds key ks0 + 16 (rr >> 3) + 8 g + (rr & 7)
       if (kSparse && ((list[u >> 1] >> (16 + wave / 2)) & 1u) == 0) {
@@ -252,6 +276,9 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
         }
 #pragma unroll
         for (int t = 0; t < kKs; ++t) {
+#pragma unroll
+          for (int i = 0; i < kCopies; ++i)
+            if (t == i * kKs / kCopies) copy(cp, i);
           if constexpr (kNext) {
             s_next = E::mfma(ka[t % kAhead], qf[t], t == 0 ? f32x16{} : s_next);
             if (t + kAhead < kKs) ka[t % kAhead] = row_frag<IsBf16, D>(kt, l32, g, t + kAhead);
@@ -296,9 +323,10 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
       s_cur = s_next;
     }
     // block u+2's tiles must be in LDS for S(u+2) in the next block; the
-    // copies just issued (block u+3) may stay in flight
-    if (more)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (BT::kPerWave + BTV::kPerWave));  // the latest block's copies
+    // copies just issued (block u+3) may stay in flight until then, and all
+    // are done before the last barrier
+    if (u + 1 < n_blk)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kCopies);  // the latest block's copies
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
