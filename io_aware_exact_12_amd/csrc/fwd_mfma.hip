@@ -16,18 +16,25 @@
 //    workgroup per CU, two waves per SIMD.  The grid is (query block,
 //    batch*head) work items, heaviest causal blocks first so the tail of the
 //    launch is short ones.
-//  * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 MFMA: the
-//    K tile is the A operand (read from LDS), Q^T the B operand (held in
-//    registers for the whole loop).  The accumulator then holds one query per
-//    lane column, so the row statistics live in that lane: lanes l and l+32
-//    share a query and split its keys.
-//  * K rows are placed in LDS in a permuted order chosen so that in the S^T
-//    accumulator lane half g holds 8 consecutive keys per 8 registers.  The
-//    probabilities, rounded to the input type, are then directly the B operand
-//    of O^T += V^T P^T with no LDS round trip.  V stays row-major in LDS and its
-//    A operand is gathered with the gfx950 LDS transpose read
-//    (ds_read_b64_tr_b16).  O^T keeps the query in the lane column too, so the
-//    rescale factor and 1/l are per-lane scalars.
+//  * Scores are computed transposed, S^T = K Q^T, with the 16x16x32 MFMA: the
+//    K rows are the A operand (read from LDS), Q^T the B operand (held in
+//    registers for the whole loop).  A wave's 32 queries are two groups of
+//    16, and a 32-key block is four 16 x 16 output tiles (key group, query
+//    group).  The accumulators hold one query per lane column, so lane
+//    16 g + l of the wave holds queries l and 16 + l, each with keys
+//    4 g .. 4 g + 3 of both key groups: four lanes share a query.
+//  * The probabilities of a query group, rounded to the input type, are
+//    directly the B operand of O^T += V^T P^T with no LDS round trip: operand
+//    element 4 h + i of lane group g is key 16 h + 4 g + i, which is where
+//    the score tiles left it.  V stays row-major in LDS and its A operand is
+//    gathered with the gfx950 LDS transpose read (ds_read_b64_tr_b16), four
+//    keys of one d column per read.  O^T keeps the queries in the lane
+//    columns too, so the rescale factors and 1/l are per-lane scalars.
+//  * Why the 16x16x32 shape: for the same products it moves a quarter of the
+//    accumulator data of the 32x32x16 shape per instruction, and the chip,
+//    held at its power limit by this loop, then runs a higher clock.  The
+//    operand reads from LDS per product are the same: each K operand feeds
+//    both query groups and each V operand both query groups.
 //  * K and V tiles are copied HBM -> LDS by buffer loads that write LDS
 //    directly (no register staging); the buffer bounds zero-fill keys past the
 //    end of the sequence.  Every wave issues the same number of copies per
@@ -35,8 +42,9 @@
 //  * Work of a wave is a chain of 32-key blocks.  Block u issues the PV MFMAs
 //    of sub-tile u-1 and the score MFMAs of sub-tile u+1, and spreads the
 //    exponentials of sub-tile u between them, so no MFMA of a block waits for
-//    that block's VALU work.  The K operand of sub-tile u+1 is read from LDS at
-//    the start of block u, the V operand of sub-tile u during its second half.
+//    that block's VALU work.  The K operands of sub-tile u+1 are read from LDS
+//    during the first half of block u, the V operands of sub-tile u during its
+//    second half.
 //  * exp is exp2 with scale*log2(e) folded into one FMA per score.  The
 //    probabilities of a block are taken against the current reference maximum
 //    without first computing the block's own maximum; the block's fp32
@@ -83,12 +91,13 @@ constexpr int kMaskNone = 0, kMaskEdge = 1, kMaskWindow = 2;
 // Block-sparse: a workgroup's list of key tiles (index | query-block bits <<
 // 16, see compact_tiles) lives in LDS after the rings.
 
-// LDS row strides (bytes).  K rows carry 16 bytes of padding: the sixteen
-// lanes of a 16-byte operand read touch sixteen consecutive rows, which then
-// start in sixteen different 4-bank groups.  V rows are read with the transpose
-// read, where each 32-lane half touches four consecutive rows over 32
-// contiguous bytes per 16-lane group; a 64-byte pad puts those four rows in
-// four disjoint 16-bank ranges.  One extra 1 KB slot at the end absorbs the
+// LDS row strides (bytes).  Both carry 32 bytes of padding.  A 16-byte K
+// operand read is served eight lanes of two lane groups at a time (lanes
+// 0-7 with 16-23, and so on, as measured with the bank-conflict counter):
+// eight consecutive rows at two 16-byte chunks, which the pad spreads over
+// all 64 banks.  V rows are read with the transpose read, where each 32-lane
+// half touches eight consecutive rows over the same 32 bytes; the pad puts
+// those eight rows in eight disjoint 8-bank ranges.  One extra 1 KB slot at the end absorbs the
 // copies of waves that have no real chunk for their last copy slot.
 // d = 96 takes the strides of d = 128: they keep both reads conflict-free and
 // split each stage into whole 1 KB copies that the waves share evenly.
@@ -97,8 +106,8 @@ constexpr int kMaskNone = 0, kMaskEdge = 1, kMaskWindow = 2;
 template <int D, int DV = D> struct Lds {
   static constexpr int kRowBytes = 2 * D;    // a K (and Q) row
   static constexpr int kVRowBytes = 2 * DV;  // a V (and O) row
-  static constexpr int kKStride = (D == 96 ? 256 : kRowBytes) + 16;
-  static constexpr int kVStride = (DV == 96 ? 256 : kVRowBytes) + 64;
+  static constexpr int kKStride = (D == 96 ? 256 : kRowBytes) + 32;
+  static constexpr int kVStride = (DV == 96 ? 256 : kVRowBytes) + 32;
   static constexpr int kKStage = kBN * kKStride;  // multiple of 1 KB
   static constexpr int kVStage = kBN * kVStride;  // multiple of 1 KB
   static constexpr int kSink = kStages * (kKStage + kVStage);
@@ -121,9 +130,12 @@ struct FwdBlock {
   using E = Elt<IsBf16>;
   using vec8 = typename E::vec8;
   using L = Lds<D, DV>;
-  static constexpr int kKs = D / 16;   // score MFMAs of one 32x32 block (k-steps over d)
-  static constexpr int kDB = DV / 32;  // 32-row blocks of O^T
-  static constexpr int kPV = 2 * kDB;  // PV MFMAs of one 32-key block
+  // A 32-key block of a wave's 32 queries is four 16 x 16 tiles (key group
+  // kg, query group qg) of the 16x16x32 MFMA.
+  static constexpr int kKf = D / 16;    // K operands of a block: (k-step of 32 d, key group)
+  static constexpr int kVf = DV / 16;   // V^T operands of a block: 16-column d-blocks of O^T
+  static constexpr int kSM = 2 * kKf;   // score MFMAs of a block
+  static constexpr int kPVM = 2 * kVf;  // PV MFMAs of a block
   static constexpr int kRowBytes = L::kRowBytes;
   // HBM -> LDS copies: a K tile is kKLoads and a V tile kVLoads wave-wide
   // 1 KB copies.  Wave w copies K chunks w + 8 i and V chunks w + 8 i of the
@@ -147,7 +159,9 @@ struct FwdBlock {
   uint32_t v_head_bytes, v_row_bytes;  // the same for v
   int64_t o_off;         // this head's first output element, and the output row stride
   int64_t o_sn;
-  int N, win, wave, lane, l32, g, q0, my_q, n_tiles, n_sub;
+  // lane = 16 g + l16: queries q0 + l16 (query group 0) and q0 + 16 + l16
+  // (group 1); keys 4 g .. 4 g + 3 of each 16-key group
+  int N, win, wave, lane, l16, g, q0, my_q, n_tiles, n_sub;
   int u_lo;   // first 32-key block this wave computes (sliding window)
   // block-sparse: the workgroup's key tiles in LDS, their count, and the bit
   // of this wave's 64-row query block in a list entry
@@ -162,14 +176,19 @@ struct FwdBlock {
   uint32_t x_off, x_kmask, x_vmask;
   int k_base, v_base;
 
-  vec8 qf[kKs];       // Q^T B operands: query my_q, d = 16 ks + 8 g + 0..7
-  f32x16 acc[kDB];    // O^T: d = 32 db + 8 (r/4) + 4 g + r%4 of query my_q
-  float m_ref;        // reference maximum the probabilities are taken against
-  float neg_mc;       // -m_ref * c, or kNoRef while m_ref = -inf
-  float l_part;       // this lane half's share of the denominator
-  f32x16 s_cur;       // scores of the block being exponentiated
-  u32x4 p_prev[2];    // probabilities of the previous block (B operands)
-  vec8 vfr[kPV];      // V^T operands of the previous block
+  vec8 qf[kKf];       // Q^T B operands 2 ks + qg: query my_q + 16 qg, d = 32 ks + 8 g + 0..7
+  f32x4 acc[kPVM];    // O^T tile 2 db + qg: d = 16 db + 4 g + 0..3 of query my_q + 16 qg
+  float m_ref[2];     // reference maxima the probabilities are taken against, per query group
+  float neg_mc[2];    // -m_ref * c, or kNoRef while m_ref = -inf
+  float l_part[2];    // this lane's share of the denominators
+  // Scores of a block: tile 2 kg + qg, register i is key 16 kg + 4 g + i of
+  // query my_q + 16 qg.
+  struct Scores {
+    f32x4 t[4];
+  };
+  Scores s_cur;       // scores of the block being exponentiated
+  u32x4 p_prev[2];    // probabilities of the previous block (B operands, per query group)
+  vec8 vfr[kVf];      // V^T operands of the previous block
 
   __device__ __forceinline__ const uint8_t* k_stage(int s) const { return smem + s * L::kKStage; }
   __device__ __forceinline__ const uint8_t* v_stage(int s) const {
@@ -182,8 +201,7 @@ struct FwdBlock {
     const int byte = ci * 1024 + lane * 16;
     const int row = byte / stride, col = byte % stride;
     if (col >= (is_v ? L::kVRowBytes : kRowBytes)) return kNoData;  // row padding
-    return is_v ? (uint32_t)row * v_row_bytes + (uint32_t)col
-                : (uint32_t)k_row_key(row) * row_bytes + (uint32_t)col;
+    return (uint32_t)row * (is_v ? v_row_bytes : row_bytes) + (uint32_t)col;
   }
 
   __device__ __forceinline__ void init(uint8_t* lds, const uint16_t* Q, const uint16_t* K,
@@ -197,8 +215,8 @@ struct FwdBlock {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
-    l32 = lane & 31;
-    g = lane >> 5;
+    l16 = lane & 15;
+    g = lane >> 4;
     const int b = bh / H, h = bh - b * H;
     const int64_t head_off = b * in.sb + h * in.sh;
     row_bytes = (uint32_t)(2 * in.sn);
@@ -212,7 +230,7 @@ struct FwdBlock {
 
     const int q0_blk = qb * kBM;
     q0 = q0_blk + 32 * wave;
-    my_q = q0 + l32;
+    my_q = q0 + l16;
     const int last_blk_row = min(N, q0_blk + kBM) - 1;
     n_tiles = Causal ? (last_blk_row / kBN + 1) : (N + kBN - 1) / kBN;
     // 32-key blocks this wave computes: all of them, or (causal) those whose
@@ -229,11 +247,13 @@ struct FwdBlock {
         (void*)(Q + (b * lq.sb + h * lq.sh)), 0, (int)((uint32_t)(N - 1) * q_row_bytes + kRowBytes),
         kRsrcFlags);
 #pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
+    for (int f = 0; f < kKf; ++f) {
+      const int ks = f >> 1, qg = f & 1;
       u32x4 raw = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(q_rs, (int)((uint32_t)my_q * q_row_bytes) + (2 * ks + g) * 16, 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     q_rs, (int)((uint32_t)(my_q + 16 * qg) * q_row_bytes) + 64 * ks + 16 * g, 0, 0));
       raw ^= q_sign;  // negative scale: flip the sign of q, exactly
-      qf[ks] = __builtin_bit_cast(vec8, raw);
+      qf[f] = __builtin_bit_cast(vec8, raw);
     }
 
 #pragma unroll
@@ -259,36 +279,45 @@ struct FwdBlock {
       src_x = kNoData;
     }
 
-    // K operand reads (A of S^T): LDS row 32 h + l32 of the tile, 16-byte chunk 2 kk + g.
-    k_base = l32 * L::kKStride + g * 16;
-    // V operand reads (A of O^T, transpose reads): for 16-key step t of the
-    // block, d-block db and half hh, lane s of each 16-lane group points at key
-    // 16 t + 8 g + 4 hh + s/4, columns 32 db + 16 (group & 1) + 4 (s & 3) .. +3;
-    // the transpose hands each lane the four keys of its own d column.
-    const int grp = lane >> 4, s16 = lane & 15;
-    v_base = (8 * g + (s16 >> 2)) * L::kVStride + 2 * (16 * (grp & 1) + 4 * (s16 & 3));
+    // K operand reads (A of S^T): for k-step ks and key group kg, LDS row
+    // 16 kg + l16 of the block, 16-byte chunk 4 ks + g.
+    k_base = l16 * L::kKStride + g * 16;
+    // V operand reads (A of O^T, transpose reads): for d-block db and key half
+    // hh, lane l16 of 16-lane group g points at key 16 hh + 4 g + l16 / 4,
+    // columns 16 db + 4 (l16 & 3) .. +3; the transpose hands each lane the four
+    // keys of d column 16 db + l16.  Operand element 4 hh + i then carries key
+    // 16 hh + 4 g + i, the key that score tile (kg = hh) holds in register i.
+    v_base = (4 * g + (l16 >> 2)) * L::kVStride + 8 * (l16 & 3);
 
 #pragma unroll
-    for (int i = 0; i < kDB; ++i) acc[i] = f32x16{};
-    m_ref = -INFINITY;
-    neg_mc = kNoRef;
-    l_part = 0.f;
+    for (int i = 0; i < kPVM; ++i) acc[i] = f32x4{};
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+      m_ref[qg] = -INFINITY;
+      neg_mc[qg] = kNoRef;
+      l_part[qg] = 0.f;
+    }
     if (kWin || kSparse) {
       // A wave whose window starts after the workgroup's first step (or a
       // block-sparse run) begins with a normal block: zeros make its PV MFMAs
       // add 0, and kNoRef sends it down the reference-update path.
-      s_cur = f32x16{};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_cur.t[i] = f32x4{};
       p_prev[0] = p_prev[1] = u32x4{};
 #pragma unroll
-      for (int i = 0; i < kPV; ++i) vfr[i] = vec8{};
+      for (int i = 0; i < kVf; ++i) vfr[i] = vec8{};
     }
   }
 
-  // Copy K tile jk into K stage sk and V tile jv into V stage sv (a tile at
-  // or past n_tiles copies zeros: its buffer is empty).  Every wave issues
-  // exactly kCopies copies, in one asm statement that saves and restores M0
-  // once.
-  __device__ __forceinline__ void load_tiles(int jk, int sk, int jv, int sv) const {
+  // Copies of K tile jk into K stage sk and V tile jv into V stage sv (a tile
+  // at or past n_tiles copies zeros: its buffer is empty): buffer ranges and
+  // LDS destinations, all wave-uniform.  Every wave issues exactly kCopies
+  // copies, either at once (load_tiles) or one by one (copy_one).
+  struct Copies {
+    i32x4 tk, tv, tx;
+    uint32_t k_st, v_st, x_lds;
+  };
+  __device__ __forceinline__ Copies prepare_tiles(int jk, int sk, int jv, int sv) const {
     const uint32_t tile_bytes = kBN * row_bytes, v_tile_bytes = kBN * v_row_bytes;
     const uint32_t k_left = jk < n_tiles ? head_bytes - (uint32_t)jk * tile_bytes : 0u;
     const uint32_t v_left = jv < n_tiles ? v_head_bytes - (uint32_t)jv * v_tile_bytes : 0u;
@@ -300,11 +329,28 @@ struct FwdBlock {
     for (int w = 0; w < 4; ++w)
       tx[w] = __builtin_amdgcn_readfirstlane((int)(((uint32_t)tk[w] & ~x_vmask) | ((uint32_t)tv[w] & x_vmask)));
     const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)smem + (uint32_t)(wave * 1024);
-    const uint32_t k_st = base + (uint32_t)(sk * L::kKStage);
-    const uint32_t v_st = base + (uint32_t)(kStages * L::kKStage + sv * L::kVStage);
+    const uint32_t k_st = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + (uint32_t)(sk * L::kKStage)));
+    const uint32_t v_st = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(base + (uint32_t)(kStages * L::kKStage + sv * L::kVStage)));
     const uint32_t x_lds = (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)((uint32_t)(uintptr_t)(lds_void*)smem + x_off + ((uint32_t)(sk * L::kKStage) & x_kmask) +
               ((uint32_t)(kStages * L::kKStage + sv * L::kVStage) & x_vmask)));
+    return Copies{tk, tv, tx, k_st, v_st, x_lds};
+  }
+  // Copy i of a prepared set: K chunks first, then V chunks, then the extra one.
+  __device__ __forceinline__ void copy_one(const Copies& cp, int i) const {
+    if (i < kFullK)
+      dma16(cp.tk, cp.k_st + (uint32_t)(i * kWaves * 1024), src_k[i]);
+    else if (i < kFullK + kFullV)
+      dma16(cp.tv, cp.v_st + (uint32_t)((i - kFullK) * kWaves * 1024), src_v[i - kFullK]);
+    else
+      dma16(cp.tx, cp.x_lds, src_x);
+  }
+  // All copies at once, in one asm statement that saves and restores M0 once.
+  __device__ __forceinline__ void load_tiles(int jk, int sk, int jv, int sv) const {
+    const Copies cp = prepare_tiles(jk, sk, jv, sv);
+    const i32x4 &tk = cp.tk, &tv = cp.tv, &tx = cp.tx;
+    const uint32_t k_st = cp.k_st, v_st = cp.v_st, x_lds = cp.x_lds;
     if constexpr (kFullK == 2 && kFullV == 2)
       dma_group5(tk, tv, tx, k_st, k_st + kWaves * 1024, v_st, v_st + kWaves * 1024, x_lds,
                  src_k[0], src_k[1], src_v[0], src_v[1], src_x);
@@ -334,12 +380,12 @@ struct FwdBlock {
     return kSparse ? kBN * tile_at(u >> 1) + 32 * (u & 1) : 32 * u;
   }
 
-  // Hide keys of block u that this lane's query may not see: the causal
-  // diagonal and the sequence end; with kMaskWindow also keys left of the
+  // Hide keys of block u that this lane's queries may not see: the causal
+  // diagonal and the sequence end; with kMaskWindow also keys left of a
   // query's sliding window.
   template <int kMask>
-  __device__ __forceinline__ void apply_mask(int u, f32x16& st) const {
-    // register r of lane half g holds key kpos(u) + 16 (r >> 3) + 8 g + (r & 7)
+  __device__ __forceinline__ void apply_mask(int u, Scores& st) const {
+    // tile 2 kg + qg, register i holds key kpos(u) + 16 kg + 4 g + i of query my_q + 16 qg
     const int k0 = kpos(u);
     // Wave-uniform: a block whose keys every row of the wave sees (none past
     // the first row's diagonal or the sequence end, none left of the last
@@ -349,73 +395,101 @@ struct FwdBlock {
     const bool cut_right = k0 + 31 > (Causal ? min(q0, N - 1) : N - 1);
     const bool cut_left = kMask == kMaskWindow && kWin && k0 <= q0 + 31 - win;
     if (!cut_right && !cut_left) return;
-    const int lim = (Causal ? min(my_q, N - 1) : N - 1) - k0 - 8 * g;
-    const int lo = my_q - win + 1 - k0 - 8 * g;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int o = 16 * (r >> 3) + (r & 7);
-      const bool hide = (kMask == kMaskWindow && kWin) ? (o > lim || o < lo) : o > lim;
-      st[r] = hide ? -INFINITY : st[r];
+    for (int qg = 0; qg < 2; ++qg) {
+      const int q = my_q + 16 * qg;
+      const int lim = (Causal ? min(q, N - 1) : N - 1) - k0 - 4 * g;
+      const int lo = q - win + 1 - k0 - 4 * g;
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int o = 16 * kg + i;
+          const bool hide = (kMask == kMaskWindow && kWin) ? (o > lim || o < lo) : o > lim;
+          st.t[2 * kg + qg][i] = hide ? -INFINITY : st.t[2 * kg + qg][i];
+        }
     }
   }
 
-  // Probabilities of scores 2e, 2e+1 against the current reference, packed
-  // into the B operand and added (in fp32) to a partial row sum.
-  __device__ __forceinline__ void exp_pair(const f32x16& st, int e, u32x4 (&pw)[2], float& sum) const {
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * e], c, neg_mc));
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * e + 1], c, neg_mc));
-    pw[e >> 2][e & 3] = E::pack2(p0, p1);
-    sum += p0 + p1;
+  // Score pair e of a block: registers 2 (e & 1), +1 of tile e >> 1, which is
+  // key group e >> 2 of query group (e >> 1) & 1.  In that query group's B
+  // operand the pair is 32-bit slot 2 (e >> 2) + (e & 1).
+  static constexpr int pair_qg(int e) { return (e >> 1) & 1; }
+  static constexpr int pair_slot(int e) { return 2 * (e >> 2) + (e & 1); }
+
+  // Probabilities of score pair e against the current reference, packed into
+  // the B operand and added (in fp32) to the query group's partial row sum.
+  __device__ __forceinline__ void exp_pair(const Scores& st, int e, u32x4 (&pw)[2], float (&sum)[2]) const {
+    const int qg = pair_qg(e), tt = e >> 1, i = 2 * (e & 1);
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st.t[tt][i], c, neg_mc[qg]));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st.t[tt][i + 1], c, neg_mc[qg]));
+    pw[qg][pair_slot(e)] = E::pack2(p0, p1);
+    sum[qg] += p0 + p1;
   }
 
-  // Raise the reference to the running maximum over the scores st (both lane
-  // halves), rescale a and l, and leave neg_mc matching.
-  __device__ __forceinline__ void raise_reference(const f32x16& st) {
-    float mx = st[0];
+  // Raise each query's reference to its running maximum over the scores st
+  // (all four lanes of the query), rescale a and l, and leave neg_mc matching.
+  __device__ __forceinline__ void raise_reference(const Scores& st) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
-    const float m_new = fmaxf(m_ref, xhalf_max(mx));
-    const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
-    m_ref = m_new;
-    neg_mc = (m_new == -INFINITY) ? kNoRef : -m_new * c;
-    l_part *= alpha;
+    for (int qg = 0; qg < 2; ++qg) {
+      float mx = st.t[qg][0];
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) acc[db] *= alpha;
+      for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st.t[2 * kg + qg][i]);
+      const float m_new = fmaxf(m_ref[qg], quad_max(mx));
+      const float alpha = (m_ref[qg] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_ref[qg] - m_new) * c);
+      m_ref[qg] = m_new;
+      neg_mc[qg] = (m_new == -INFINITY) ? kNoRef : -m_new * c;
+      l_part[qg] *= alpha;
+#pragma unroll
+      for (int db = 0; db < kVf; ++db) acc[2 * db + qg] *= alpha;
+    }
+  }
+
+  // K operand r = 2 ks + kg of the block whose 32 K rows start at kt.
+  static __device__ __forceinline__ vec8 k_operand(const uint8_t* kt, int r) {
+    return *reinterpret_cast<const vec8*>(kt + (r & 1) * 16 * L::kKStride + (r >> 1) * 64);
   }
 
   // Scores of block u (K tile u/2, half u&1, still resident in LDS during the
   // tile step that holds block u), masked when kMask.
   template <int kMask>
-  __device__ __forceinline__ f32x16 scores(int u) const {
+  __device__ __forceinline__ Scores scores(int u) const {
     const uint8_t* kt = k_stage((u >> 1) & 3) + k_base + (u & 1) * 32 * L::kKStride;
-    f32x16 st = f32x16{};
+    Scores st;
 #pragma unroll
-    for (int kk = 0; kk < kKs; ++kk)
-      st = E::mfma(*reinterpret_cast<const vec8*>(kt + kk * 32), qf[kk], st);
+    for (int i = 0; i < 4; ++i) st.t[i] = f32x4{};
+#pragma unroll
+    for (int r = 0; r < kKf; ++r) {
+      const vec8 kf = k_operand(kt, r);
+      const int ks = r >> 1, kg = r & 1;
+#pragma unroll
+      for (int qg = 0; qg < 2; ++qg) st.t[2 * kg + qg] = E::mfma16(kf, qf[2 * ks + qg], st.t[2 * kg + qg]);
+    }
     if (kMask != kMaskNone) apply_mask<kMask>(u, st);
     return st;
   }
 
-  // MFMA slot of step st (0 scale, 1 exp2, 2 pack and partial sum) of score
-  // pair e, for blocks of 16, 14, 12 (d = 96), 10, 8, 6 or 4 MFMA slots.  Steps that
-  // land in the same slot run in program order.
+  // MFMA slot of step st of score pair e among a block's kSlots MFMAs: 0
+  // scales both scores, 1 and 2 take the exp2 of the first and the second, 3
+  // packs them and adds them to the partial sum.  The pairs spread evenly
+  // over the block; in blocks of 24 or more MFMAs each exp2 (a quarter-rate
+  // instruction) has a slot of its own and the pack waits two slots for the
+  // second.  Steps that land in the same slot run in program order.
   template <int kSlots>
   static constexpr int slot_of(int e, int st) {
-    return kSlots == 16 ? e + (st == 0 ? 0 : st == 1 ? 2 : 5)
-         : kSlots == 14 ? (7 * e) / 8 + (st == 0 ? 0 : st == 1 ? 2 : 5)
-         : kSlots == 12 ? (3 * e) / 4 + (st == 0 ? 0 : st == 1 ? 2 : 4)
-         : kSlots == 10 ? (5 * e) / 8 + (st == 0 ? 0 : st == 1 ? 2 : 4)
-         : (kSlots == 8 || kSlots == 6) ? e / 2 + st
-                        : (e / 4 + st < 3 ? e / 4 + st : 3);
+    constexpr bool kWide = kSlots >= 24;
+    const int at = (e * kSlots) / 8 + (st == 0 ? 0 : st == 1 ? 1 : st == 2 ? (kWide ? 2 : 1) : (kWide ? 4 : 2));
+    return at < kSlots ? at : kSlots - 1;
   }
 
   // Block u: PV MFMAs of block u-1 (none if kFirst), score MFMAs of block u+1,
   // and between them the probabilities of block u.  On entry s_cur holds the
-  // scores of block u, p_prev / vfr the operands of block u-1.  The K operand
-  // read for score MFMA i is issued right after PV MFMA i, the V operand read
-  // for next block's PV MFMA i right after score MFMA i: every operand is read
-  // a full phase before its use, and each read reuses the registers of the
-  // operand the preceding MFMA just consumed.  On a wave's last block the
+  // scores of block u, p_prev / vfr the operands of block u-1.  The K operands
+  // of block u+1 are read from LDS during the PV MFMAs, the V operands of
+  // block u (for the next block's PV MFMAs) during the score MFMAs: every
+  // operand is read a full phase before its use.  On a wave's last block the
   // scores of "block u+1" are still formed from whatever the K stage holds and
   // never used, so every block runs the same code.
   //
@@ -427,101 +501,108 @@ struct FwdBlock {
   // p_prev = vfr = 0 make its PV MFMAs add 0.
   //
   // kHalf (0 or 1) is the block's place in its tile step; it sets the wave's
-  // issue priority (see step()).
-  template <int kMask, bool kFirst = false, int kHalf = 0>
-  __device__ __forceinline__ void block(int u) {
-    constexpr int kMfmas = (kFirst ? 0 : kPV) + kKs;
-    static_assert(kMfmas == 16 || kMfmas == 14 || kMfmas == 12 || kMfmas == 10 || kMfmas == 8 ||
-                      kMfmas == 6 || kMfmas == 4,
-                  "slot schedules exist for 4, 6, 8, 10, 12, 14 and 16 MFMAs");
-    auto slot = [](int e, int st) { return slot_of<kMfmas>(e, st); };
-    // K operand of block u+1: K tile (u+1)/2, half (u+1)&1
+  // issue priority (see step()).  With kCopy the block also issues the tile
+  // step's copies *cp, spread over its MFMA slots.
+  template <int kMask, bool kFirst = false, int kHalf = 0, bool kCopy = false>
+  __device__ __forceinline__ void block(int u, const Copies* cp = nullptr) {
+    constexpr int kMfmas = (kFirst ? 0 : kPVM) + kSM;
+    static_assert(kMfmas >= 8 && kMfmas <= 32, "a block holds 8 to 32 MFMAs");
+    // K operands of block u+1: K tile (u+1)/2, half (u+1)&1
     const uint8_t* kt = k_stage(((u + 1) >> 1) & 3) + k_base + ((u + 1) & 1) * 32 * L::kKStride;
-    // V operand of block u (for the next block's PV MFMAs): V tile u/2, half u&1.
+    // V operands of block u (for the next block's PV MFMAs): V tile u/2, half u&1.
     // The stage offset is hidden from the compiler (an empty asm on an SGPR)
     // so that it is not folded into the reads' constant offsets: past 64 KB
     // they no longer fit the 16-bit LDS offset field and every read would
     // need an address add of its own.
-    uint32_t v_off = kStages * L::kKStage + ((u >> 1) & 3) * L::kVStage + (u & 1) * 32 * L::kVStride;
+    uint32_t v_off = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(kStages * L::kKStage + ((u >> 1) & 3) * L::kVStage + (u & 1) * 32 * L::kVStride));
     asm("" : "+s"(v_off));
     const uint8_t* vt = smem + v_off + v_base;
-    vec8 kfr[kKs];
+    vec8 kfr[kKf];
     if (kFirst) {
 #pragma unroll
-      for (int i = 0; i < kKs; ++i) kfr[i] = *reinterpret_cast<const vec8*>(kt + i * 32);
+      for (int r = 0; r < kKf; ++r) kfr[r] = k_operand(kt, r);
     }
     if (kMask != kMaskNone) apply_mask<kMask>(u, s_cur);
     if (kFirst) raise_reference(s_cur);  // the first block sets the reference outright
 
     u32x4 pw[2];
-    float sum[2];  // partial row sums of even and odd score pairs
-    f32x16 s_next;
+    float sum[2];  // partial row sums of the two query groups
+    Scores s_next;
     float pr[16];  // scaled scores, then probabilities
-#pragma unroll
-    for (int t = 0; t < kMfmas; ++t) {
-      if (!kFirst && t < kPV) {
-        // PV order 0, 2, 4, .., 1, 3, ..: no two adjacent MFMAs share an
-        // accumulator, and the operands of the second key half come last
-        const int f = (t < kPV / 2) ? 2 * t : 2 * (t - kPV / 2) + 1;
-        acc[f >> 1] = E::mfma(vfr[f], __builtin_bit_cast(vec8, p_prev[f & 1]), acc[f >> 1]);
-        // K operands r = t, t + kPV, ..: all are read in the PV phase
-#pragma unroll
-        for (int r = t; r < kKs; r += kPV) kfr[r] = *reinterpret_cast<const vec8*>(kt + r * 32);
+    static_for<kMfmas>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      if constexpr (!kFirst && t < kPVM) {
+        // PV MFMA t: d-block t / 2, query group t & 1 (adjacent MFMAs never
+        // share an accumulator, and share the V operand)
+        acc[t] = E::mfma16(vfr[t >> 1], __builtin_bit_cast(vec8, p_prev[t & 1]), acc[t]);
+        static_for<kKf>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          if constexpr ((r * kPVM) / kKf == t) kfr[r] = k_operand(kt, r);
+        });
       } else {
-        const int i = kFirst ? t : t - kPV;  // score k-step
-        s_next = E::mfma(kfr[i], qf[i], i == 0 ? f32x16{} : s_next);
-        // V^T operands f = i, i + kKs, .. of block u: two transpose reads each
-#pragma unroll
-        for (int f = i; f < kPV; f += kKs) {
-          const int db = f >> 1, tt = f & 1;
-          const uint8_t* vp = vt + 16 * tt * L::kVStride + 64 * db;
-          const auto lo = E::read_tr((const lds_void*)vp);
-          const auto hi = E::read_tr((const lds_void*)(vp + 4 * L::kVStride));
-          vfr[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+        // score MFMA i: k-step i / 4 of tile i & 3 (key group, query group)
+        constexpr int i = kFirst ? t : t - kPVM;
+        constexpr int ks = i >> 2, tile = i & 3, kg = tile >> 1, qg = tile & 1;
+        s_next.t[tile] = E::mfma16(kfr[2 * ks + kg], qf[2 * ks + qg], ks == 0 ? f32x4{} : s_next.t[tile]);
+        // V^T operand f of block u: d-block f, two transpose reads (key halves)
+        static_for<kVf>([&](auto fc) {
+          constexpr int f = decltype(fc)::value;
+          if constexpr ((f * kSM) / kVf == i) {
+            const uint8_t* vp = vt + 32 * f;
+            const auto lo = E::read_tr((const lds_void*)vp);
+            const auto hi = E::read_tr((const lds_void*)(vp + 16 * L::kVStride));
+            vfr[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+        });
+      }
+      // the tile step's copies, spread over the block's MFMA slots
+      if constexpr (kCopy) {
+        static_for<kCopies>([&](auto ic) {
+          constexpr int ci = decltype(ic)::value;
+          if constexpr (t == ci * kMfmas / kCopies) copy_one(*cp, ci);
+        });
       }
       // Probabilities of the 8 score pairs, software-pipelined so that each
-      // step of a pair (scale, exp2, then pack and fp32 partial sum) runs a
-      // few MFMA slots after the step it depends on and never stalls the
-      // wave's in-order issue.
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (t == slot(e, 0)) {
-          pr[2 * e] = __builtin_fmaf(s_cur[2 * e], c, neg_mc);
-          pr[2 * e + 1] = __builtin_fmaf(s_cur[2 * e + 1], c, neg_mc);
+      // step of a pair (scale, exp2 of each score, then pack and fp32 partial
+      // sum) runs a slot or more after the step it depends on and never
+      // stalls the wave's in-order issue.
+      static_for<8>([&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        constexpr int qg = pair_qg(e), tt = e >> 1, ir = 2 * (e & 1);
+        if constexpr (t == slot_of<kMfmas>(e, 0)) {
+          pr[2 * e] = __builtin_fmaf(s_cur.t[tt][ir], c, neg_mc[qg]);
+          pr[2 * e + 1] = __builtin_fmaf(s_cur.t[tt][ir + 1], c, neg_mc[qg]);
         }
-        if (t == slot(e, 1)) {
-          pr[2 * e] = __builtin_amdgcn_exp2f(pr[2 * e]);
-          pr[2 * e + 1] = __builtin_amdgcn_exp2f(pr[2 * e + 1]);
-        }
-        if (t == slot(e, 2)) {
-          pw[e >> 2][e & 3] = E::pack2(pr[2 * e], pr[2 * e + 1]);
+        if constexpr (t == slot_of<kMfmas>(e, 1)) pr[2 * e] = __builtin_amdgcn_exp2f(pr[2 * e]);
+        if constexpr (t == slot_of<kMfmas>(e, 2)) pr[2 * e + 1] = __builtin_amdgcn_exp2f(pr[2 * e + 1]);
+        if constexpr (t == slot_of<kMfmas>(e, 3)) {
+          pw[qg][pair_slot(e)] = E::pack2(pr[2 * e], pr[2 * e + 1]);
           const float pair = pr[2 * e] + pr[2 * e + 1];
-          sum[e & 1] = e < 2 ? pair : sum[e & 1] + pair;
+          sum[qg] = (e & 5) == 0 ? pair : sum[qg] + pair;  // pairs 0 and 2 come first in their group
         }
-      }
+      });
       // half way through the block the wave's priority steps down
-      if (t == kMfmas / 2 - 1) __builtin_amdgcn_s_setprio(kHalf == 0 ? 2 : 0);
+      if constexpr (t == kMfmas / 2 - 1) __builtin_amdgcn_s_setprio(kHalf == 0 ? 2 : 0);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     // Keep the packing inside the MFMA stream: the reference-update path below
     // overwrites pw, and without this use the compiler sinks the conversions
     // past its branch, right in front of the next block's first PV MFMA.
     asm volatile("" ::"v"(pw[0]), "v"(pw[1]));
-    float s_tot = sum[0] + sum[1];
-    if (!kFirst && __builtin_amdgcn_ballot_w64(s_tot > kSumCap<IsBf16>) != 0) {
+    if (!kFirst &&
+        __builtin_amdgcn_ballot_w64(sum[0] > kSumCap<IsBf16> || sum[1] > kSumCap<IsBf16>) != 0) {
       // rare: some probability of this block may exceed the cap (or a row
       // sees its first key).  The scores are formed again from LDS rather
       // than kept live through the block.
-      const f32x16 st = scores<kMask>(u);
+      const Scores st = scores<kMask>(u);
       raise_reference(st);
-      s_tot = 0.f;
-      float s2 = 0.f;
+      sum[0] = sum[1] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) exp_pair(st, e, pw, (e & 1) ? s2 : s_tot);
-      s_tot += s2;
+      for (int e = 0; e < 8; ++e) exp_pair(st, e, pw, sum);
     }
-    l_part += s_tot;
+    l_part[0] += sum[0];
+    l_part[1] += sum[1];
     p_prev[0] = pw[0];
     p_prev[1] = pw[1];
     s_cur = s_next;
@@ -531,8 +612,8 @@ struct FwdBlock {
   // PV MFMAs of the wave's last block.
   __device__ __forceinline__ void drain() {
 #pragma unroll
-    for (int t = 0; t < kPV; ++t)
-      acc[t >> 1] = E::mfma(vfr[t], __builtin_bit_cast(vec8, p_prev[t & 1]), acc[t >> 1]);
+    for (int t = 0; t < kPVM; ++t)
+      acc[t] = E::mfma16(vfr[t >> 1], __builtin_bit_cast(vec8, p_prev[t & 1]), acc[t]);
   }
 
   // Tile step j: blocks 2j and 2j+1.  They read K tiles j (second half) and
@@ -553,8 +634,13 @@ struct FwdBlock {
   template <int kMask, bool kFirstStep = false>
   __device__ __forceinline__ void step(int j) {
     __builtin_amdgcn_s_setprio(3);
-    load_tiles(j + 3, (j + 3) & 3, j + 2, (j + 2) & 3);
+    // block 2j spreads the step's copies over its MFMAs, so that the texture
+    // unit moves them while the matrix cores work; a wave that does not
+    // compute that block issues them at once
+    const Copies cp = prepare_tiles(j + 3, (j + 3) & 3, j + 2, (j + 2) & 3);
     if (kFirstStep) {
+#pragma unroll
+      for (int i = 0; i < kCopies; ++i) copy_one(cp, i);
       if (u_lo == 2 * j && u_lo < n_sub) block<kMask, true, 0>(2 * j);
       if (u_lo == 2 * j + 1 && u_lo < n_sub)
         block<kMask, true, 1>(2 * j + 1);
@@ -562,7 +648,12 @@ struct FwdBlock {
         block<kMask, false, 1>(2 * j + 1);
     } else {
       const int u = 2 * j;
-      if (u >= u_lo && u < n_sub) block<kMask, false, 0>(u);
+      if (u >= u_lo && u < n_sub) {
+        block<kMask, false, 0, true>(u, &cp);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kCopies; ++i) copy_one(cp, i);
+      }
       if (u + 1 >= u_lo && u + 1 < n_sub) block<kMask, false, 1>(u + 1);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -670,23 +761,25 @@ struct FwdBlock {
   // that see no key store O = 0 and LSE = -inf.
   __device__ __forceinline__ void store(uint16_t* O, float* LSE, int bh) {
     if (!kSparse && n_sub <= u_lo) return;
-    const float l_tot = xhalf_sum(l_part);
-    const float inv = (!kSparse || l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-    if (my_q >= N) return;
-    uint16_t* orow = O + o_off + (int64_t)my_q * o_sn;
     typedef __attribute__((ext_vector_type(4))) typename E::scalar h4_t;
 #pragma unroll
-    for (int db = 0; db < kDB; ++db)
+    for (int qg = 0; qg < 2; ++qg) {
+      const float l_tot = quad_sum(l_part[qg]);
+      const float inv = (!kSparse || l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+      const int q = my_q + 16 * qg;
+      if (q < N) {
+        uint16_t* orow = O + o_off + (int64_t)q * o_sn;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const f32x4 v4 = {acc[db][4 * gq] * inv, acc[db][4 * gq + 1] * inv,
-                          acc[db][4 * gq + 2] * inv, acc[db][4 * gq + 3] * inv};
-        const auto h4 = __builtin_convertvector(v4, h4_t);
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * gq + 4 * g) = __builtin_bit_cast(u32x2, h4);
+        for (int db = 0; db < kVf; ++db) {
+          const f32x4 v4 = acc[2 * db + qg] * inv;
+          const auto h4 = __builtin_convertvector(v4, h4_t);
+          *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * g) = __builtin_bit_cast(u32x2, h4);
+        }
+        if (LSE != nullptr && g == 0)
+          LSE[(int64_t)bh * N + q] =
+              ((m_ref[qg] == -INFINITY ? 0.f : m_ref[qg] * c) + __builtin_amdgcn_logf(l_tot)) * kLn2;
       }
-    if (LSE != nullptr && g == 0)
-      LSE[(int64_t)bh * N + my_q] =
-          ((m_ref == -INFINITY ? 0.f : m_ref * c) + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
   }
 };
 

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <type_traits>
+#include <utility>
 
 namespace fa {
 namespace mfma {
@@ -135,6 +137,19 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 
 template <bool V> struct BoolTag { static constexpr bool value = V; };
 
+// f(std::integral_constant<int, 0>{}), .., f(std::integral_constant<int, N-1>{}):
+// a loop whose index is a compile-time constant in every iteration, unrolled
+// by construction (a long unrolled schedule must not fall back to a runtime
+// loop with dynamically indexed register arrays).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <bool IsBf16> struct Elt;
 template <> struct Elt<true> {
   using scalar = __bf16;
@@ -147,6 +162,9 @@ template <> struct Elt<true> {
   using vec4 = bf16x4;
   static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ vec4 read_tr(const lds_void* p) {
     return __builtin_bit_cast(vec4, read_tr16(p));
@@ -163,6 +181,9 @@ template <> struct Elt<false> {
   using vec4 = f16x4;
   static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ vec4 read_tr(const lds_void* p) {
     return __builtin_bit_cast(vec4, read_tr16(p));
@@ -190,6 +211,19 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
                                                   __builtin_bit_cast(uint32_t, x), false, false);
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+// The same over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (v_permlane16_swap
+// pairs lanes l and l ^ 16).  Max and sum are commutative, so all four lanes
+// get bitwise the same result.
+__device__ __forceinline__ float quad_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return xhalf_max(fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return xhalf_sum(__builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 
 // Kernel modes: plain (causal or not), causal sliding window, block-sparse.
