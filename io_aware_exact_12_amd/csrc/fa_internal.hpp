@@ -82,6 +82,9 @@ inline bool dv_pair_built(int64_t d, int64_t dv) {
 // Launchers return the hipError_t of the launch (hipSuccess when enqueued).
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s);
+// d = d_v = 64 (fwd_mfma64.hip)
+hipError_t launch_fwd64_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd64_f16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 // Tail rows r0 .. N-1 (at most 32) of an unmasked bf16 / fp16 forward with
 // d_v = d in {64, 96, 128}: one workgroup per head, keys split over its waves.

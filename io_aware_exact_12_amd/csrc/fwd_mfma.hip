@@ -859,7 +859,9 @@ hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
     return a.dv == 96 ? launch_dv<IsBf16, 64, 96>(a, s) : launch_dv<IsBf16, 64, 128>(a, s);
   }
   if (a.d == 128) return dispatch_d<IsBf16, 128>(a, s);
-  return a.d == 96 ? dispatch_d<IsBf16, 96>(a, s) : dispatch_d<IsBf16, 64>(a, s);
+  if (a.d == 96) return dispatch_d<IsBf16, 96>(a, s);
+  // d = d_v = 64: the 32x32x16 kernel (see fwd_mfma64.hip)
+  return IsBf16 ? launch_fwd64_bf16(a, s) : launch_fwd64_f16(a, s);
 }
 
 }  // namespace
