@@ -55,11 +55,19 @@ def progress(msg):
     print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
+def code_of(text: str) -> str:
+    """A C++ source without its comments and blank lines, so that a comment edit
+    leaves the kernel's identity unchanged."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "io_aware_exact_12_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "io_aware_exact_12_amd", "csrc", f)) as fh:
+            h.update(code_of(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

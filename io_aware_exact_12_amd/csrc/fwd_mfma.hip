@@ -38,7 +38,8 @@
 //  * K and V tiles are copied HBM -> LDS by buffer loads that write LDS
 //    directly (no register staging); the buffer bounds zero-fill keys past the
 //    end of the sequence.  Every wave issues the same number of copies per
-//    tile step, so the copy code has no branches.
+//    tile step, so the waits on them are constants; a wave that computes the
+//    step's first block issues them between that block's MFMAs.
 //  * Work of a wave is a chain of 32-key blocks.  Block u issues the PV MFMAs
 //    of sub-tile u-1 and the score MFMAs of sub-tile u+1, and spreads the
 //    exponentials of sub-tile u between them, so no MFMA of a block waits for
@@ -71,7 +72,7 @@ constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kStages = 4;        // LDS ring depth of the K and of the V tiles
 constexpr int kBN = 64;           // keys per tile
 constexpr int kThreads = 64 * kWaves;
-// A block whose partial row sum (16 probabilities of one lane half) exceeds
+// A block whose partial row sum (the 8 probabilities of one query in one lane) exceeds
 // the cap moves the reference maximum, so every probability stays below it:
 // 2^15 for fp16, whose P operand reaches 65504, and 2^24 for bf16, which has
 // the fp32 exponent range.  The probabilities' relative precision does not
