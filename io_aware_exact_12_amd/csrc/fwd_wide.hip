@@ -17,9 +17,11 @@
 //   [S(u+1) = K Q^T, 16 MFMAs] with the exp2, packing and row sums of P(u)
 //                                 placed between them,
 //   [O^T += V^T P^T of block u, 16 MFMAs].
-// The reference maximum only moves when a block's maximum exceeds it by more
-// than kLazy (log2 units): probabilities stay below 2^kLazy and the rescale of
-// the 128 accumulators is rare.  The result does not depend on the reference,
+// A block's probabilities are taken against the current reference maximum
+// without first computing the block's own maximum; only when a lane's partial
+// row sum exceeds kSumCap (so some probability may) is the reference raised
+// to the running maximum, the 128 accumulators rescaled and the block's
+// probabilities formed again.  The result does not depend on the reference,
 // which cancels between numerator and denominator.
 #include <hip/hip_runtime.h>
 #include <cstdint>
@@ -36,9 +38,14 @@ using namespace mfma;
 using namespace tiles;
 
 constexpr float kLn2 = 0.6931471805599453f;
-// 2^15 for fp16 (its P operand reaches 65504), 2^24 for bf16 (fp32 exponent
-// range; bounds |V| by about 2^104 / N so that the fp32 numerator sum stays finite)
-template <bool IsBf16> constexpr float kLazy = IsBf16 ? 24.f : 15.f;
+// Cap on a lane's partial row sum of a block (16 probabilities): 2^15 for
+// fp16 (its P operand reaches 65504), 2^24 for bf16 (fp32 exponent range;
+// bounds |V| by about 2^104 / N so that the fp32 numerator sum stays finite)
+template <bool IsBf16> constexpr float kSumCap = IsBf16 ? 16777216.0f : 32768.0f;
+// Exponent offset of a row with no reference yet (every key seen so far
+// hidden): a visible score then gives probability +inf, so the partial sum
+// passes the cap and the block sets the reference; a hidden one gives 0.
+constexpr float kNoRef = 1e30f;
 constexpr int kB = 32;       // keys per block (one streamed tile)
 constexpr int kStages = 4;
 constexpr int kAhead = 2;    // LDS operand reads issued this many MFMAs before their use
@@ -201,6 +208,7 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
 #pragma unroll
   for (int i = 0; i < kDB; ++i) acc[i] = f32x16{};
   float m = -INFINITY;  // reference: raw (sign-adjusted) score of this lane's query
+  float neg_mc = kNoRef;  // -m * c, or kNoRef while m = -inf
   float l = 0.f;        // this lane half's share of the row sum, relative to m
   f32x16 s_cur = f32x16{}, s_next = f32x16{};
 
@@ -245,21 +253,6 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
           if (kj >= N || (Causal && kj > my_q) || (kWin && kj <= my_q - win)) s_cur[rr] = -INFINITY;
         }
       }
-      float mx = s_cur[0];
-#pragma unroll
-      for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, s_cur[rr]);
-      mx = xhalf_max(mx);
-      // (-inf) - (-inf) is NaN and compares false: a row that has seen no key
-      // yet keeps its reference until a block shows it one
-      if (__builtin_amdgcn_ballot_w64((mx - m) * c > kLazy<IsBf16>) != 0) {
-        const float m_new = fmaxf(m, mx);
-        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) acc[db] *= alpha;
-        m = m_new;
-      }
-      const float neg_mc = m == -INFINITY ? 0.f : -m * c;
 
       // S(u+1) with P(u) between its MFMAs; a wave's last block forms no S
       // (two copies of the loop, so that no branch sits between the MFMAs)
@@ -305,6 +298,33 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
         phase_a(std::true_type{});
       else
         phase_a(std::false_type{});
+      // Keep the packing inside the MFMA stream (the rare path below
+      // overwrites pw; without this use the compiler sinks the conversions
+      // past its branch).
+      asm volatile("" ::"v"(pw[0]), "v"(pw[1]));
+      if (__builtin_amdgcn_ballot_w64(sum[0] + sum[1] > kSumCap<IsBf16>) != 0) {
+        // rare: raise the reference to the running maximum over both lane
+        // halves, rescale l and a, and take this block's probabilities again.
+        // A row whose block shows no key keeps m = -inf and kNoRef.
+        float mx = s_cur[0];
+#pragma unroll
+        for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, s_cur[rr]);
+        const float m_new = fmaxf(m, xhalf_max(mx));
+        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) acc[db] *= alpha;
+        m = m_new;
+        neg_mc = m_new == -INFINITY ? kNoRef : -m_new * c;
+        sum[0] = sum[1] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[2 * e], c, neg_mc));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[2 * e + 1], c, neg_mc));
+          pw[e >> 2][e & 3] = E::pack2(p0, p1);
+          sum[e & 1] += p0 + p1;
+        }
+      }
       l += sum[0] + sum[1];
 
       // O^T += V^T P^T of block u; operand reads two MFMAs ahead
