@@ -258,6 +258,11 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
       // (two copies of the loop, so that no branch sits between the MFMAs)
       u32x4 pw[2];
       float sum[2] = {0.f, 0.f};
+      // the first V^T operands of the PV MFMAs below are read two score MFMAs
+      // before the score phase ends (block u's V tile is resident), so the
+      // PV phase does not start on an LDS wait
+      const uint8_t* vt = v_tile(u);
+      vec8 va[kAhead];
       auto phase_a = [&](auto next) {
         constexpr bool kNext = decltype(next)::value;
         const uint8_t* kt = k_tile(u + 1);
@@ -290,6 +295,10 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
               pw[e >> 2][e & 3] = E::pack2(pr[2 * e], pr[2 * e + 1]);
               sum[e & 1] += pr[2 * e] + pr[2 * e + 1];
             }
+          }
+          if (t == (kKs >= 2 ? kKs - 2 : 0)) {
+#pragma unroll
+            for (int r = 0; r < kAhead && r < 2 * kDB; ++r) va[r] = tr_frag<IsBf16, DV>(vt, lane, r / kDB, r % kDB);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -328,10 +337,6 @@ __global__ __launch_bounds__(kThr, 1) void fwd_wide_kernel(
       l += sum[0] + sum[1];
 
       // O^T += V^T P^T of block u; operand reads two MFMAs ahead
-      const uint8_t* vt = v_tile(u);
-      vec8 va[kAhead];
-#pragma unroll
-      for (int r = 0; r < kAhead && r < 2 * kDB; ++r) va[r] = tr_frag<IsBf16, DV>(vt, lane, r / kDB, r % kDB);
 #pragma unroll
       for (int i = 0; i < 2 * kDB; ++i) {
         const int tt = i / kDB, db = i % kDB;
