@@ -91,11 +91,8 @@ constexpr int kMaskNone = 0, kMaskEdge = 1, kMaskWindow = 2;
 // read, where each 32-lane half touches four consecutive rows over 32
 // contiguous bytes per 16-lane group; a 64-byte pad puts those four rows in
 // four disjoint 16-bank ranges.  One extra 1 KB slot at the end absorbs the
-// copies of waves that have no real chunk for their last copy slot.
-// d = 96 takes the strides of d = 128: they keep both reads conflict-free and
-// split each stage into whole 1 KB copies that the waves share evenly.
-// DV is the width of V (and O) rows; it differs from D only in the d_v != d
-// launches.
+// copies of waves that have no real chunk for their last copy slot.  Only
+// d = d_v = 64 is launched from this source.
 template <int D, int DV = D> struct Lds {
   static constexpr int kRowBytes = 2 * D;    // a K (and Q) row
   static constexpr int kVRowBytes = 2 * DV;  // a V (and O) row
@@ -419,16 +416,12 @@ struct FwdBlock {
   }
 
   // MFMA slot of step st (0 scale, 1 exp2, 2 pack and partial sum) of score
-  // pair e, for blocks of 16, 14, 12 (d = 96), 10, 8, 6 or 4 MFMA slots.  Steps that
-  // land in the same slot run in program order.
+  // pair e, for blocks of 8 MFMA slots (or 4, a wave's first block).  Steps
+  // that land in the same slot run in program order.
   template <int kSlots>
   static constexpr int slot_of(int e, int st) {
-    return kSlots == 16 ? e + (st == 0 ? 0 : st == 1 ? 2 : 5)
-         : kSlots == 14 ? (7 * e) / 8 + (st == 0 ? 0 : st == 1 ? 2 : 5)
-         : kSlots == 12 ? (3 * e) / 4 + (st == 0 ? 0 : st == 1 ? 2 : 4)
-         : kSlots == 10 ? (5 * e) / 8 + (st == 0 ? 0 : st == 1 ? 2 : 4)
-         : (kSlots == 8 || kSlots == 6) ? e / 2 + st
-                        : (e / 4 + st < 3 ? e / 4 + st : 3);
+    static_assert(kSlots == 8 || kSlots == 4, "d = 64 blocks hold 8 or 4 MFMAs");
+    return kSlots == 8 ? e / 2 + st : (e / 4 + st < 3 ? e / 4 + st : 3);
   }
 
   // Block u: PV MFMAs of block u-1 (none if kFirst), score MFMAs of block u+1,
@@ -453,9 +446,7 @@ struct FwdBlock {
   template <int kMask, bool kFirst = false, int kHalf = 0, bool kCopy = false>
   __device__ __forceinline__ void block(int u, const Copies* cp = nullptr) {
     constexpr int kMfmas = (kFirst ? 0 : kPV) + kKs;
-    static_assert(kMfmas == 16 || kMfmas == 14 || kMfmas == 12 || kMfmas == 10 || kMfmas == 8 ||
-                      kMfmas == 6 || kMfmas == 4,
-                  "slot schedules exist for 4, 6, 8, 10, 12, 14 and 16 MFMAs");
+    static_assert(kMfmas == 8 || kMfmas == 4, "slot schedules exist for 4 and 8 MFMAs");
     auto slot = [](int e, int st) { return slot_of<kMfmas>(e, st); };
     // K operand of block u+1: K tile (u+1)/2, half (u+1)&1
     const uint8_t* kt = k_stage(((u + 1) >> 1) & 3) + k_base + ((u + 1) & 1) * 32 * L::kKStride;
